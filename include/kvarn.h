@@ -1,0 +1,207 @@
+/*
+ * kvarn.h -- C ABI of the KVarN hot path on MI355X (gfx950).
+ *
+ * KVarN quantizes a KV cache without calibration: each 128-token group of
+ * post-RoPE K and V of one KV head is rotated along the channel axis by a
+ * Hadamard matrix, variance-normalized over the token and channel axes with
+ * 16 Sinkhorn-style iterations, rounded to nearest and stored as a record of
+ * codes plus scale metadata.  The first 128 tokens (the sink) and the
+ * in-progress group (the tail) stay exact in fp16.  Decode attention reads
+ * the records directly in the rotated frame and rotates its output back once.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "KVarN: Variance-Normalized KV-Cache Quantization Mitigates Error
+ *        Accumulation in Reasoning Tasks" (fig1.dev summary of arXiv
+ *        2606.03458): "What it is", "Why it matters".
+ *   [P2] "KVarN KV Cache: Implementation and Benchmarks" (anbeeld.com):
+ *        §1 "Where KVarN Comes From", §2.1 "Sink, Body, And Tail".
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer is allocated and owned by the caller.  The library never
+ *     allocates, frees or synchronizes; all work is queued on `stream` (a
+ *     hipStream_t; NULL = the default stream) in call order.
+ *   - Pointers marked "device" must be device-accessible memory of the
+ *     current HIP device; "host" pointers are read before the call returns.
+ *   - Argument errors are detected on the host before anything is queued and
+ *     returned as a negative kvarn_status; kvarn_last_error() then holds a
+ *     message (thread-local).  Launch failures return KVARN_EHIP.
+ *   - fp16 = IEEE binary16.  Inputs must be finite and small enough that the
+ *     scales of reading R8 below fit fp16 (|x| < 2^12 is always safe).
+ *   - The record layout (reading R9 of the oracle):
+ *       record = [codes][s: 128 x fp16][c: D x fp16],
+ *       K codes token-major (row t = token t's D codes),
+ *       V codes channel-major (row j = channel j's 128 codes);
+ *       in a row, code i sits at bit b*(i mod 32/b) of 32-bit little-endian
+ *       word floor(i*b/32).  Dequantized value (rotated frame):
+ *       s_t * (code_tj - (2^b-1)/2) * c_j; original frame: times H_D/sqrt(D).
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVARN_OK = 0,
+  KVARN_EINVAL = -1,       /* null pointer, negative size, bad field */
+  KVARN_EUNSUPPORTED = -2, /* valid but not implemented (head_dim, bits, GQA) */
+  KVARN_ERANGE = -3,       /* a length exceeds a capacity */
+  KVARN_EWORKSPACE = -4,   /* workspace too small */
+  KVARN_EHIP = -5          /* the HIP runtime reported an error */
+} kvarn_status;
+
+/* Group, sink and tail capacity are 128 tokens each [P2 §2.1]. */
+#define KVARN_GROUP 128
+#define KVARN_SINK 128
+#define KVARN_SINKHORN_ITERS 16 /* [P2 §1] */
+
+typedef struct {
+  int32_t head_dim;       /* D: 128 or 256 */
+  int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;   /* Hkv; Hq/Hkv must be 1, 2 or 4 */
+  int32_t k_bits;         /* 2 or 4 */
+  int32_t v_bits;         /* 2 or 4 */
+  int32_t group;          /* must be 128 */
+  int32_t sink;           /* must be 128 */
+  int32_t sinkhorn_iters; /* 0..64; KVarN uses 16 */
+} kvarn_config;
+
+/*
+ * Cache view (pointers only).  Element (b, h, i, d) of an fp16 block is at
+ * index ((b*Hkv + h)*128 + i)*D + d.  Record g of (b, h) starts at byte
+ * ((b*Hkv + h)*max_groups + g) * kvarn_group_bytes(cfg): the K record first,
+ * then the V record.  seq_len[b] = tokens cached for request b.  Positions
+ * [0,128) live in the sink, group g covers positions [128+128g, 256+128g),
+ * and the tail holds positions [128+128*G, n) with G = max(0,(n-128)/128)
+ * sealed groups [P2 §2.1].  The cache holds at most
+ * 128 + 128*max_groups + 127 tokens per request.
+ */
+typedef struct {
+  void *sink_k, *sink_v; /* device fp16 [batch][Hkv][128][D] */
+  void *tail_k, *tail_v; /* device fp16 [batch][Hkv][128][D] */
+  void *records;         /* device, batch*Hkv*max_groups*kvarn_group_bytes(cfg) bytes */
+  int32_t *seq_len;      /* device int32 [batch] */
+  int32_t batch;
+  int32_t max_groups;
+} kvarn_cache;
+
+/* Pure host helpers (no GPU needed). ---------------------------------- */
+
+/* Checks a config; KVARN_OK or the status an entry point would return. */
+kvarn_status kvarn_check_config(const kvarn_config *cfg);
+
+/* Bytes of one record: 128*D*bits/8 + 2*128 + 2*D; 0 if unsupported. */
+size_t kvarn_record_bytes(int32_t head_dim, int32_t bits);
+
+/* Bytes of one (K record, V record) pair; 0 for an invalid config. */
+size_t kvarn_group_bytes(const kvarn_config *cfg);
+
+/* Workspace that kvarn_decode_attn needs for this batch and max_groups. */
+size_t kvarn_decode_workspace_bytes(const kvarn_config *cfg, int32_t batch, int32_t max_groups);
+
+/* Message of the last error on this thread ("" if none). */
+const char *kvarn_last_error(void);
+
+/* Stable name of a status code. */
+const char *kvarn_status_string(kvarn_status s);
+
+/* Hot-path entry points. ------------------------------------------------ */
+
+/*
+ * Append one token per request [P2 §2.1].  k_new, v_new: device fp16
+ * [batch][Hkv][D], post-RoPE.  For each request b with n = seq_len[b], the
+ * token goes to sink[n] if n < 128, else to tail[(n-128) mod 128]; then
+ * seq_len[b] = n+1.  A request whose cache is full (n >= 128 +
+ * 128*max_groups + 127, so the token would complete a group that has no
+ * record slot) is left unchanged.  Call
+ * kvarn_seal_group after every append so a full tail is sealed before the
+ * next append overwrites it.
+ */
+kvarn_status kvarn_append(const kvarn_config *cfg, const kvarn_cache *cache,
+                          const void *k_new, const void *v_new, void *stream);
+
+/*
+ * Seal on arrival [P2 §2.1]: every request b whose newest token completed a
+ * group (n = seq_len[b] >= 256 and (n-128) mod 128 == 0) has group
+ * g = (n-128)/128 - 1 quantized from its tail into record g, for every KV
+ * head, K and V: Hadamard rotation, `sinkhorn_iters` alternating token and
+ * channel RMS rescalings, per-token round to nearest [P1 "What it is"; P2 §1].
+ * The tail then counts as empty (no data moves).  Other requests are
+ * untouched.  seq_len is read on the device, so no host synchronization is
+ * needed.
+ */
+kvarn_status kvarn_seal_group(const kvarn_config *cfg, const kvarn_cache *cache, void *stream);
+
+/*
+ * Bulk ingest of a prompt: for each request b, tokens [0, len_host[b]) of
+ * k, v (device fp16 [batch][Hkv][src_tokens][D]) fill the sink, every
+ * complete group is sealed into its record, the rest goes to the tail, and
+ * seq_len[b] = len_host[b].  len_host is a host array [batch]; each length
+ * must be <= src_tokens and <= the cache capacity (else KVARN_ERANGE).
+ */
+kvarn_status kvarn_prefill(const kvarn_config *cfg, const kvarn_cache *cache,
+                           const void *k, const void *v, int64_t src_tokens,
+                           const int32_t *len_host, void *stream);
+
+/*
+ * Decode attention [P2 §1, §2.1]: for every request b and query head h
+ * (KV head floor(h*Hkv/Hq)), attends the query q (device fp16 [batch][Hq][D],
+ * post-RoPE) over all seq_len[b] cached positions: the exact sink and tail in
+ * the original frame, the sealed records in the rotated frame with the query
+ * rotated by the same Hadamard matrix; the record part of the output is
+ * rotated back once.  out: device fp32 [batch][Hq][D].  softmax_scale
+ * multiplies q.k (use 1/sqrt(D)).  workspace: device, at least
+ * kvarn_decode_workspace_bytes(cfg, batch, max_groups) bytes, 256-byte
+ * aligned; its contents are scratch.  A request with seq_len 0 gets zeros.
+ */
+kvarn_status kvarn_decode_attn(const kvarn_config *cfg, const kvarn_cache *cache,
+                               const void *q, float *out, float softmax_scale,
+                               void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The two phases of kvarn_decode_attn, for callers that schedule them apart
+ * (kvarn_decode_attn == partial then combine, same arguments):
+ *   partial: the split-K kernel; writes per-split (max, sum, output) partials
+ *            of every request and query head into `workspace`;
+ *   combine: log-sum-exp merge of those partials, one inverse Hadamard of the
+ *            record part per query head, normalization; writes `out`.
+ * The workspace must not be touched between the two calls, and the cache
+ * (seq_len included) must be unchanged.
+ */
+kvarn_status kvarn_decode_attn_partial(const kvarn_config *cfg, const kvarn_cache *cache, const void *q,
+                                       float softmax_scale, void *workspace, size_t ws_bytes, void *stream);
+kvarn_status kvarn_decode_attn_combine(const kvarn_config *cfg, const kvarn_cache *cache, float *out,
+                                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Seal n independent tiles (the same kernel as kvarn_seal_group).
+ * src: device fp16 [n][128][D].  dst: device; tile i's record is written at
+ * dst + i*dst_stride (dst_stride >= kvarn_record_bytes, multiple of 16).
+ * kind 0 = K layout (token-major codes), 1 = V layout (channel-major).
+ * dbg: NULL, or device fp32 [n][128 + D] receiving each tile's token scales
+ * s_t and channel scales c_j before their fp16 rounding.
+ */
+kvarn_status kvarn_seal_tiles(int32_t head_dim, int32_t bits, int32_t kind, int32_t sinkhorn_iters,
+                              const void *src, void *dst, int64_t dst_stride, float *dbg,
+                              int32_t n, void *stream);
+
+/*
+ * Convert records to the standard fp16 layout [P2 §2.1: attention paths
+ * that cannot read records convert them first].  For n records at
+ * src + i*src_stride (kind 0 = K, 1 = V), writes the original-frame
+ * reconstruction (s_t*(code-mid)*c_j, times H_D/sqrt(D)) rounded to fp16 into
+ * dst (device fp16 [n][128][D]).
+ */
+kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
+                                   const void *src, int64_t src_stride, void *dst,
+                                   int32_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

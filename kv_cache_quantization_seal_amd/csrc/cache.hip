@@ -1,0 +1,165 @@
+// KVarN cache bookkeeping kernels: append one token, prefill copies, and the
+// record -> fp16 conversion.
+//
+// The sink (positions [0,128)) and the in-progress group (the tail) stay exact
+// in fp16; a full tail is sealed into a record
+// ["KVarN KV Cache: Implementation and Benchmarks" (anbeeld.com), §2.1 "Sink,
+// Body, And Tail"].  Records can be converted back to a standard fp16 layout
+// for attention paths that do not read them directly (same section).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace kvarn {
+
+// One workgroup per request: read n, copy every KV head's K and V row into
+// its slot, then advance seq_len.  Copies move 16-byte chunks.
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(CacheArgs c, const uint4* __restrict__ k_new,
+                                                     const uint4* __restrict__ v_new) {
+  constexpr int CH = D / 8;  // 16-byte chunks per fp16 row
+  const int b = blockIdx.x;
+  const int n = c.seq_len[b];
+  // Capacity 128 + 128*max_groups + 127: the tail may hold all but the last
+  // token of a group that has no record slot left.
+  const bool full = n < 0 || n >= kSink + kGroup * c.max_groups + kGroup - 1;
+  if (!full) {
+    const int slot = n < kSink ? n : (n - kSink) % kGroup;
+    uint4* dk = reinterpret_cast<uint4*>(n < kSink ? c.sink_k : c.tail_k);
+    uint4* dv = reinterpret_cast<uint4*>(n < kSink ? c.sink_v : c.tail_v);
+    const int per_kind = c.hkv * CH;
+    for (int i = threadIdx.x; i < 2 * per_kind; i += blockDim.x) {
+      const int kind = i / per_kind;
+      const int r = i % per_kind;
+      const int h = r / CH, part = r % CH;
+      const int64_t src = ((int64_t)b * c.hkv + h) * CH + part;
+      const int64_t dst = (((int64_t)b * c.hkv + h) * kGroup + slot) * CH + part;
+      if (kind == 0)
+        dk[dst] = k_new[src];
+      else
+        dv[dst] = v_new[src];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && !full) c.seq_len[b] = n + 1;
+}
+
+// One workgroup per (KV head, request): sink and tail copies of a prompt.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_copy_kernel(CacheArgs c, const uint4* __restrict__ k,
+                                                           const uint4* __restrict__ v, int64_t src_tokens,
+                                                           PrefillLens lens, int b0) {
+  constexpr int CH = D / 8;
+  const int h = blockIdx.x;
+  const int bl = blockIdx.y;
+  const int b = b0 + bl;
+  const int len = lens.len[bl];
+  const int n_sink = len < kSink ? len : kSink;
+  const int n_groups = len > kSink ? (len - kSink) / kGroup : 0;
+  const int tail_lo = kSink + kGroup * n_groups;
+  const int n_tail = len > kSink ? len - tail_lo : 0;
+  const int64_t bh = (int64_t)b * c.hkv + h;
+  uint4* sk = reinterpret_cast<uint4*>(c.sink_k) + bh * kGroup * CH;
+  uint4* sv = reinterpret_cast<uint4*>(c.sink_v) + bh * kGroup * CH;
+  uint4* tk = reinterpret_cast<uint4*>(c.tail_k) + bh * kGroup * CH;
+  uint4* tv = reinterpret_cast<uint4*>(c.tail_v) + bh * kGroup * CH;
+  const uint4* ks = k + bh * src_tokens * CH;
+  const uint4* vs = v + bh * src_tokens * CH;
+  for (int i = threadIdx.x; i < n_sink * CH; i += blockDim.x) {
+    sk[i] = ks[i];
+    sv[i] = vs[i];
+  }
+  for (int i = threadIdx.x; i < n_tail * CH; i += blockDim.x) {
+    tk[i] = ks[(int64_t)tail_lo * CH + i];
+    tv[i] = vs[(int64_t)tail_lo * CH + i];
+  }
+  if (h == 0 && threadIdx.x == 0) c.seq_len[b] = len;
+}
+
+// Record -> fp16 original-frame rows.  Thread (t, rb) rebuilds channels
+// [64 rb, 64 rb + 64) of token t: s_t (code - mid) c_j, then H_D / sqrt(D).
+template <int D, int BITS, int KIND>
+__global__ __launch_bounds__(2 * D) void dequant_kernel(const uint8_t* __restrict__ src, int64_t src_stride,
+                                                        __half* __restrict__ dst) {
+  constexpr int NB = D / 64;
+  constexpr int P = D + 4;
+  constexpr int CODE_BYTES = kGroup * D * BITS / 8;
+  constexpr float MID = 0.5f * ((1 << BITS) - 1);
+  __shared__ float xs[NB > 1 ? kGroup * P : 1];
+  const uint8_t* rec = src + blockIdx.x * src_stride;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rb = w % NB;
+  const int t = 64 * (w / NB) + lane;
+  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(rec + CODE_BYTES);
+  const uint16_t* c16 = s16 + kGroup;
+  const float st = h2f(s16[t]);
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int j = 64 * rb + i;
+    uint32_t code;
+    if (KIND == 0) {
+      const int idx = j;  // token-major: code j of row t
+      const uint32_t word = reinterpret_cast<const uint32_t*>(rec + (size_t)t * (D * BITS / 8))[idx * BITS / 32];
+      code = (word >> (BITS * (idx % (32 / BITS)))) & ((1u << BITS) - 1);
+    } else {
+      const int idx = t;  // channel-major: code t of row j
+      const uint32_t word = reinterpret_cast<const uint32_t*>(rec + (size_t)j * (kGroup * BITS / 8))[idx * BITS / 32];
+      code = (word >> (BITS * (idx % (32 / BITS)))) & ((1u << BITS) - 1);
+    }
+    x[i] = st * ((float)code - MID) * h2f(c16[j]);
+  }
+  rotate_row_slice<D, P>(x, xs, t, rb);
+  const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
+  uint4* out = reinterpret_cast<uint4*>(dst + ((int64_t)blockIdx.x * kGroup + t) * D + 64 * rb);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      wd[e] = (uint32_t)f2h_rne(x[8 * k + 2 * e] * rs) | ((uint32_t)f2h_rne(x[8 * k + 2 * e + 1] * rs) << 16);
+    out[k] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+}
+
+hipError_t launch_append(int D, const CacheArgs& c, const void* k, const void* v, hipStream_t st) {
+  if (D == 128)
+    hipLaunchKernelGGL(append_kernel<128>, dim3(c.batch), dim3(256), 0, st, c, (const uint4*)k, (const uint4*)v);
+  else
+    hipLaunchKernelGGL(append_kernel<256>, dim3(c.batch), dim3(256), 0, st, c, (const uint4*)k, (const uint4*)v);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const void* v, int64_t src_tokens,
+                               const PrefillLens& lens, int b0, int nb, hipStream_t st) {
+  if (D == 128)
+    hipLaunchKernelGGL(prefill_copy_kernel<128>, dim3(c.hkv, nb), dim3(256), 0, st, c, (const uint4*)k,
+                       (const uint4*)v, src_tokens, lens, b0);
+  else
+    hipLaunchKernelGGL(prefill_copy_kernel<256>, dim3(c.hkv, nb), dim3(256), 0, st, c, (const uint4*)k,
+                       (const uint4*)v, src_tokens, lens, b0);
+  return hipGetLastError();
+}
+
+template <int D, int BITS>
+static void launch_dq(int kind, const void* src, int64_t stride, void* dst, int n, hipStream_t st) {
+  if (kind == 0)
+    hipLaunchKernelGGL((dequant_kernel<D, BITS, 0>), dim3(n), dim3(2 * D), 0, st, (const uint8_t*)src, stride,
+                       (__half*)dst);
+  else
+    hipLaunchKernelGGL((dequant_kernel<D, BITS, 1>), dim3(n), dim3(2 * D), 0, st, (const uint8_t*)src, stride,
+                       (__half*)dst);
+}
+
+hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
+                          hipStream_t st) {
+  if (D == 128) {
+    if (bits == 2) launch_dq<128, 2>(kind, src, src_stride, dst, n, st);
+    else launch_dq<128, 4>(kind, src, src_stride, dst, n, st);
+  } else {
+    if (bits == 2) launch_dq<256, 2>(kind, src, src_stride, dst, n, st);
+    else launch_dq<256, 4>(kind, src, src_stride, dst, n, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvarn

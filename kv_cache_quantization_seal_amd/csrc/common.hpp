@@ -1,0 +1,154 @@
+// Device helpers shared by the KVarN HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+constexpr int kGroup = 128;  // tokens per sealed group
+constexpr int kSink = 128;   // exact leading tokens
+constexpr int kWave = 64;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+__device__ __forceinline__ uint16_t f2h_rne(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+// Order LDS traffic between lanes of one wave (no cross-wave barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Reductions across the 16 lanes of one row (lanes 16r .. 16r+15).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1, 16);
+  v += __shfl_xor(v, 2, 16);
+  v += __shfl_xor(v, 4, 16);
+  v += __shfl_xor(v, 8, 16);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Position p (0..15) of an unpacked 16-code block -> code index within the
+// block, for the unpacking used by the decode kernel:
+//   2-bit: dword w -> bytes (w >> 2k) & 0x03030303, k = 0..3: byte b of
+//          dword k is code 4b + k;
+//   4-bit: dwords w0,w1 -> w0 & M, (w0 >> 4) & M, w1 & M, (w1 >> 4) & M with
+//          M = 0x0F0F0F0F: byte b of dword k is code 8(k/2) + 2b + (k%2).
+template <int BITS>
+__host__ __device__ constexpr int unpack_index(int p) {
+  return BITS == 2 ? 4 * (p & 3) + (p >> 2) : 8 * ((p >> 2) >> 1) + 2 * (p & 3) + ((p >> 2) & 1);
+}
+
+// Unpack one 16-code block (BITS*2 bytes) into 16 int8 MFMA operand bytes.
+template <int BITS>
+__device__ __forceinline__ v4i unpack16(const uint32_t* w) {
+  v4i r;
+  if constexpr (BITS == 2) {
+    const uint32_t x = w[0];
+    r[0] = (int)(x & 0x03030303u);
+    r[1] = (int)((x >> 2) & 0x03030303u);
+    r[2] = (int)((x >> 4) & 0x03030303u);
+    r[3] = (int)((x >> 6) & 0x03030303u);
+  } else {
+    r[0] = (int)(w[0] & 0x0F0F0F0Fu);
+    r[1] = (int)((w[0] >> 4) & 0x0F0F0F0Fu);
+    r[2] = (int)(w[1] & 0x0F0F0F0Fu);
+    r[3] = (int)((w[1] >> 4) & 0x0F0F0F0Fu);
+  }
+  return r;
+}
+
+// Split x (|x| <= 127.5) into three int8 limbs a0 + a1/254 + a2/254^2 with
+// round-to-nearest at each level; returns the limbs as exact floats.
+__device__ __forceinline__ void limbs3(float x, float& a0, float& a1, float& a2) {
+  a0 = rintf(x);
+  float r1 = (x - a0) * 254.0f;
+  a1 = rintf(r1);
+  float r2 = (r1 - a1) * 254.0f;
+  a2 = rintf(r2);
+}
+
+// Pack four exact small integers (as floats, in [-128, 127]) into one dword of
+// int8 bytes (byte 0 = first).
+__device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d) {
+  const uint32_t x0 = (uint32_t)((int)a) & 0xFFu;
+  const uint32_t x1 = (uint32_t)((int)b) & 0xFFu;
+  const uint32_t x2 = (uint32_t)((int)c) & 0xFFu;
+  const uint32_t x3 = (uint32_t)((int)d) & 0xFFu;
+  return x0 | (x1 << 8) | (x2 << 16) | (x3 << 24);
+}
+
+
+// Natural-order Sylvester Hadamard transform (unnormalized) of token rows held
+// as 64-channel slices: thread (t, rb) holds channels [64 rb, 64 rb + 64) of
+// token t in x.  The butterflies over the six low channel-index bits run in
+// registers; for D > 64 the block-index bits are combined through LDS
+// (xs = [128][P] fp32 scratch, which this overwrites).  Contains barriers: all
+// threads of the block must call it.
+template <int D, int P>
+__device__ __forceinline__ void rotate_row_slice(float (&x)[64], float* xs, int t, int rb) {
+  constexpr int NB = D / 64;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (!(i & s)) {
+        const float a = x[i], b = x[i + s];
+        x[i] = a + b;
+        x[i + s] = a - b;
+      }
+    }
+  }
+  if constexpr (NB > 1) {
+    float* xrow = xs + t * P + 64 * rb;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      *reinterpret_cast<float4*>(xrow + 4 * k) = make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
+    __syncthreads();
+    // y_{64 rb + i} = sum_o (-1)^popcount(rb & o) x_{64 o + i}
+    const float own = (__popc(rb) & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= own;
+#pragma unroll
+    for (int o = 0; o < NB; ++o) {
+      if (o == rb) continue;
+      const float sg = (__popc(rb & o) & 1) ? -1.0f : 1.0f;
+      const float* other = xs + t * P + 64 * o;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float4 q = *reinterpret_cast<const float4*>(other + 4 * k);
+        x[4 * k] = fmaf(sg, q.x, x[4 * k]);
+        x[4 * k + 1] = fmaf(sg, q.y, x[4 * k + 1]);
+        x[4 * k + 2] = fmaf(sg, q.z, x[4 * k + 2]);
+        x[4 * k + 3] = fmaf(sg, q.w, x[4 * k + 3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace kvarn

@@ -1,0 +1,299 @@
+// C ABI of the KVarN hot path: host-side validation and kernel dispatch.
+// Every argument check runs before anything is queued, so a rejected call
+// leaves the GPU untouched (and needs no GPU at all).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kvarn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvarn_status fail(kvarn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kvarn_status ok() {
+  g_err[0] = '\0';
+  return KVARN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool bits_ok(int b) { return b == 2 || b == 4; }
+bool dim_ok(int d) { return d == 128 || d == 256; }
+
+kvarn_status check_cfg(const kvarn_config* c) {
+  if (!c) return fail(KVARN_EINVAL, "config is NULL");
+  if (c->group != KVARN_GROUP || c->sink != KVARN_SINK)
+    return fail(KVARN_EUNSUPPORTED, "group and sink must both be 128 (got %d, %d)", c->group, c->sink);
+  if (!dim_ok(c->head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", c->head_dim);
+  if (!bits_ok(c->k_bits) || !bits_ok(c->v_bits))
+    return fail(KVARN_EUNSUPPORTED, "k_bits and v_bits must be 2 or 4 (got %d, %d)", c->k_bits, c->v_bits);
+  if (c->num_q_heads <= 0 || c->num_kv_heads <= 0)
+    return fail(KVARN_EINVAL, "head counts must be positive (got %d, %d)", c->num_q_heads, c->num_kv_heads);
+  if (c->num_q_heads % c->num_kv_heads)
+    return fail(KVARN_EINVAL, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", c->num_q_heads,
+                c->num_kv_heads);
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4)
+    return fail(KVARN_EUNSUPPORTED, "query heads per KV head must be 1, 2 or 4 (got %d)", g);
+  if (c->sinkhorn_iters < 0 || c->sinkhorn_iters > 64)
+    return fail(KVARN_EINVAL, "sinkhorn_iters must be in [0, 64] (got %d)", c->sinkhorn_iters);
+  return KVARN_OK;
+}
+
+size_t rec_bytes(int d, int bits) { return (size_t)KVARN_GROUP * d * bits / 8 + 2 * KVARN_GROUP + 2 * (size_t)d; }
+
+kvarn_status check_cache(const kvarn_config* c, const kvarn_cache* k) {
+  if (!k) return fail(KVARN_EINVAL, "cache is NULL");
+  if (k->batch <= 0) return fail(KVARN_EINVAL, "cache batch must be positive (got %d)", k->batch);
+  if (k->max_groups < 0) return fail(KVARN_EINVAL, "cache max_groups must be >= 0 (got %d)", k->max_groups);
+  if (!k->sink_k || !k->sink_v || !k->tail_k || !k->tail_v || !k->seq_len)
+    return fail(KVARN_EINVAL, "cache sink/tail/seq_len pointers must be non-NULL");
+  if (k->max_groups > 0 && !k->records) return fail(KVARN_EINVAL, "cache records is NULL");
+  if (!aligned(k->sink_k, 16) || !aligned(k->sink_v, 16) || !aligned(k->tail_k, 16) || !aligned(k->tail_v, 16) ||
+      !aligned(k->records, 16) || !aligned(k->seq_len, 4))
+    return fail(KVARN_EINVAL, "cache buffers must be 16-byte aligned");
+  (void)c;
+  return KVARN_OK;
+}
+
+kvarn::CacheArgs cache_args(const kvarn_config* c, const kvarn_cache* k) {
+  kvarn::CacheArgs a;
+  a.sink_k = (__half*)k->sink_k;
+  a.sink_v = (__half*)k->sink_v;
+  a.tail_k = (__half*)k->tail_k;
+  a.tail_v = (__half*)k->tail_v;
+  a.records = (const uint8_t*)k->records;
+  a.seq_len = k->seq_len;
+  a.batch = k->batch;
+  a.hkv = c->num_kv_heads;
+  a.max_groups = k->max_groups;
+  a.rec_k_bytes = (int)rec_bytes(c->head_dim, c->k_bits);
+  a.group_bytes = (int64_t)a.rec_k_bytes + (int64_t)rec_bytes(c->head_dim, c->v_bits);
+  return a;
+}
+
+kvarn_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVARN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvarn_status kvarn_check_config(const kvarn_config* cfg) {
+  const kvarn_status s = check_cfg(cfg);
+  return s == KVARN_OK ? ok() : s;
+}
+
+size_t kvarn_record_bytes(int32_t head_dim, int32_t bits) {
+  if (!dim_ok(head_dim) || !bits_ok(bits)) return 0;
+  return rec_bytes(head_dim, bits);
+}
+
+size_t kvarn_group_bytes(const kvarn_config* cfg) {
+  if (check_cfg(cfg) != KVARN_OK) return 0;
+  return rec_bytes(cfg->head_dim, cfg->k_bits) + rec_bytes(cfg->head_dim, cfg->v_bits);
+}
+
+size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t max_groups) {
+  if (check_cfg(cfg) != KVARN_OK || batch <= 0 || max_groups < 0) return 0;
+  return kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch, max_groups).ws_bytes;
+}
+
+const char* kvarn_last_error(void) { return g_err; }
+
+const char* kvarn_status_string(kvarn_status s) {
+  switch (s) {
+    case KVARN_OK: return "KVARN_OK";
+    case KVARN_EINVAL: return "KVARN_EINVAL";
+    case KVARN_EUNSUPPORTED: return "KVARN_EUNSUPPORTED";
+    case KVARN_ERANGE: return "KVARN_ERANGE";
+    case KVARN_EWORKSPACE: return "KVARN_EWORKSPACE";
+    case KVARN_EHIP: return "KVARN_EHIP";
+  }
+  return "KVARN_UNKNOWN";
+}
+
+kvarn_status kvarn_append(const kvarn_config* cfg, const kvarn_cache* cache, const void* k_new, const void* v_new,
+                          void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (!k_new || !v_new) return fail(KVARN_EINVAL, "k_new and v_new must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVARN_EINVAL, "k_new and v_new must be 16-byte aligned");
+  return hip_status(kvarn::launch_append(cfg->head_dim, cache_args(cfg, cache), k_new, v_new, (hipStream_t)stream),
+                    "kvarn_append launch");
+}
+
+kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache, void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (cache->max_groups == 0) return ok();
+  const kvarn::CacheArgs c = cache_args(cfg, cache);
+  kvarn::SealStreamArgs a;
+  a.tail_k = c.tail_k;
+  a.tail_v = c.tail_v;
+  a.seq_len = c.seq_len;
+  a.records = (uint8_t*)cache->records;
+  a.group_bytes = c.group_bytes;
+  a.rec_k_bytes = c.rec_k_bytes;
+  a.hkv = c.hkv;
+  a.max_groups = c.max_groups;
+  a.iters = cfg->sinkhorn_iters;
+  const int64_t nbh = (int64_t)cache->batch * cfg->num_kv_heads;
+  if (nbh > 0x7fffffff) return fail(KVARN_ERANGE, "batch * num_kv_heads too large");
+  return hip_status(kvarn::launch_seal_stream(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, (int)nbh,
+                                              (hipStream_t)stream),
+                    "kvarn_seal_group launch");
+}
+
+kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, const void* k, const void* v,
+                           int64_t src_tokens, const int32_t* len_host, void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (!k || !v || !len_host) return fail(KVARN_EINVAL, "k, v and len_host must be non-NULL");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVARN_EINVAL, "k and v must be 16-byte aligned");
+  if (src_tokens < 0) return fail(KVARN_EINVAL, "src_tokens must be >= 0");
+  const int64_t cap = (int64_t)KVARN_SINK + (int64_t)KVARN_GROUP * cache->max_groups + KVARN_GROUP - 1;
+  for (int b = 0; b < cache->batch; ++b) {
+    if (len_host[b] < 0) return fail(KVARN_EINVAL, "len_host[%d] = %d is negative", b, len_host[b]);
+    if (len_host[b] > src_tokens)
+      return fail(KVARN_ERANGE, "len_host[%d] = %d exceeds src_tokens = %lld", b, len_host[b], (long long)src_tokens);
+    if (len_host[b] > cap)
+      return fail(KVARN_ERANGE, "len_host[%d] = %d exceeds the cache capacity %lld", b, len_host[b], (long long)cap);
+  }
+  const kvarn::CacheArgs c = cache_args(cfg, cache);
+  hipStream_t st = (hipStream_t)stream;
+  for (int b0 = 0; b0 < cache->batch; b0 += kvarn::kMaxPrefillBatch) {
+    const int nb = cache->batch - b0 < kvarn::kMaxPrefillBatch ? cache->batch - b0 : kvarn::kMaxPrefillBatch;
+    kvarn::PrefillLens lens;
+    memset(&lens, 0, sizeof(lens));
+    int max_g = 0;
+    for (int i = 0; i < nb; ++i) {
+      lens.len[i] = len_host[b0 + i];
+      const int g = lens.len[i] > KVARN_SINK ? (lens.len[i] - KVARN_SINK) / KVARN_GROUP : 0;
+      if (g > max_g) max_g = g;
+    }
+    hipError_t e = kvarn::launch_prefill_copy(cfg->head_dim, c, k, v, src_tokens, lens, b0, nb, st);
+    if (e != hipSuccess) return hip_status(e, "kvarn_prefill copy launch");
+    if (max_g > 0) {
+      kvarn::SealPrefillArgs a;
+      a.k = (const __half*)k;
+      a.v = (const __half*)v;
+      a.src_tokens = src_tokens;
+      a.records = (uint8_t*)cache->records;
+      a.group_bytes = c.group_bytes;
+      a.rec_k_bytes = c.rec_k_bytes;
+      a.hkv = c.hkv;
+      a.max_groups = c.max_groups;
+      a.b0 = b0;
+      a.iters = cfg->sinkhorn_iters;
+      a.lens = lens;
+      e = kvarn::launch_seal_prefill(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, max_g, nb * c.hkv, st);
+      if (e != hipSuccess) return hip_status(e, "kvarn_prefill seal launch");
+    }
+  }
+  return ok();
+}
+
+static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,
+                                  float softmax_scale, void* workspace, size_t ws_bytes, int phases, void* stream,
+                                  const char* what) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if ((phases & 1) && !q) return fail(KVARN_EINVAL, "q must be non-NULL");
+  if ((phases & 2) && !out) return fail(KVARN_EINVAL, "out must be non-NULL");
+  if ((q && !aligned(q, 16)) || (out && !aligned(out, 16)))
+    return fail(KVARN_EINVAL, "q and out must be 16-byte aligned");
+  const kvarn::DecodePlan p =
+      kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch, cache->max_groups);
+  if (!workspace || ws_bytes < p.ws_bytes)
+    return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, p.ws_bytes);
+  if (!aligned(workspace, 256)) return fail(KVARN_EINVAL, "workspace must be 256-byte aligned");
+  if (!(softmax_scale == softmax_scale)) return fail(KVARN_EINVAL, "softmax_scale is NaN");
+  kvarn::DecodeArgs a;
+  a.c = cache_args(cfg, cache);
+  a.q = (const __half*)q;
+  a.out = out;
+  const size_t rows = (size_t)cache->batch * cfg->num_q_heads * p.nsplit;
+  const size_t o_bytes = (rows * cfg->head_dim * sizeof(float) + 255) & ~(size_t)255;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float*)((char*)workspace + o_bytes);
+  a.scale = softmax_scale;
+  a.hq = cfg->num_q_heads;
+  a.nsplit = p.nsplit;
+  a.n_rec_splits = p.n_rec_splits;
+  a.groups_per_split = p.groups_per_split;
+  a.groups_per_wave = p.groups_per_wave;
+  return hip_status(kvarn::launch_decode(cfg->head_dim, cfg->k_bits, cfg->v_bits,
+                                         cfg->num_q_heads / cfg->num_kv_heads, a, phases, (hipStream_t)stream),
+                    what);
+}
+
+kvarn_status kvarn_decode_attn(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,
+                               float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_common(cfg, cache, q, out, softmax_scale, workspace, ws_bytes, 3, stream, "kvarn_decode_attn launch");
+}
+
+kvarn_status kvarn_decode_attn_partial(const kvarn_config* cfg, const kvarn_cache* cache, const void* q,
+                                       float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_common(cfg, cache, q, nullptr, softmax_scale, workspace, ws_bytes, 1, stream,
+                       "kvarn_decode_attn_partial launch");
+}
+
+kvarn_status kvarn_decode_attn_combine(const kvarn_config* cfg, const kvarn_cache* cache, float* out, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+  return decode_common(cfg, cache, nullptr, out, 1.0f, workspace, ws_bytes, 2, stream,
+                       "kvarn_decode_attn_combine launch");
+}
+
+kvarn_status kvarn_seal_tiles(int32_t head_dim, int32_t bits, int32_t kind, int32_t sinkhorn_iters, const void* src,
+                              void* dst, int64_t dst_stride, float* dbg, int32_t n, void* stream) {
+  if (!dim_ok(head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", head_dim);
+  if (!bits_ok(bits)) return fail(KVARN_EUNSUPPORTED, "bits must be 2 or 4 (got %d)", bits);
+  if (kind != 0 && kind != 1) return fail(KVARN_EINVAL, "kind must be 0 (K) or 1 (V) (got %d)", kind);
+  if (sinkhorn_iters < 0 || sinkhorn_iters > 64) return fail(KVARN_EINVAL, "sinkhorn_iters must be in [0, 64]");
+  if (n < 0) return fail(KVARN_EINVAL, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(KVARN_EINVAL, "src and dst must be non-NULL");
+  if (!aligned(src, 16) || !aligned(dst, 16) || (dbg && !aligned(dbg, 4)))
+    return fail(KVARN_EINVAL, "src and dst must be 16-byte aligned");
+  if (dst_stride < (int64_t)rec_bytes(head_dim, bits) || dst_stride % 16)
+    return fail(KVARN_EINVAL, "dst_stride must be >= the record size and a multiple of 16");
+  return hip_status(kvarn::launch_seal_tiles(head_dim, bits, kind, src, dst, dst_stride, dbg, n, sinkhorn_iters,
+                                             (hipStream_t)stream),
+                    "kvarn_seal_tiles launch");
+}
+
+kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind, const void* src, int64_t src_stride,
+                                   void* dst, int32_t n, void* stream) {
+  if (!dim_ok(head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", head_dim);
+  if (!bits_ok(bits)) return fail(KVARN_EUNSUPPORTED, "bits must be 2 or 4 (got %d)", bits);
+  if (kind != 0 && kind != 1) return fail(KVARN_EINVAL, "kind must be 0 (K) or 1 (V) (got %d)", kind);
+  if (n < 0) return fail(KVARN_EINVAL, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(KVARN_EINVAL, "src and dst must be non-NULL");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(KVARN_EINVAL, "src and dst must be 16-byte aligned");
+  if (src_stride < (int64_t)rec_bytes(head_dim, bits) || src_stride % 16)
+    return fail(KVARN_EINVAL, "src_stride must be >= the record size and a multiple of 16");
+  return hip_status(kvarn::launch_dequant(head_dim, bits, kind, src, src_stride, dst, n, (hipStream_t)stream),
+                    "kvarn_dequant_records launch");
+}
+
+}  // extern "C"

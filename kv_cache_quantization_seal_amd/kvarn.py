@@ -1,0 +1,219 @@
+"""ctypes binding of libkvarn.so (the C ABI declared in include/kvarn.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels.  PyTorch provides device memory and the current HIP stream.  If the
+native library is missing, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvarn.so")
+_lib = None
+
+OK, EINVAL, EUNSUPPORTED, ERANGE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
+GROUP = 128
+SINK = 128
+SINKHORN_ITERS = 16
+EXPORTS = (
+    "kvarn_check_config", "kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
+    "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_seal_group", "kvarn_prefill",
+    "kvarn_decode_attn", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
+    "kvarn_dequant_records",
+)
+
+
+class KvarnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("sink", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32)]
+
+
+class CacheView(ctypes.Structure):
+    _fields_ = [("sink_k", ctypes.c_void_p), ("sink_v", ctypes.c_void_p), ("tail_k", ctypes.c_void_p),
+                ("tail_v", ctypes.c_void_p), ("records", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("batch", ctypes.c_int32), ("max_groups", ctypes.c_int32)]
+
+
+def lib():
+    """Load libkvarn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_quantization_seal_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        cp, vp, i32, i64, f32 = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        sz = ctypes.c_size_t
+        L.kvarn_check_config.argtypes = [cp(Config)]
+        L.kvarn_record_bytes.argtypes = [i32, i32]
+        L.kvarn_record_bytes.restype = sz
+        L.kvarn_group_bytes.argtypes = [cp(Config)]
+        L.kvarn_group_bytes.restype = sz
+        L.kvarn_decode_workspace_bytes.argtypes = [cp(Config), i32, i32]
+        L.kvarn_decode_workspace_bytes.restype = sz
+        L.kvarn_last_error.restype = ctypes.c_char_p
+        L.kvarn_status_string.argtypes = [ctypes.c_int]
+        L.kvarn_status_string.restype = ctypes.c_char_p
+        L.kvarn_append.argtypes = [cp(Config), cp(CacheView), vp, vp, vp]
+        L.kvarn_seal_group.argtypes = [cp(Config), cp(CacheView), vp]
+        L.kvarn_prefill.argtypes = [cp(Config), cp(CacheView), vp, vp, i64, cp(i32), vp]
+        L.kvarn_decode_attn.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp, sz, vp]
+        L.kvarn_decode_attn_partial.argtypes = [cp(Config), cp(CacheView), vp, f32, vp, sz, vp]
+        L.kvarn_decode_attn_combine.argtypes = [cp(Config), cp(CacheView), vp, vp, sz, vp]
+        L.kvarn_seal_tiles.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp, i32, vp]
+        L.kvarn_dequant_records.argtypes = [i32, i32, i32, vp, i64, vp, i32, vp]
+        for name in EXPORTS:
+            if name not in ("kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
+                            "kvarn_last_error", "kvarn_status_string"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_name(s: int) -> str:
+    return {0: "KVARN_OK", -1: "KVARN_EINVAL", -2: "KVARN_EUNSUPPORTED", -3: "KVARN_ERANGE",
+            -4: "KVARN_EWORKSPACE", -5: "KVARN_EHIP"}.get(s, f"status {s}")
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise KvarnError(status, lib().kvarn_last_error().decode())
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the KVarN library must be contiguous")
+    return t.data_ptr()
+
+
+def make_config(head_dim: int, num_q_heads: int, num_kv_heads: int, k_bits: int, v_bits: int,
+                sinkhorn_iters: int = SINKHORN_ITERS) -> Config:
+    return Config(head_dim, num_q_heads, num_kv_heads, k_bits, v_bits, GROUP, SINK, sinkhorn_iters)
+
+
+def record_bytes(head_dim: int, bits: int) -> int:
+    return int(lib().kvarn_record_bytes(head_dim, bits))
+
+
+def group_bytes(cfg: Config) -> int:
+    return int(lib().kvarn_group_bytes(ctypes.byref(cfg)))
+
+
+def check_config(cfg: Config) -> int:
+    return int(lib().kvarn_check_config(ctypes.byref(cfg)))
+
+
+def decode_workspace_bytes(cfg: Config, batch: int, max_groups: int) -> int:
+    return int(lib().kvarn_decode_workspace_bytes(ctypes.byref(cfg), batch, max_groups))
+
+
+class KVarNCache:
+    """Device-resident KVarN cache of one attention layer (torch-allocated)."""
+
+    def __init__(self, cfg: Config, batch: int, max_groups: int, device="cuda"):
+        self.cfg = cfg
+        self.batch = batch
+        self.max_groups = max_groups
+        d, hkv = cfg.head_dim, cfg.num_kv_heads
+        f16 = dict(dtype=torch.float16, device=device)
+        self.sink_k = torch.zeros(batch, hkv, SINK, d, **f16)
+        self.sink_v = torch.zeros(batch, hkv, SINK, d, **f16)
+        self.tail_k = torch.zeros(batch, hkv, GROUP, d, **f16)
+        self.tail_v = torch.zeros(batch, hkv, GROUP, d, **f16)
+        self.rec_k_bytes = record_bytes(d, cfg.k_bits)
+        self.group_bytes = group_bytes(cfg)
+        self.records = torch.zeros(max(1, batch * hkv * max_groups * self.group_bytes), dtype=torch.uint8,
+                                   device=device)
+        self.seq_len = torch.zeros(batch, dtype=torch.int32, device=device)
+        ws = decode_workspace_bytes(cfg, batch, max_groups)
+        self.workspace = torch.empty(max(256, ws), dtype=torch.uint8, device=device)
+        self.view = CacheView(_ptr(self.sink_k), _ptr(self.sink_v), _ptr(self.tail_k), _ptr(self.tail_v),
+                              _ptr(self.records), _ptr(self.seq_len), batch, max_groups)
+
+    @property
+    def capacity(self) -> int:
+        return SINK + GROUP * self.max_groups + GROUP - 1
+
+    def record(self, b: int, h: int, g: int, kind: str) -> torch.Tensor:
+        """Bytes of one stored record (a view)."""
+        base = ((b * self.cfg.num_kv_heads + h) * self.max_groups + g) * self.group_bytes
+        if kind == "k":
+            return self.records[base:base + self.rec_k_bytes]
+        return self.records[base + self.rec_k_bytes:base + self.group_bytes]
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        _check(lib().kvarn_append(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k_new), _ptr(v_new),
+                                  _stream(stream)))
+
+    def seal_group(self, stream=None) -> None:
+        _check(lib().kvarn_seal_group(ctypes.byref(self.cfg), ctypes.byref(self.view), _stream(stream)))
+
+    def prefill(self, k: torch.Tensor, v: torch.Tensor, lengths: Sequence[int], stream=None) -> None:
+        arr = (ctypes.c_int32 * self.batch)(*[int(x) for x in lengths])
+        _check(lib().kvarn_prefill(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k), _ptr(v),
+                                   int(k.shape[2]), arr, _stream(stream)))
+
+    def decode_attn(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                    stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if scale is None:
+            scale = self.cfg.head_dim ** -0.5
+        _check(lib().kvarn_decode_attn(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q), _ptr(out),
+                                       float(scale), _ptr(self.workspace), self.workspace.numel(),
+                                       _stream(stream)))
+        return out
+
+    def decode_partial(self, q: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:
+        if scale is None:
+            scale = self.cfg.head_dim ** -0.5
+        _check(lib().kvarn_decode_attn_partial(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q),
+                                               float(scale), _ptr(self.workspace), self.workspace.numel(),
+                                               _stream(stream)))
+
+    def decode_combine(self, out: torch.Tensor, stream=None) -> torch.Tensor:
+        _check(lib().kvarn_decode_attn_combine(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(out),
+                                               _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
+        return out
+
+
+def seal_tiles(src: torch.Tensor, bits: int, kind: str, out: Optional[torch.Tensor] = None,
+               dbg: Optional[torch.Tensor] = None, iters: int = SINKHORN_ITERS, stream=None) -> torch.Tensor:
+    """Seal fp16 tiles [n][128][D]; returns records as uint8 [n][record_bytes]."""
+    n, t, d = src.shape
+    rb = record_bytes(d, bits)
+    if out is None:
+        out = torch.empty(n, rb, dtype=torch.uint8, device=src.device)
+    _check(lib().kvarn_seal_tiles(d, bits, 0 if kind == "k" else 1, iters, _ptr(src), _ptr(out),
+                                  out.stride(0), _ptr(dbg), n, _stream(stream)))
+    return out
+
+
+def dequant_records(recs: torch.Tensor, head_dim: int, bits: int, kind: str, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Records uint8 [n][>= record_bytes] -> fp16 [n][128][D], original frame."""
+    n = recs.shape[0]
+    if out is None:
+        out = torch.empty(n, GROUP, head_dim, dtype=torch.float16, device=recs.device)
+    _check(lib().kvarn_dequant_records(head_dim, bits, 0 if kind == "k" else 1, _ptr(recs), recs.stride(0),
+                                       _ptr(out), n, _stream(stream)))
+    return out

@@ -1,0 +1,94 @@
+"""GPU decode attention vs the oracle.
+
+Decode is checked on caches the oracle built (sink, tail and records encoded
+by the oracle, so independent of the GPU seal), over ragged lengths, GQA
+ratios 1/2/4, head dims 128/256 and 2/4-bit K and V.  Tolerance: 2e-3 max-abs
+on the fp32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_seal_amd import kvarn as K
+from kv_cache_quantization_seal_amd import synth
+from oracle import kvarn_oracle as O
+from tests.gpu_util import ATTN_ATOL, upload_states
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(d, hq, hkv, kb, vb, lens, seed):
+    wl = synth.Workload("t", 90 + seed, len(lens), hq, hkv, d, max(lens), 0, kb, vb, 0)
+    states, qs = [], []
+    for b, n in enumerate(lens):
+        row = []
+        for h in range(hkv):
+            k, v = synth.kv_stream(wl, b, h, max(n, 1))
+            row.append(O.state_from_stream(k[:n], v[:n], kb, vb))
+        states.append(row)
+        qs.append(synth.queries(wl, b, 1)[0])
+    return states, np.stack(qs)
+
+
+def _run(d, hq, hkv, kb, vb, lens, seed=0, max_groups=None):
+    states, q = _case(d, hq, hkv, kb, vb, lens, seed)
+    if max_groups is None:
+        max_groups = max(1, max((n - 128) // 128 for n in lens) + 1)
+    cfg = K.make_config(d, hq, hkv, kb, vb)
+    cache = K.KVarNCache(cfg, len(lens), max_groups)
+    upload_states(cache, states)
+    out = cache.decode_attn(torch.from_numpy(q).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    err = 0.0
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(out[b] == 0)
+            continue
+        ref = O.decode_attention(q[b], states[b], hkv)
+        err = max(err, np.abs(out[b] - ref).max())
+    return err
+
+
+def test_tiny_parity_workload():
+    wl = synth.WORKLOADS["tiny_parity"]
+    k, v = synth.kv_stream(wl, 0, 0, 512)
+    q = synth.queries(wl, 0, 1)[0]
+    st = O.state_from_stream(k, v, 2, 2)
+    cfg = K.make_config(128, 1, 1, 2, 2)
+    cache = K.KVarNCache(cfg, 1, 3)
+    upload_states(cache, [[st]])
+    out = cache.decode_attn(torch.from_numpy(q[None]).cuda()).cpu().numpy()[0]
+    ref = O.decode_attention(q, [st], 1)
+    err = np.abs(out - ref).max()
+    print(f"tiny parity max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("lens", [[1], [128], [129], [255], [256], [300, 77, 513], [1000, 0, 640]])
+def test_ragged_lengths_gqa4(lens):
+    err = _run(128, 8, 2, 2, 2, lens, seed=len(lens))
+    print(f"lens={lens}: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("d,hq,hkv,kb,vb", [
+    (128, 4, 4, 2, 2), (128, 4, 2, 4, 4), (128, 8, 2, 2, 4), (128, 8, 2, 4, 2),
+    (256, 4, 2, 4, 2), (256, 4, 1, 2, 2), (256, 2, 2, 4, 4),
+])
+def test_shapes_and_widths(d, hq, hkv, kb, vb):
+    err = _run(d, hq, hkv, kb, vb, [700, 389], seed=d + kb * 10 + vb)
+    print(f"d={d} hq={hq} hkv={hkv} k{kb} v{vb}: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+
+
+def test_many_groups_one_request():
+    err = _run(128, 4, 1, 2, 2, [128 + 128 * 40 + 17], seed=5)
+    print(f"41 groups: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+
+
+def test_spare_capacity_is_ignored():
+    # max_groups larger than any request needs; unused record slots hold junk.
+    err = _run(128, 4, 2, 2, 2, [400, 200], seed=6, max_groups=9)
+    assert err <= ATTN_ATOL

@@ -1,0 +1,64 @@
+"""GPU sealing vs the oracle, tile by tile (kvarn_seal_tiles).
+
+Tiles follow the synthetic recipe (outlier channels, lognormal token norms),
+plus degenerate tiles: all zero, a zero token and a zero channel, rank one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_seal_amd import kvarn as K
+from kv_cache_quantization_seal_amd import synth
+from oracle import kvarn_oracle as O
+from tests.gpu_util import check_sealed_tile
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiles(d, n, seed):
+    tiles = [synth.gaussian_tile(seed * 1000 + i, 128, d) for i in range(n)]
+    z = np.zeros((128, d), np.float16)
+    holes = synth.gaussian_tile(seed + 7, 128, d)
+    holes[3] = 0
+    holes[:, 5] = 0
+    rng = np.random.default_rng(seed)
+    r1 = np.outer(rng.lognormal(0, 1, 128), rng.standard_normal(d)).astype(np.float16)
+    small = (synth.gaussian_tile(seed + 9, 128, d).astype(np.float32) * 1e-3).astype(np.float16)
+    return np.stack(tiles + [z, holes, r1, small])
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_seal_tiles_parity(d, bits, kind):
+    x = _tiles(d, 9, seed=d + bits + (kind == "v"))
+    src = torch.from_numpy(x).cuda()
+    dbg = torch.zeros(len(x), 128 + d, dtype=torch.float32, device="cuda")
+    recs = K.seal_tiles(src, bits, kind, dbg=dbg)
+    torch.cuda.synchronize()
+    recs_h = recs.cpu().numpy()
+    dbg_h = dbg.cpu().numpy()
+    stats = {}
+    for i in range(len(x)):
+        ref = O.seal_tile(x[i], bits)
+        check_sealed_tile(recs_h[i].tobytes(), dbg_h[i], ref, d, bits, kind, stats)
+    print(f"d={d} bits={bits} kind={kind}: {stats['code_mismatch']} of {stats['codes']} codes differ (ties)")
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+def test_seal_iteration_count(iters):
+    x = _tiles(128, 3, seed=40 + iters)
+    dbg = torch.zeros(len(x), 256, dtype=torch.float32, device="cuda")
+    recs = K.seal_tiles(torch.from_numpy(x).cuda(), 2, "k", dbg=dbg, iters=iters).cpu().numpy()
+    for i in range(len(x)):
+        check_sealed_tile(recs[i].tobytes(), dbg[i].cpu().numpy(), O.seal_tile(x[i], 2, iters=iters), 128, 2, "k")
+
+
+def test_seal_record_stride():
+    x = _tiles(128, 2, seed=3)
+    out = torch.full((len(x), 4608 + 128), 0xAB, dtype=torch.uint8, device="cuda")
+    K.seal_tiles(torch.from_numpy(x).cuda(), 2, "v", out=out)
+    h = out.cpu().numpy()
+    assert np.all(h[:, 4608:] == 0xAB)   # padding untouched
+    for i in range(len(x)):
+        check_sealed_tile(h[i, :4608].tobytes(), None, O.seal_tile(x[i], 2), 128, 2, "v")
