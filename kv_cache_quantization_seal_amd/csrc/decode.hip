@@ -51,7 +51,8 @@ struct alignas(16) DecodeSmem {
       alignas(16) uint16_t meta[kWaves][2][kGroup + D];  // [K|V][s(128) c(D)] fp16
     } rec;
     struct {
-      float p[kWaves][GQ][64];
+      alignas(16) uint16_t v[kWaves][32][D + 8];  // V rows of the wave's 32 exact tokens (fp16)
+      alignas(16) float p[kWaves][32][4];          // softmax numerators [token][head]
     } ex;
   } u;
   float mm[kWaves][GQ];
@@ -328,56 +329,67 @@ __device__ void record_split(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, 
   }
 }
 
+// Exact part: the sink and the tail, fp16, original frame.  Exact split es
+// covers exact tokens [128 es, 128 es + 128); wave w takes 32 of them, lane
+// (token, half) holds half a K row and half a V row.  QK: fp32 FMAs against
+// the LDS query; PV: V rows staged in LDS, lane = channel group.
 template <int D, int GQ>
-__device__ void exact_split(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int n) {
+__device__ void exact_split(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int n) {
+  constexpr int HALF = D / 2;
   constexpr int CPLX = D / 64;  // channels per lane in the PV part
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int half = l >> 5, tl = l & 31;
   const int n_sink = min(n, kSink);
   const int tau = n > kSink ? (n - kSink) % kGroup : 0;
-  const int n_exact = n_sink + tau;
+  const int n_exact = max(0, n_sink + tau);
   const int64_t bh = (int64_t)b * a.c.hkv + kvh;
-  const int e = 64 * w + l;
+  const int e = kGroup * es + 32 * w + tl;
   const bool valid = e < n_exact;
-  const __half* krow = nullptr;
-  if (valid)
-    krow = (e < n_sink ? a.c.sink_k + (bh * kGroup + e) * D : a.c.tail_k + (bh * kGroup + (e - n_sink)) * D);
   float dot[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
+  uint16_t* vrow = &sm.u.ex.v[w][tl][half * HALF];
   if (valid) {
-#pragma unroll 4
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      const uint4 kv = reinterpret_cast<const uint4*>(krow)[c8];
-      const uint32_t ws[4] = {kv.x, kv.y, kv.z, kv.w};
-      float kf[8];
+    const size_t row = e < n_sink ? (size_t)(bh * kGroup + e) : (size_t)(bh * kGroup + (e - n_sink));
+    const uint4* kp = reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_k : a.c.tail_k) + row * D + half * HALF);
+    const uint4* vp = reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_v : a.c.tail_v) + row * D + half * HALF);
+    uint4 kr[HALF / 8], vr[HALF / 8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kf[2 * i] = h2f((uint16_t)(ws[i] & 0xFFFFu));
-        kf[2 * i + 1] = h2f((uint16_t)(ws[i] >> 16));
-      }
+    for (int c = 0; c < HALF / 8; ++c) {
+      kr[c] = kp[c];
+      vr[c] = vp[c];
+    }
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = vr[c];
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) {
+      const uint32_t ws[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const float4 qa = *reinterpret_cast<const float4*>(&sm.qx[h][8 * c8]);
-        const float4 qb = *reinterpret_cast<const float4*>(&sm.qx[h][8 * c8 + 4]);
-        dot[h] = fmaf(qa.x, kf[0], dot[h]);
-        dot[h] = fmaf(qa.y, kf[1], dot[h]);
-        dot[h] = fmaf(qa.z, kf[2], dot[h]);
-        dot[h] = fmaf(qa.w, kf[3], dot[h]);
-        dot[h] = fmaf(qb.x, kf[4], dot[h]);
-        dot[h] = fmaf(qb.y, kf[5], dot[h]);
-        dot[h] = fmaf(qb.z, kf[6], dot[h]);
-        dot[h] = fmaf(qb.w, kf[7], dot[h]);
+        const float4 qa = *reinterpret_cast<const float4*>(&sm.qx[h][half * HALF + 8 * c]);
+        const float4 qb = *reinterpret_cast<const float4*>(&sm.qx[h][half * HALF + 8 * c + 4]);
+        dot[h] = fmaf(qa.x, h2f((uint16_t)(ws[0] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qa.y, h2f((uint16_t)(ws[0] >> 16)), dot[h]);
+        dot[h] = fmaf(qa.z, h2f((uint16_t)(ws[1] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qa.w, h2f((uint16_t)(ws[1] >> 16)), dot[h]);
+        dot[h] = fmaf(qb.x, h2f((uint16_t)(ws[2] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qb.y, h2f((uint16_t)(ws[2] >> 16)), dot[h]);
+        dot[h] = fmaf(qb.z, h2f((uint16_t)(ws[3] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qb.w, h2f((uint16_t)(ws[3] >> 16)), dot[h]);
       }
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = make_uint4(0, 0, 0, 0);
   }
   float mh[GQ], lh[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const float lg = valid ? dot[h] : -INFINITY;
+    const float lg = valid ? dot[h] + __shfl_xor(dot[h], 32, 64) : -INFINITY;
     mh[h] = wave_max(lg);
     const float p = (valid && mh[h] != -INFINITY) ? exp2f(lg - mh[h]) : 0.f;
-    lh[h] = wave_sum(p);
-    sm.u.ex.p[w][h][l] = p;
+    lh[h] = wave_sum(half == 0 ? p : 0.f);
+    if (half == 0) sm.u.ex.p[w][tl][h] = p;
   }
   wave_sync();
   float o[GQ][CPLX];
@@ -385,28 +397,26 @@ __device__ void exact_split(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, i
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
     for (int c = 0; c < CPLX; ++c) o[h][c] = 0.f;
-  const int e_end = min(64 * w + 64, n_exact);
-  for (int ee = 64 * w; ee < e_end; ++ee) {
-    const __half* vrow = ee < n_sink ? a.c.sink_v + (bh * kGroup + ee) * D
-                                     : a.c.tail_v + (bh * kGroup + (ee - n_sink)) * D;
+  const int nt = min(32, max(0, n_exact - (kGroup * es + 32 * w)));
+  for (int t = 0; t < nt; ++t) {
+    const float4 pv = *reinterpret_cast<const float4*>(&sm.u.ex.p[w][t][0]);
+    const float ph[4] = {pv.x, pv.y, pv.z, pv.w};
     float vf[CPLX];
     if constexpr (CPLX == 2) {
-      const uint32_t x = reinterpret_cast<const uint32_t*>(vrow)[l];
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(&sm.u.ex.v[w][t][2 * l]);
       vf[0] = h2f((uint16_t)(x & 0xFFFFu));
       vf[1] = h2f((uint16_t)(x >> 16));
     } else {
-      const uint2 x = reinterpret_cast<const uint2*>(vrow)[l];
+      const uint2 x = *reinterpret_cast<const uint2*>(&sm.u.ex.v[w][t][4 * l]);
       vf[0] = h2f((uint16_t)(x.x & 0xFFFFu));
       vf[1] = h2f((uint16_t)(x.x >> 16));
       vf[2] = h2f((uint16_t)(x.y & 0xFFFFu));
       vf[3] = h2f((uint16_t)(x.y >> 16));
     }
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const float p = sm.u.ex.p[w][h][ee - 64 * w];
+    for (int h = 0; h < GQ; ++h)
 #pragma unroll
-      for (int c = 0; c < CPLX; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
-    }
+      for (int c = 0; c < CPLX; ++c) o[h][c] = fmaf(ph[h], vf[c], o[h][c]);
   }
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
@@ -439,43 +449,99 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (split < a.n_rec_splits)
     record_split<D, KB, VB, GQ>(sm, a, b, kvh, split, n);
   else
-    exact_split<D, GQ>(sm, a, b, kvh, n);
+    exact_split<D, GQ>(sm, a, b, kvh, split - a.n_rec_splits, n);
   merge_and_store<D, GQ>(sm, a, b, kvh, split);
 }
 
-// One workgroup (D threads) per (query head, request): log-sum-exp merge of
+// One workgroup (256 threads) per (query head, request): log-sum-exp merge of
 // all splits, one inverse Hadamard of the record part, normalization.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  __shared__ float buf[D];
-  const int hq = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int MAXS = 1024;  // splits handled per pass of the weight table
+  __shared__ float wgt[MAXS];
+  __shared__ float red[256];
+  __shared__ float orot[D];
+  __shared__ float oex[D];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t base = ((int64_t)b * a.hq + hq) * a.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_ml[2 * (base + s)]);
-  float L = 0.f, orot = 0.f, oex = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.ws_ml[2 * (base + s)];
-      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      L = fmaf(f, a.ws_ml[2 * (base + s) + 1], L);
-      const float v = f * a.ws_o[(base + s) * D + j];
-      if (s < a.n_rec_splits)
-        orot += v;
+  // Global max over splits.
+  float m = -INFINITY;
+  for (int s = tid; s < a.nsplit; s += 256) m = fmaxf(m, a.ws_ml[2 * (base + s)]);
+  red[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int idx = tid; idx < D; idx += 256) {
+    orot[idx] = 0.f;
+    oex[idx] = 0.f;
+  }
+  // Channel partial sums: thread (j, part) sums splits part, part + P, ...
+  constexpr int P = 256 / D;  // 2 for D = 128, 1 for D = 256
+  const int j = tid % D, part = tid / D;
+  float accr = 0.f, acce = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += MAXS) {
+    const int cnt = min(MAXS, a.nsplit - s0);
+    __syncthreads();
+    for (int s = tid; s < cnt; s += 256) {
+      const float ms = a.ws_ml[2 * (base + s0 + s)];
+      const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      wgt[s] = f;
+      lsum = fmaf(f, a.ws_ml[2 * (base + s0 + s) + 1], lsum);
+    }
+    __syncthreads();
+    int s = part;
+    for (; s + 7 * P < cnt; s += 8 * P) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.ws_o[(base + s0 + s + u * P) * D + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ss = s0 + s + u * P;
+        if (ss < a.n_rec_splits)
+          accr = fmaf(wgt[s + u * P], v[u], accr);
+        else
+          acce = fmaf(wgt[s + u * P], v[u], acce);
+      }
+    }
+    for (; s < cnt; s += P) {
+      const float v = a.ws_o[(base + s0 + s) * D + j];
+      if (s0 + s < a.n_rec_splits)
+        accr = fmaf(wgt[s], v, accr);
       else
-        oex += v;
+        acce = fmaf(wgt[s], v, acce);
     }
   }
-  buf[j] = orot;
+  red[tid] = lsum;
   __syncthreads();
-  for (int s = 1; s < D; s <<= 1) {
-    const float x = buf[j], y = buf[j ^ s];
-    __syncthreads();
-    buf[j] = (j & s) ? y - x : x + y;
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
-  const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
-  const float o = L > 0.f ? (buf[j] * rs + oex) / L : 0.f;
-  a.out[((int64_t)b * a.hq + hq) * D + j] = o;
+  const float L = red[0];
+  atomicAdd(&orot[j], accr);
+  atomicAdd(&oex[j], acce);
+  __syncthreads();
+  // Inverse rotation of the record part (H symmetric): orot <- orot H.
+  for (int st = 1; st < D; st <<= 1) {
+    float x = 0.f, y = 0.f;
+    if (tid < D) {
+      x = orot[tid];
+      y = orot[tid ^ st];
+    }
+    __syncthreads();
+    if (tid < D) orot[tid] = (tid & st) ? y - x : x + y;
+    __syncthreads();
+  }
+  if (tid < D) {
+    const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
+    const float o = L > 0.f ? (orot[tid] * rs + oex[tid]) / L : 0.f;
+    a.out[((int64_t)b * a.hq + hq) * D + tid] = o;
+  }
 }
 
 DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups) {
@@ -487,7 +553,7 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups) {
   p.groups_per_wave = gpw;
   p.groups_per_split = kWaves * gpw;
   p.n_rec_splits = max_groups > 0 ? (max_groups + p.groups_per_split - 1) / p.groups_per_split : 0;
-  p.n_exact_splits = 1;
+  p.n_exact_splits = 2;  // exact tokens [0,128) and [128,256)
   p.nsplit = p.n_rec_splits + p.n_exact_splits;
   const size_t rows = (size_t)batch * hq * p.nsplit;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
@@ -500,7 +566,7 @@ static void launch_t(const DecodeArgs& a, int phases, hipStream_t st) {
   if (phases & 1)
     hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, GQ>), dim3(a.nsplit, a.c.hkv, a.c.batch), dim3(256), 0, st,
                        a);
-  if (phases & 2) hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.hq, a.c.batch), dim3(D), 0, st, a);
+  if (phases & 2) hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.hq, a.c.batch), dim3(256), 0, st, a);
 }
 
 template <int D, int KB, int VB>
