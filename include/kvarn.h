@@ -156,7 +156,8 @@ kvarn_status kvarn_prefill(const kvarn_config *cfg, const kvarn_cache *cache,
  * rotated back once.  out: device fp32 [batch][Hq][D].  softmax_scale
  * multiplies q.k (use 1/sqrt(D)).  workspace: device, at least
  * kvarn_decode_workspace_bytes(cfg, batch, max_groups) bytes, 256-byte
- * aligned; its contents are scratch.  A request with seq_len 0 gets zeros.
+ * aligned; its contents are scratch, and calls sharing a workspace must not
+ * overlap.  A request with seq_len 0 gets zeros.
  */
 kvarn_status kvarn_decode_attn(const kvarn_config *cfg, const kvarn_cache *cache,
                                const void *q, float *out, float softmax_scale,

@@ -22,6 +22,7 @@ SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 

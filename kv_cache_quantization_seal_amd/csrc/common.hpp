@@ -28,19 +28,25 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Reductions across the 16 lanes of one row (lanes 16r .. 16r+15).
+// Reductions across the 16 lanes of one DPP row (lanes 16r .. 16r+15), every
+// lane receiving the result: swap neighbours, swap pairs, mirror within the
+// half row, mirror within the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 16));
-  v = fmaxf(v, __shfl_xor(v, 2, 16));
-  v = fmaxf(v, __shfl_xor(v, 4, 16));
-  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1, 16);
-  v += __shfl_xor(v, 2, 16);
-  v += __shfl_xor(v, 4, 16);
-  v += __shfl_xor(v, 8, 16);
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
@@ -80,6 +86,31 @@ __device__ __forceinline__ v4i unpack16(const uint32_t* w) {
     r[3] = (int)((w[1] >> 4) & 0x0F0F0F0Fu);
   }
   return r;
+}
+
+// Magic-number rounding: for |x| < 2^22, x + 1.5*2^23 rounds x to the nearest
+// integer (ties to even) in the low mantissa bits, whose low byte is then
+// rint(x) as a two's complement int8.
+constexpr float kMagic = 12582912.0f;
+
+// Three radix-128 int8 limbs of the real number y*inv (|y*inv| <= 127.5):
+// y*inv ~ a0 + a1/128 + a2/128^2, |error| <= 0.5/128^2.  Returns the three
+// magic-rounded floats; limb i is the low byte of f[i].
+__device__ __forceinline__ void limbs_r128(float y, float inv, float& f0, float& f1, float& f2) {
+  f0 = fmaf(y, inv, kMagic);
+  const float a0 = f0 - kMagic;
+  const float t1 = fmaf(y, inv, -a0);
+  f1 = fmaf(t1, 128.0f, kMagic);
+  const float a1 = f1 - kMagic;
+  const float t2 = fmaf(t1, 128.0f, -a1);
+  f2 = fmaf(t2, 128.0f, kMagic);
+}
+
+// Low bytes of four magic-rounded floats -> one dword (byte 0 = first).
+__device__ __forceinline__ uint32_t pack_low_bytes(float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Split x (|x| <= 127.5) into three int8 limbs a0 + a1/254 + a2/254^2 with

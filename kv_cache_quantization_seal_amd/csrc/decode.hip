@@ -9,16 +9,22 @@
 // original frame; records are read directly, never expanded in memory (same
 // page, §2.1 "Sink, Body, And Tail").
 //
-// Record part (one wavefront per 128-token group, GQ query heads sharing it):
-//   logit_t = s^K_t * sum_j q~_j (code_tj - mid) with q~ = q_r * c^K * scale,
-//   w_t = p_t * s^V_t,   o_rot_j += c^V_j * sum_t w_t (code_tj - mid).
-// Both sums run on v_mfma_i32_16x16x64_i8.  The codes are exact int8
-// operands.  q~ (per group, per head) and w (per group, per head) are split
-// into three int8 limbs x ~ E (a0 + a1/254 + a2/254^2) with |x - ...| <=
-// E/(2*254^2) relative to the group maximum E/127; the 16 MFMA rows carry
-// (head, limb) pairs, so one lane ends up with all limbs of one head and
-// recombines them exactly: 2 C_i - (2^b - 1) S_i is an exact integer (S_i =
-// limb sum), converted once to fp32.
+// Record splits.  A workgroup (4 waves) walks a range of 128-token groups of
+// one (request, KV head).  Each group's K and V records are copied into a
+// double-buffered LDS slot (the next group's loads are in flight while the
+// current one is computed) and the four waves share the work:
+//   logit_t = s^K_t * sum_j q~_j (code_tj - mid),  q~ = q_r * c^K * scale,
+//   w_t = p_t * s^V_t,  o_rot_j += c^V_j * sum_t w_t (code_tj - mid).
+// Both sums run on v_mfma_i32_16x16x64_i8 with the codes as exact int8
+// operands.  q~ and w are split into three radix-128 int8 limbs
+// x * inv ~ a0 + a1/128 + a2/128^2 (|error| <= 0.5/128^2 of the group maximum
+// scaled to the top-limb range); the 16 MFMA rows carry (head, limb) pairs,
+// so each lane holds every limb of one head and recombines them exactly in
+// int32, with one conversion to fp32.
+//   wave h < GQ : q~ limbs of head h;
+//   wave w      : QK for token tiles nt = 2w, 2w+1; PV for channel tiles
+//                 ct = w*(D/64) .. w*(D/64) + D/64 - 1.
+// Softmax maxima per head are exchanged through LDS (base-2 online softmax).
 //
 // Operand layouts (lane l, lane group G = l/16, n = l%16):
 //   * B operand of QK = K codes: column n of N-tile nt is token tok(nt, n);
@@ -31,8 +37,8 @@
 //     unpack_index<VB>(p).
 //   * B operand of PV = V codes (channel-major rows): column n of N-tile ct
 //     is channel 16 ct + n, same token slots.
-//   tok(nt, n) = 16 (n/2) + unpack_index<VB>(8 (n%2) + nt) makes the w limbs
-//   of one lane land on 8 consecutive LDS bytes.
+//   tok(nt, n) = 16 (n/2) + unpack_index<VB>(8 (n%2) + nt): the w limbs of
+//   lane n sit at LDS bytes 8n + nt.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,21 +46,45 @@ namespace kvarn {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
+constexpr int kExactTok = 16;  // exact tokens per wave per round
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <int D, int KB, int VB>
+struct RecGeom {
+  static constexpr int KS = D / 64;                      // QK K-steps
+  static constexpr int NCT = D / 16;                     // PV channel tiles
+  static constexpr int CTW = NCT / kWaves;               // channel tiles per wave
+  static constexpr int LBK = KS * 2 * KB;                // K-code bytes per lane per token
+  static constexpr int LBV = 4 * VB;                     // V-code bytes per lane per channel
+  static constexpr int KROW = D * KB / 8;                // bytes of one token row of K codes
+  static constexpr int VROW = kGroup * VB / 8;           // bytes of one channel row of V codes
+  static constexpr int KCODE = kGroup * D * KB / 8;
+  static constexpr int VCODE = kGroup * D * VB / 8;
+  static constexpr int KREC = KCODE + 2 * kGroup + 2 * D;
+  static constexpr int VREC = VCODE + 2 * kGroup + 2 * D;
+  static constexpr int GB = KREC + VREC;                 // staged bytes per group
+  static constexpr int CHUNKS = GB / 16;
+  static constexpr int CPT = (CHUNKS + 255) / 256;       // 16-byte chunks per thread
+};
+
+template <int D, int KB, int VB, int GQ>
+struct alignas(16) RecSmem {
+  alignas(16) uint8_t buf[2][RecGeom<D, KB, VB>::GB];  // staged K record | V record
+  alignas(16) uint8_t ql[GQ][3][D];                    // q~ limbs, operand order
+  alignas(16) uint8_t wl[GQ][3][kGroup];               // w limbs, operand order
+  float qx[GQ][D];                                     // scaled query, rotated in place
+  float e[GQ];                                         // q~ maximum per head (this group)
+  float pmax[kWaves][GQ];                              // per-wave partial maxima
+  float lsum[kWaves][GQ];
+};
 
 template <int D, int GQ>
-struct alignas(16) DecodeSmem {
-  alignas(16) float qx[GQ][D];  // scaled query (original frame, then rotated in place)
-  union alignas(16) {
-    struct {
-      alignas(16) uint8_t ql[kWaves][4][3][D];        // q~ limbs in operand order
-      alignas(16) uint8_t wl[kWaves][4][3][kGroup];   // w limbs in operand order
-      alignas(16) uint16_t meta[kWaves][2][kGroup + D];  // [K|V][s(128) c(D)] fp16
-    } rec;
-    struct {
-      alignas(16) uint16_t v[kWaves][32][D + 8];  // V rows of the wave's 32 exact tokens (fp16)
-      alignas(16) float p[kWaves][32][4];          // softmax numerators [token][head]
-    } ex;
-  } u;
+struct alignas(16) ExactSmem {
+  alignas(16) uint16_t v[kWaves][kExactTok][D + 8];  // V rows of one round (fp16)
+  alignas(16) float p[kWaves][kExactTok][4];         // softmax numerators [token][head]
+  float qx[GQ][D];
   float mm[kWaves][GQ];
   float ll[kWaves][GQ];
   float oo[kWaves][GQ][D];
@@ -65,392 +95,444 @@ __device__ __forceinline__ int tok_of(int nt, int n) {
   return 16 * (n >> 1) + unpack_index<VB>(8 * (n & 1) + nt);
 }
 
-template <int NBYTES>
-__device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src) {
-  if constexpr (NBYTES == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(src);
-    dst[0] = v.x;
-    dst[1] = v.y;
-  } else {
-#pragma unroll
-    for (int k = 0; k < NBYTES / 16; ++k) {
-      const uint4 v = reinterpret_cast<const uint4*>(src)[k];
-      dst[4 * k] = v.x;
-      dst[4 * k + 1] = v.y;
-      dst[4 * k + 2] = v.z;
-      dst[4 * k + 3] = v.w;
-    }
-  }
+// Buffer resource over `bytes` bytes at a wave-uniform base; loads past the
+// end return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-// Merge the per-wave (m, l, o) of the workgroup and write one partial.
-template <int D, int GQ>
-__device__ __forceinline__ void merge_and_store(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh,
-                                                int split) {
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GQ * D; idx += blockDim.x) {
-    const int h = idx / D, ch = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.mm[w][h]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.mm[w][h];
-        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        L = fmaf(f, sm.ll[w][h], L);
-        O = fmaf(f, sm.oo[w][h][ch], O);
-      }
-    }
-    const int64_t row = ((int64_t)b * a.hq + kvh * GQ + h) * a.nsplit + split;
-    a.ws_o[row * D + ch] = O;
-    if (ch == 0) {
-      a.ws_ml[2 * row] = M;
-      a.ws_ml[2 * row + 1] = L;
-    }
-  }
+// Largest |top limb| so that sum_j A_j (2 code_j - L) fits int32, with
+// A_j = a0*2^14 + a1*2^7 + a2 and |a1|,|a2| <= 64, over k_terms terms.
+__host__ __device__ constexpr float top_limb(int k_terms, int levels) {
+  return (k_terms * levels <= 768) ? 127.0f : (k_terms * levels <= 1920 ? 63.0f : 31.0f);
 }
 
+__device__ __forceinline__ void store_partial_ml(const DecodeArgs& a, int b, int hq_idx, int split, float m, float l) {
+  const int64_t row = ((int64_t)b * a.hq + hq_idx) * a.nsplit + split;
+  a.ws_ml[2 * row] = m;
+  a.ws_ml[2 * row + 1] = l;
+}
+
+// ---------------------------------------------------------------------------
+// Record split (workgroup-cooperative)
+// ---------------------------------------------------------------------------
 template <int D, int KB, int VB, int GQ>
-__device__ void record_split(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int split, int nseq) {
-  constexpr int KS = D / 64;              // QK K-steps
-  constexpr int CPL = D / 16;             // q~ values produced per lane
-  constexpr int LBK = KS * 2 * KB;        // K-code bytes per lane per token
-  constexpr int LBV = 2 * 2 * VB;         // V-code bytes per lane per channel
-  constexpr int KROW = D * KB / 8;        // bytes per token row of K codes
-  constexpr int VROW = kGroup * VB / 8;   // bytes per channel row of V codes
-  constexpr int KCODE = kGroup * D * KB / 8;
-  constexpr int VCODE = kGroup * D * VB / 8;
-  constexpr int NCT = D / 16;             // PV N-tiles
-  constexpr int LK = (1 << KB) - 1;
-  constexpr int LV = (1 << VB) - 1;
-  constexpr int META_CHUNKS = (kGroup + D) * 2 / 16;  // 16-byte chunks per K or V meta
+__device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, int b, int kvh, int split,
+                             int nseq) {
+  using Gm = RecGeom<D, KB, VB>;
+  constexpr int KS = Gm::KS, CTW = Gm::CTW, CPT = Gm::CPT;
+  constexpr int LK = (1 << KB) - 1, LV = (1 << VB) - 1;
+  constexpr float QMAX = top_limb(D, LK);
+  constexpr float WMAX = top_limb(kGroup, LV);
+  constexpr int QPL = D / 64;  // q~ values produced per lane (wave h < GQ)
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
   const int G = l >> 4, n = l & 15;
   const bool hvalid = G < GQ;
+  const int hm = n >> 2, im = n & 3;  // A-operand row of this lane: (head, limb)
+  const bool arow_valid = hm < GQ && im < 3;
 
-  // Rotate the scaled query in place: qx <- qx H_D / sqrt(D).
+  const uint8_t* recs = a.c.records + (((int64_t)b * a.c.hkv + kvh) * a.c.max_groups) * a.c.group_bytes;
+  const int g0 = split * a.groups_per_split;
+  const int gcap = min(g0 + a.groups_per_split, a.c.max_groups);  // slots that exist
+  const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
+  const int g1 = min(gcap, n_groups);
+
+  // The first group's stage loads go out before anything else (the slot
+  // exists, so the load is safe before seq_len decides whether it is used).
+  v4u stage[CPT];
+  auto load_stage = [&](int g) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(recs + (int64_t)g * a.c.group_bytes, Gm::GB);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) stage[k] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * k), 0, 0);
+  };
+  auto store_stage = [&](uint8_t* dst) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      if (tid + 256 * k < Gm::CHUNKS) *reinterpret_cast<v4u*>(dst + 16 * (tid + 256 * k)) = stage[k];
+  };
+  if (g0 < gcap) load_stage(g0);
+
+  // Scaled query (log2 domain) of the GQ heads, rotated: qx <- qx H_D.
+  for (int idx = tid; idx < GQ * D; idx += 256) {
+    const int h = idx / D, j = idx % D;
+    sm.qx[h][j] = __half2float(a.q[((int64_t)b * a.hq + kvh * GQ + h) * D + j]) * a.scale * kLog2e;
+  }
+  __syncthreads();
   for (int s = 1; s < D; s <<= 1) {
-    for (int idx = threadIdx.x; idx < GQ * D / 2; idx += blockDim.x) {
-      const int h = idx / (D / 2), r = idx % (D / 2);
-      const int lo = ((r & ~(s - 1)) << 1) | (r & (s - 1));
+    for (int idx = tid; idx < GQ * D / 2; idx += 256) {
+      const int h = idx / (D / 2), rr = idx % (D / 2);
+      const int lo = ((rr & ~(s - 1)) << 1) | (rr & (s - 1));
       const float x0 = sm.qx[h][lo], x1 = sm.qx[h][lo + s];
       sm.qx[h][lo] = x0 + x1;
       sm.qx[h][lo + s] = x0 - x1;
     }
     __syncthreads();
   }
+  // q~ producer (wave w < GQ, head w): operand bytes [QPL*l, QPL*l + QPL).
   const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
-  float qr[CPL];
-  int chq[CPL];
+  float qr[QPL];
+  int qch[QPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    const int ob = n * CPL + e;
-    chq[e] = 16 * (ob >> 4) + unpack_index<KB>(ob & 15);
-    qr[e] = hvalid ? sm.qx[G][chq[e]] * rs : 0.f;
+  for (int e = 0; e < QPL; ++e) {
+    const int ob = QPL * l + e;
+    qch[e] = 16 * (ob >> 4) + unpack_index<KB>(ob & 15);
+    qr[e] = w < GQ ? sm.qx[w][qch[e]] * rs : 0.f;
   }
+  if (g0 < g1) store_stage(sm.buf[0]);
+  __syncthreads();
 
-  const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
-  const int g0 = split * a.groups_per_split;
-  const int g1 = min(g0 + a.groups_per_split, n_groups);
+  float m_run = -INFINITY, l_run = 0.f;  // head G (replicated in every wave)
+  float o_acc[CTW];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) o_acc[c] = 0.f;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float o_acc[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) o_acc[ct] = 0.f;
+  for (int g = g0, it = 0; g < g1; ++g, ++it) {
+    const uint8_t* cur = sm.buf[it & 1];
+    const bool more = g + 1 < g1;
+    if (more) load_stage(g + 1);
+    const uint16_t* sk16 = reinterpret_cast<const uint16_t*>(cur + Gm::KCODE);
+    const uint16_t* ck16 = sk16 + kGroup;
+    const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(cur + Gm::KREC + Gm::VCODE);
+    const uint16_t* cv16 = sv16 + kGroup;
 
-  const int mrow = n;  // A-operand row of this lane: (head mrow/4, limb mrow%4)
-  const int hm = mrow >> 2, im = mrow & 3;
-  const bool arow_valid = hm < GQ && im < 3;
-  uint8_t* qlw = &sm.u.rec.ql[w][0][0][0];
-  uint8_t* wlw = &sm.u.rec.wl[w][0][0][0];
-  uint16_t* metaw = &sm.u.rec.meta[w][0][0];
-
-  for (int g = g0 + w; g < g1; g += kWaves) {
-    const uint8_t* rec = a.c.records + (((int64_t)b * a.c.hkv + kvh) * a.c.max_groups + g) * a.c.group_bytes;
-    const uint8_t* vrec = rec + a.c.rec_k_bytes;
-    // Scale metadata -> LDS (K: s, c; V: s, c), 16-byte chunks.
-    for (int i = l; i < 2 * META_CHUNKS; i += kWave) {
-      const int kind = i / META_CHUNKS, c = i % META_CHUNKS;
-      const uint8_t* srcm = kind ? vrec + VCODE : rec + KCODE;
-      reinterpret_cast<uint4*>(metaw + kind * (kGroup + D))[c] = reinterpret_cast<const uint4*>(srcm)[c];
-    }
-    // Code operands straight to registers.
-    uint32_t kc[8][LBK / 4];
+    // (A) q~ limbs of head w.
+    if (w < GQ) {
+      float y[QPL];
+      float ym = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      load_bytes<LBK>(kc[nt], rec + tok_of<VB>(nt, n) * KROW + G * LBK);
-    uint32_t vc[NCT][LBV / 4];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) load_bytes<LBV>(vc[ct], vrec + (16 * ct + n) * VROW + G * LBV);
-    wave_sync();
-
-    // q~ = q_r * c^K for this lane's channels, limbs into LDS.
-    const uint16_t* ck = metaw + kGroup;
-    float y[CPL];
-    float ymax = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      y[e] = qr[e] * h2f(ck[chq[e]]);
-      ymax = fmaxf(ymax, fabsf(y[e]));
-    }
-    const float E = row16_max(ymax);
-    const float qinv = E > 0.f ? 127.0f / E : 0.f;
-    float ssum0 = 0.f, ssum1 = 0.f, ssum2 = 0.f;
-    if (hvalid) {
-#pragma unroll
-      for (int e4 = 0; e4 < CPL / 4; ++e4) {
-        float l0[4], l1[4], l2[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          limbs3(y[4 * e4 + e] * qinv, l0[e], l1[e], l2[e]);
-          ssum0 += l0[e];
-          ssum1 += l1[e];
-          ssum2 += l2[e];
-        }
-        uint32_t* q0 = reinterpret_cast<uint32_t*>(qlw + (G * 3 + 0) * D + n * CPL) + e4;
-        uint32_t* q1 = reinterpret_cast<uint32_t*>(qlw + (G * 3 + 1) * D + n * CPL) + e4;
-        uint32_t* q2 = reinterpret_cast<uint32_t*>(qlw + (G * 3 + 2) * D + n * CPL) + e4;
-        *q0 = pack4_i8(l0[0], l0[1], l0[2], l0[3]);
-        *q1 = pack4_i8(l1[0], l1[1], l1[2], l1[3]);
-        *q2 = pack4_i8(l2[0], l2[1], l2[2], l2[3]);
+      for (int e = 0; e < QPL; ++e) {
+        y[e] = qr[e] * h2f(ck16[qch[e]]);
+        ym = fmaxf(ym, fabsf(y[e]));
       }
+      const float E = wave_max(ym);
+      const float inv = E > 0.f ? QMAX * __builtin_amdgcn_rcpf(E) : 0.f;
+      float f0[QPL], f1[QPL], f2[QPL];
+#pragma unroll
+      for (int e = 0; e < QPL; ++e) limbs_r128(y[e], inv, f0[e], f1[e], f2[e]);
+      uint8_t* base = &sm.ql[w][0][QPL * l];
+      if constexpr (QPL == 2) {
+        const uint32_t b0 = __builtin_amdgcn_perm(__float_as_uint(f0[1]), __float_as_uint(f0[0]), 0x0c0c0400u);
+        const uint32_t b1 = __builtin_amdgcn_perm(__float_as_uint(f1[1]), __float_as_uint(f1[0]), 0x0c0c0400u);
+        const uint32_t b2 = __builtin_amdgcn_perm(__float_as_uint(f2[1]), __float_as_uint(f2[0]), 0x0c0c0400u);
+        *reinterpret_cast<uint16_t*>(base) = (uint16_t)b0;
+        *reinterpret_cast<uint16_t*>(base + D) = (uint16_t)b1;
+        *reinterpret_cast<uint16_t*>(base + 2 * D) = (uint16_t)b2;
+      } else {
+        *reinterpret_cast<uint32_t*>(base) = pack_low_bytes(f0[0], f0[1], f0[2], f0[3]);
+        *reinterpret_cast<uint32_t*>(base + D) = pack_low_bytes(f1[0], f1[1], f1[2], f1[3]);
+        *reinterpret_cast<uint32_t*>(base + 2 * D) = pack_low_bytes(f2[0], f2[1], f2[2], f2[3]);
+      }
+      if (l == 0) sm.e[w] = E;
     }
-    const int S0 = (int)row16_sum(ssum0), S1 = (int)row16_sum(ssum1), S2 = (int)row16_sum(ssum2);
-    wave_sync();
+    __syncthreads();  // B1: q~ limbs ready
+
+    // (B) QK for token tiles 2w, 2w+1.
     v4i aq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (arow_valid) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qlw + (hm * 3 + im) * D + 16 * (G * KS + s));
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ql[hm][im][16 * (G * KS + s)]);
         aq[s] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
       } else {
         aq[s] = v4i{0, 0, 0, 0};
       }
     }
-
-    // QK on MFMA; recombine the limbs into base-2 logits.
-    const uint16_t* sk = metaw;
-    const uint16_t* sv = metaw + (kGroup + D);
-    const float kscale = E * (0.5f / 127.0f);
-    float logit[8];
-    float gmax = -INFINITY;
+    v4i sacc = {0, 0, 0, 0};
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], ones, sacc, 0, 0, 0);
+    const uint32_t negls =
+        0u - (uint32_t)LK * (((uint32_t)sacc[0] << 14) + ((uint32_t)sacc[1] << 7) + (uint32_t)sacc[2]);
+    const float kscale = (hvalid ? sm.e[G] : 0.f) * (1.0f / (QMAX * 32768.0f));
+    float logit[2];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int nt = 2 * w + t;
+      const int tok = tok_of<VB>(nt, n);
+      const uint8_t* kp = cur + tok * Gm::KROW + G * Gm::LBK;
+      uint32_t kw[Gm::LBK / 4];
+#pragma unroll
+      for (int k = 0; k < Gm::LBK / 4; ++k) kw[k] = reinterpret_cast<const uint32_t*>(kp)[k];
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack16<KB>(&kc[nt][s * (2 * KB / 4)]), acc, 0, 0, 0);
-      const float f0 = (float)(2 * acc[0] - LK * S0);
-      const float f1 = (float)(2 * acc[1] - LK * S1);
-      const float f2 = (float)(2 * acc[2] - LK * S2);
-      const float f = fmaf(fmaf(f2, 1.0f / 254.0f, f1), 1.0f / 254.0f, f0);
-      const int tok = tok_of<VB>(nt, n);
-      logit[nt] = hvalid ? f * kscale * h2f(sk[tok]) : -INFINITY;
-      gmax = fmaxf(gmax, logit[nt]);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack16<KB>(&kw[s * (KB / 2)]), acc, 0, 0, 0);
+      const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
+      const int yv = (int)((x << 1) + negls);
+      logit[t] = hvalid ? (float)yv * (h2f(sk16[tok]) * kscale) : -INFINITY;
+      lmax = fmaxf(lmax, logit[t]);
     }
-    gmax = row16_max(gmax);
-    const float m_new = fmaxf(m_run, gmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f, wmax = 0.f;
-    float wv[8];
+    lmax = row16_max(lmax);
+    if (n == 0 && hvalid) sm.pmax[w][G] = lmax;
+    __syncthreads();  // B2: logit maxima
+    float gmax = -INFINITY;
+    if (hvalid) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const float p = hvalid ? exp2f(logit[nt] - m_new) : 0.f;
+      for (int k = 0; k < kWaves; ++k) gmax = fmaxf(gmax, sm.pmax[k][G]);
+    }
+    const float m_new = fmaxf(m_run, gmax);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float wv[2];
+    float psum = 0.f, wmax = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float p = hvalid ? __builtin_amdgcn_exp2f(logit[t] - m_new) : 0.f;
       psum += p;
-      wv[nt] = p * h2f(sv[tok_of<VB>(nt, n)]);
-      wmax = fmaxf(wmax, wv[nt]);
+      wv[t] = p * h2f(sv16[tok_of<VB>(2 * w + t, n)]);
+      wmax = fmaxf(wmax, wv[t]);
     }
     l_run = fmaf(l_run, alpha, psum);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) o_acc[ct] *= alpha;
-    const float W = row16_max(wmax);
-    const float winv = W > 0.f ? 127.0f / W : 0.f;
-    float t0 = 0.f, t1 = 0.f, t2 = 0.f;
-    {
-      float l0[8], l1[8], l2[8];
+    for (int c = 0; c < CTW; ++c) o_acc[c] *= alpha;
+    wmax = row16_max(wmax);
+    __syncthreads();  // everyone has read pmax (reused below)
+    if (n == 0 && hvalid) sm.pmax[w][G] = wmax;
+    __syncthreads();  // B3: w maxima
+    float W = 0.f;
+    if (hvalid) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        limbs3(wv[nt] * winv, l0[nt], l1[nt], l2[nt]);
-        t0 += l0[nt];
-        t1 += l1[nt];
-        t2 += l2[nt];
-      }
-      if (hvalid) {
-        uint2* w0 = reinterpret_cast<uint2*>(wlw + (G * 3 + 0) * kGroup + 8 * n);
-        uint2* w1 = reinterpret_cast<uint2*>(wlw + (G * 3 + 1) * kGroup + 8 * n);
-        uint2* w2 = reinterpret_cast<uint2*>(wlw + (G * 3 + 2) * kGroup + 8 * n);
-        *w0 = make_uint2(pack4_i8(l0[0], l0[1], l0[2], l0[3]), pack4_i8(l0[4], l0[5], l0[6], l0[7]));
-        *w1 = make_uint2(pack4_i8(l1[0], l1[1], l1[2], l1[3]), pack4_i8(l1[4], l1[5], l1[6], l1[7]));
-        *w2 = make_uint2(pack4_i8(l2[0], l2[1], l2[2], l2[3]), pack4_i8(l2[4], l2[5], l2[6], l2[7]));
-      }
+      for (int k = 0; k < kWaves; ++k) W = fmaxf(W, sm.pmax[k][G]);
     }
-    const int T0 = (int)row16_sum(t0), T1 = (int)row16_sum(t1), T2 = (int)row16_sum(t2);
-    wave_sync();
+    const float winv = W > 0.f ? WMAX * __builtin_amdgcn_rcpf(W) : 0.f;
+    if (hvalid) {
+      float f0[2], f1[2], f2[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) limbs_r128(wv[t], winv, f0[t], f1[t], f2[t]);
+      uint8_t* base = &sm.wl[G][0][8 * n + 2 * w];
+      *reinterpret_cast<uint16_t*>(base) =
+          (uint16_t)__builtin_amdgcn_perm(__float_as_uint(f0[1]), __float_as_uint(f0[0]), 0x0c0c0400u);
+      *reinterpret_cast<uint16_t*>(base + kGroup) =
+          (uint16_t)__builtin_amdgcn_perm(__float_as_uint(f1[1]), __float_as_uint(f1[0]), 0x0c0c0400u);
+      *reinterpret_cast<uint16_t*>(base + 2 * kGroup) =
+          (uint16_t)__builtin_amdgcn_perm(__float_as_uint(f2[1]), __float_as_uint(f2[0]), 0x0c0c0400u);
+    }
+    __syncthreads();  // B4: w limbs ready
+
+    // (E) PV for this wave's channel tiles.
     v4i aw[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (arow_valid) {
-        const uint4 v = *reinterpret_cast<const uint4*>(wlw + (hm * 3 + im) * kGroup + 16 * (2 * G + s));
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.wl[hm][im][16 * (2 * G + s)]);
         aw[s] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
       } else {
         aw[s] = v4i{0, 0, 0, 0};
       }
     }
-    // PV on MFMA: rows (head G, limb i), column channel 16 ct + n.
-    const uint16_t* cv = sv + kGroup;
-    const float vscale = W * (0.5f / 127.0f);
+    v4i tacc = {0, 0, 0, 0};
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+    for (int s = 0; s < 2; ++s) tacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], ones, tacc, 0, 0, 0);
+    const uint32_t neglt =
+        0u - (uint32_t)LV * (((uint32_t)tacc[0] << 14) + ((uint32_t)tacc[1] << 7) + (uint32_t)tacc[2]);
+    const float vscale = W * (1.0f / (WMAX * 32768.0f));
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+      const int ct = w * CTW + c;
+      const uint8_t* vp = cur + Gm::KREC + (16 * ct + n) * Gm::VROW + G * Gm::LBV;
+      uint32_t vw[Gm::LBV / 4];
+#pragma unroll
+      for (int k = 0; k < Gm::LBV / 4; ++k) vw[k] = reinterpret_cast<const uint32_t*>(vp)[k];
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], unpack16<VB>(&vc[ct][s * (2 * VB / 4)]), acc, 0, 0, 0);
-      const float f0 = (float)(2 * acc[0] - LV * T0);
-      const float f1 = (float)(2 * acc[1] - LV * T1);
-      const float f2 = (float)(2 * acc[2] - LV * T2);
-      const float f = fmaf(fmaf(f2, 1.0f / 254.0f, f1), 1.0f / 254.0f, f0);
-      o_acc[ct] = fmaf(f * vscale, h2f(cv[16 * ct + n]), o_acc[ct]);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], unpack16<VB>(&vw[s * (VB / 2)]), acc, 0, 0, 0);
+      const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
+      const int yv = (int)((x << 1) + neglt);
+      o_acc[c] = fmaf((float)yv * vscale, h2f(cv16[16 * ct + n]), o_acc[c]);
     }
-    wave_sync();  // LDS areas are rewritten by the next group
+    if (more) store_stage(sm.buf[(it + 1) & 1]);
+    __syncthreads();  // B0: next group staged; LDS areas free for reuse
   }
 
-  const float l_tot = row16_sum(l_run);
+  // Partial of this split: m (replicated), l (sum over waves), o (disjoint
+  // channel tiles per wave), straight to the workspace.
+  const float lw = row16_sum(l_run);
+  if (n == 0 && hvalid) sm.lsum[w][G] = lw;
+  __syncthreads();
   if (hvalid) {
-    if (n == 0) {
-      sm.mm[w][G] = m_run;
-      sm.ll[w][G] = l_tot;
-    }
+    const int hq_idx = kvh * GQ + G;
+    const int64_t row = ((int64_t)b * a.hq + hq_idx) * a.nsplit + split;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) sm.oo[w][G][16 * ct + n] = o_acc[ct];
+    for (int c = 0; c < CTW; ++c) a.ws_o[row * D + 16 * (w * CTW + c) + n] = o_acc[c];
+    if (w == 0 && n == 0) {
+      float L = 0.f;
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) L += sm.lsum[k][G];
+      store_partial_ml(a, b, hq_idx, split, m_run, L);
+    }
   }
 }
 
-// Exact part: the sink and the tail, fp16, original frame.  Exact split es
-// covers exact tokens [128 es, 128 es + 128); wave w takes 32 of them, lane
-// (token, half) holds half a K row and half a V row.  QK: fp32 FMAs against
-// the LDS query; PV: V rows staged in LDS, lane = channel group.
+// ---------------------------------------------------------------------------
+// Exact split: the sink and the tail, fp16, original frame.  Exact split es
+// covers exact tokens [128 es, 128 es + 128); wave w takes 32 of them in two
+// rounds of 16; lane (token, quarter) holds a quarter of a K row and of a V
+// row.  QK: fp32 FMAs against the LDS query; PV: V rows staged in LDS.
+// ---------------------------------------------------------------------------
 template <int D, int GQ>
-__device__ void exact_split(DecodeSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int n) {
-  constexpr int HALF = D / 2;
+__device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int split, int n) {
+  constexpr int QD = D / 4;     // channels per lane (quarter row)
   constexpr int CPLX = D / 64;  // channels per lane in the PV part
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int half = l >> 5, tl = l & 31;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int quarter = l >> 4, tl = l & 15;
+  for (int idx = tid; idx < GQ * D; idx += 256) {
+    const int h = idx / D, j = idx % D;
+    sm.qx[h][j] = __half2float(a.q[((int64_t)b * a.hq + kvh * GQ + h) * D + j]) * a.scale * kLog2e;
+  }
+  __syncthreads();
   const int n_sink = min(n, kSink);
   const int tau = n > kSink ? (n - kSink) % kGroup : 0;
   const int n_exact = max(0, n_sink + tau);
   const int64_t bh = (int64_t)b * a.c.hkv + kvh;
-  const int e = kGroup * es + 32 * w + tl;
-  const bool valid = e < n_exact;
-  float dot[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
-  uint16_t* vrow = &sm.u.ex.v[w][tl][half * HALF];
-  if (valid) {
-    const size_t row = e < n_sink ? (size_t)(bh * kGroup + e) : (size_t)(bh * kGroup + (e - n_sink));
-    const uint4* kp = reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_k : a.c.tail_k) + row * D + half * HALF);
-    const uint4* vp = reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_v : a.c.tail_v) + row * D + half * HALF);
-    uint4 kr[HALF / 8], vr[HALF / 8];
-#pragma unroll
-    for (int c = 0; c < HALF / 8; ++c) {
-      kr[c] = kp[c];
-      vr[c] = vp[c];
-    }
-#pragma unroll
-    for (int c = 0; c < HALF / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = vr[c];
-#pragma unroll
-    for (int c = 0; c < HALF / 8; ++c) {
-      const uint32_t ws[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        const float4 qa = *reinterpret_cast<const float4*>(&sm.qx[h][half * HALF + 8 * c]);
-        const float4 qb = *reinterpret_cast<const float4*>(&sm.qx[h][half * HALF + 8 * c + 4]);
-        dot[h] = fmaf(qa.x, h2f((uint16_t)(ws[0] & 0xFFFFu)), dot[h]);
-        dot[h] = fmaf(qa.y, h2f((uint16_t)(ws[0] >> 16)), dot[h]);
-        dot[h] = fmaf(qa.z, h2f((uint16_t)(ws[1] & 0xFFFFu)), dot[h]);
-        dot[h] = fmaf(qa.w, h2f((uint16_t)(ws[1] >> 16)), dot[h]);
-        dot[h] = fmaf(qb.x, h2f((uint16_t)(ws[2] & 0xFFFFu)), dot[h]);
-        dot[h] = fmaf(qb.y, h2f((uint16_t)(ws[2] >> 16)), dot[h]);
-        dot[h] = fmaf(qb.z, h2f((uint16_t)(ws[3] & 0xFFFFu)), dot[h]);
-        dot[h] = fmaf(qb.w, h2f((uint16_t)(ws[3] >> 16)), dot[h]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < HALF / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = make_uint4(0, 0, 0, 0);
-  }
-  float mh[GQ], lh[GQ];
+
+  float m_run[GQ], l_run[GQ], o[GQ][CPLX];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const float lg = valid ? dot[h] + __shfl_xor(dot[h], 32, 64) : -INFINITY;
-    mh[h] = wave_max(lg);
-    const float p = (valid && mh[h] != -INFINITY) ? exp2f(lg - mh[h]) : 0.f;
-    lh[h] = wave_sum(half == 0 ? p : 0.f);
-    if (half == 0) sm.u.ex.p[w][tl][h] = p;
-  }
-  wave_sync();
-  float o[GQ][CPLX];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
 #pragma unroll
     for (int c = 0; c < CPLX; ++c) o[h][c] = 0.f;
-  const int nt = min(32, max(0, n_exact - (kGroup * es + 32 * w)));
-  for (int t = 0; t < nt; ++t) {
-    const float4 pv = *reinterpret_cast<const float4*>(&sm.u.ex.p[w][t][0]);
-    const float ph[4] = {pv.x, pv.y, pv.z, pv.w};
-    float vf[CPLX];
-    if constexpr (CPLX == 2) {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(&sm.u.ex.v[w][t][2 * l]);
-      vf[0] = h2f((uint16_t)(x & 0xFFFFu));
-      vf[1] = h2f((uint16_t)(x >> 16));
+  }
+  for (int round = 0; round < 2; ++round) {
+    const int e0 = kGroup * es + 32 * w + kExactTok * round;
+    const int e = e0 + tl;
+    const bool valid = e < n_exact;
+    float dot[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
+    uint16_t* vrow = &sm.v[w][tl][quarter * QD];
+    if (valid) {
+      const size_t row = e < n_sink ? (size_t)(bh * kGroup + e) : (size_t)(bh * kGroup + (e - n_sink));
+      const uint4* kp =
+          reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_k : a.c.tail_k) + row * D + quarter * QD);
+      const uint4* vp =
+          reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_v : a.c.tail_v) + row * D + quarter * QD);
+      uint4 kr[QD / 8], vr[QD / 8];
+#pragma unroll
+      for (int c = 0; c < QD / 8; ++c) {
+        kr[c] = kp[c];
+        vr[c] = vp[c];
+      }
+#pragma unroll
+      for (int c = 0; c < QD / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = vr[c];
+#pragma unroll
+      for (int c = 0; c < QD / 8; ++c) {
+        const uint32_t ws[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          const float4 qa = *reinterpret_cast<const float4*>(&sm.qx[h][quarter * QD + 8 * c]);
+          const float4 qb = *reinterpret_cast<const float4*>(&sm.qx[h][quarter * QD + 8 * c + 4]);
+          dot[h] = fmaf(qa.x, h2f((uint16_t)(ws[0] & 0xFFFFu)), dot[h]);
+          dot[h] = fmaf(qa.y, h2f((uint16_t)(ws[0] >> 16)), dot[h]);
+          dot[h] = fmaf(qa.z, h2f((uint16_t)(ws[1] & 0xFFFFu)), dot[h]);
+          dot[h] = fmaf(qa.w, h2f((uint16_t)(ws[1] >> 16)), dot[h]);
+          dot[h] = fmaf(qb.x, h2f((uint16_t)(ws[2] & 0xFFFFu)), dot[h]);
+          dot[h] = fmaf(qb.y, h2f((uint16_t)(ws[2] >> 16)), dot[h]);
+          dot[h] = fmaf(qb.z, h2f((uint16_t)(ws[3] & 0xFFFFu)), dot[h]);
+          dot[h] = fmaf(qb.w, h2f((uint16_t)(ws[3] >> 16)), dot[h]);
+        }
+      }
     } else {
-      const uint2 x = *reinterpret_cast<const uint2*>(&sm.u.ex.v[w][t][4 * l]);
-      vf[0] = h2f((uint16_t)(x.x & 0xFFFFu));
-      vf[1] = h2f((uint16_t)(x.x >> 16));
-      vf[2] = h2f((uint16_t)(x.y & 0xFFFFu));
-      vf[3] = h2f((uint16_t)(x.y >> 16));
+#pragma unroll
+      for (int c = 0; c < QD / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = make_uint4(0, 0, 0, 0);
     }
+    float pt[GQ];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
+    for (int h = 0; h < GQ; ++h) {
+      float lg = dot[h];
+      lg += __shfl_xor(lg, 16, 64);
+      lg += __shfl_xor(lg, 32, 64);
+      lg = valid ? lg : -INFINITY;
+      const float rmax = wave_max(lg);
+      const float m_new = fmaxf(m_run[h], rmax);
+      const float alpha = (m_run[h] == -INFINITY) ? 0.f : exp2f(m_run[h] - m_new);
+      const float p = (valid && m_new != -INFINITY) ? exp2f(lg - m_new) : 0.f;
+      pt[h] = p;
+      l_run[h] = l_run[h] * alpha + wave_sum(quarter == 0 ? p : 0.f);
+      m_run[h] = m_new;
 #pragma unroll
-      for (int c = 0; c < CPLX; ++c) o[h][c] = fmaf(ph[h], vf[c], o[h][c]);
+      for (int c = 0; c < CPLX; ++c) o[h][c] *= alpha;
+    }
+    if (quarter == 0) {
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) sm.p[w][tl][h] = pt[h];
+    }
+    wave_sync();
+    const int nt = min(kExactTok, max(0, n_exact - e0));
+    for (int t = 0; t < nt; ++t) {
+      const float4 pv = *reinterpret_cast<const float4*>(&sm.p[w][t][0]);
+      const float ph[4] = {pv.x, pv.y, pv.z, pv.w};
+      float vf[CPLX];
+      if constexpr (CPLX == 2) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(&sm.v[w][t][2 * l]);
+        vf[0] = h2f((uint16_t)(x & 0xFFFFu));
+        vf[1] = h2f((uint16_t)(x >> 16));
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(&sm.v[w][t][4 * l]);
+        vf[0] = h2f((uint16_t)(x.x & 0xFFFFu));
+        vf[1] = h2f((uint16_t)(x.x >> 16));
+        vf[2] = h2f((uint16_t)(x.y & 0xFFFFu));
+        vf[3] = h2f((uint16_t)(x.y >> 16));
+      }
+#pragma unroll
+      for (int h = 0; h < GQ; ++h)
+#pragma unroll
+        for (int c = 0; c < CPLX; ++c) o[h][c] = fmaf(ph[h], vf[c], o[h][c]);
+    }
+    wave_sync();  // the staging rows are rewritten next round
   }
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
     if (l == 0) {
-      sm.mm[w][h] = mh[h];
-      sm.ll[w][h] = lh[h];
+      sm.mm[w][h] = m_run[h];
+      sm.ll[w][h] = l_run[h];
     }
 #pragma unroll
     for (int c = 0; c < CPLX; ++c) sm.oo[w][h][CPLX * l + c] = o[h][c];
   }
+  __syncthreads();
+  for (int idx = tid; idx < GQ * D; idx += 256) {
+    const int h = idx / D, ch = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm.mm[k][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        const float mw = sm.mm[k][h];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        L = fmaf(f, sm.ll[k][h], L);
+        O = fmaf(f, sm.oo[k][h][ch], O);
+      }
+    }
+    const int64_t row = ((int64_t)b * a.hq + kvh * GQ + h) * a.nsplit + split;
+    a.ws_o[row * D + ch] = O;
+    if (ch == 0) store_partial_ml(a, b, kvh * GQ + h, split, M, L);
+  }
 }
 
 template <int D, int KB, int VB, int GQ>
+union DecodeSmemU {
+  RecSmem<D, KB, VB, GQ> rec;
+  ExactSmem<D, GQ> ex;
+};
+
+template <int D, int KB, int VB, int GQ>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  __shared__ DecodeSmem<D, GQ> sm;
+  __shared__ DecodeSmemU<D, KB, VB, GQ> sm;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int n = a.c.seq_len[b];
-  // Scaled query (log2 domain) of the GQ heads that share KV head kvh.
-  for (int idx = threadIdx.x; idx < GQ * D; idx += blockDim.x) {
-    const int h = idx / D, j = idx % D;
-    const float qv = __half2float(a.q[((int64_t)b * a.hq + kvh * GQ + h) * D + j]);
-    sm.qx[h][j] = qv * a.scale * kLog2e;
-  }
-  for (int idx = threadIdx.x; idx < kWaves * GQ; idx += blockDim.x) {
-    sm.mm[idx / GQ][idx % GQ] = -INFINITY;
-    sm.ll[idx / GQ][idx % GQ] = 0.f;
-  }
-  for (int idx = threadIdx.x; idx < kWaves * GQ * D; idx += blockDim.x) (&sm.oo[0][0][0])[idx] = 0.f;
-  __syncthreads();
   if (split < a.n_rec_splits)
-    record_split<D, KB, VB, GQ>(sm, a, b, kvh, split, n);
+    record_split<D, KB, VB, GQ>(sm.rec, a, b, kvh, split, n);
   else
-    exact_split<D, GQ>(sm, a, b, kvh, split - a.n_rec_splits, n);
-  merge_and_store<D, GQ>(sm, a, b, kvh, split);
+    exact_split<D, GQ>(sm.ex, a, b, kvh, split - a.n_rec_splits, split, n);
 }
 
 // One workgroup (256 threads) per (query head, request): log-sum-exp merge of
@@ -464,7 +546,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float oex[D];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t base = ((int64_t)b * a.hq + hq) * a.nsplit;
-  // Global max over splits.
   float m = -INFINITY;
   for (int s = tid; s < a.nsplit; s += 256) m = fmaxf(m, a.ws_ml[2 * (base + s)]);
   red[tid] = m;
@@ -480,8 +561,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     orot[idx] = 0.f;
     oex[idx] = 0.f;
   }
-  // Channel partial sums: thread (j, part) sums splits part, part + P, ...
-  constexpr int P = 256 / D;  // 2 for D = 128, 1 for D = 256
+  constexpr int P = 256 / D;  // threads per channel
   const int j = tid % D, part = tid / D;
   float accr = 0.f, acce = 0.f;
   for (int s0 = 0; s0 < a.nsplit; s0 += MAXS) {
@@ -501,8 +581,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       for (int u = 0; u < 8; ++u) v[u] = a.ws_o[(base + s0 + s + u * P) * D + j];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int ss = s0 + s + u * P;
-        if (ss < a.n_rec_splits)
+        if (s0 + s + u * P < a.n_rec_splits)
           accr = fmaf(wgt[s + u * P], v[u], accr);
         else
           acce = fmaf(wgt[s + u * P], v[u], acce);
@@ -546,14 +625,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups) {
   DecodePlan p;
-  const int64_t total = (int64_t)batch * hkv * max_groups;
-  const int64_t target_waves = 2048;  // 256 CUs x 8 waves
-  int gpw = (int)((total + target_waves - 1) / target_waves);
-  if (gpw < 1) gpw = 1;
-  p.groups_per_wave = gpw;
-  p.groups_per_split = kWaves * gpw;
-  p.n_rec_splits = max_groups > 0 ? (max_groups + p.groups_per_split - 1) / p.groups_per_split : 0;
+  // About four workgroups per CU on 256 CUs, each walking a contiguous range
+  // of groups of one (request, KV head).
+  const int64_t pairs = (int64_t)batch * hkv;
+  const int64_t target = 1024;
   p.n_exact_splits = 2;  // exact tokens [0,128) and [128,256)
+  int gps = 1;
+  if (max_groups > 0) {
+    while (gps < max_groups) {
+      const int64_t splits = (max_groups + gps - 1) / gps;
+      if (pairs * (splits + p.n_exact_splits) <= target) break;
+      ++gps;
+    }
+  }
+  p.groups_per_split = gps;
+  p.groups_per_wave = gps;
+  p.n_rec_splits = max_groups > 0 ? (max_groups + gps - 1) / gps : 0;
   p.nsplit = p.n_rec_splits + p.n_exact_splits;
   const size_t rows = (size_t)batch * hq * p.nsplit;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;

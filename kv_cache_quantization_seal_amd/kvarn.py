@@ -145,7 +145,7 @@ class KVarNCache:
                                    device=device)
         self.seq_len = torch.zeros(batch, dtype=torch.int32, device=device)
         ws = decode_workspace_bytes(cfg, batch, max_groups)
-        self.workspace = torch.empty(max(256, ws), dtype=torch.uint8, device=device)
+        self.workspace = torch.zeros(max(256, ws), dtype=torch.uint8, device=device)  # counters start at 0
         self.view = CacheView(_ptr(self.sink_k), _ptr(self.sink_v), _ptr(self.tail_k), _ptr(self.tail_v),
                               _ptr(self.records), _ptr(self.seq_len), batch, max_groups)
 

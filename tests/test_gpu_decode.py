@@ -92,3 +92,20 @@ def test_spare_capacity_is_ignored():
     # max_groups larger than any request needs; unused record slots hold junk.
     err = _run(128, 4, 2, 2, 2, [400, 200], seed=6, max_groups=9)
     assert err <= ATTN_ATOL
+
+
+def test_two_phase_equals_fused():
+    d, hq, hkv, kb, vb = 128, 8, 2, 2, 2
+    lens = [900, 300]
+    states, q = _case(d, hq, hkv, kb, vb, lens, 11)
+    cfg = K.make_config(d, hq, hkv, kb, vb)
+    cache = K.KVarNCache(cfg, len(lens), 7)
+    upload_states(cache, states)
+    qd = torch.from_numpy(q).cuda()
+    fused = cache.decode_attn(qd).clone()
+    cache.decode_partial(qd)
+    two = cache.decode_combine(torch.empty_like(fused))
+    again = cache.decode_attn(qd)   # counters were left at zero
+    torch.cuda.synchronize()
+    assert torch.allclose(fused, two, atol=1e-6, rtol=1e-5)
+    assert torch.equal(fused, again)
