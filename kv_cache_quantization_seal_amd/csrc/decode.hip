@@ -10,9 +10,10 @@
 // page, §2.1 "Sink, Body, And Tail").
 //
 // Record splits.  A workgroup (4 waves) walks a range of 128-token groups of
-// one (request, KV head).  Each group's K and V records are copied into a
-// double-buffered LDS slot (the next group's loads are in flight while the
-// current one is computed) and the four waves share the work:
+// one (request, KV head).  Each group's K and V records are copied into one
+// of two LDS slots through two register stages (the next two groups' loads
+// are in flight while the current one is computed) and the four waves share
+// the work:
 //   logit_t = s^K_t * sum_j q~_j (code_tj - mid),  q~ = q_r * c^K * scale,
 //   w_t = p_t * s^V_t,  o_rot_j += c^V_j * sum_t w_t (code_tj - mid).
 // Both sums run on v_mfma_i32_16x16x64_i8 with the codes as exact int8
@@ -39,6 +40,9 @@
 //     is channel 16 ct + n, same token slots.
 //   tok(nt, n) = 16 (n/2) + unpack_index<VB>(8 (n%2) + nt): the w limbs of
 //   lane n sit at LDS bytes 8n + nt.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -55,7 +59,7 @@ template <int D, int KB, int VB>
 struct RecGeom {
   static constexpr int KS = D / 64;                      // QK K-steps
   static constexpr int NCT = D / 16;                     // PV channel tiles
-  static constexpr int CTW = NCT / kWaves;               // channel tiles per wave
+  static constexpr int NTT = kGroup / 16;                // QK token tiles
   static constexpr int LBK = KS * 2 * KB;                // K-code bytes per lane per token
   static constexpr int LBV = 4 * VB;                     // V-code bytes per lane per channel
   static constexpr int KROW = D * KB / 8;                // bytes of one token row of K codes
@@ -64,20 +68,23 @@ struct RecGeom {
   static constexpr int VCODE = kGroup * D * VB / 8;
   static constexpr int KREC = KCODE + 2 * kGroup + 2 * D;
   static constexpr int VREC = VCODE + 2 * kGroup + 2 * D;
-  static constexpr int GB = KREC + VREC;                 // staged bytes per group
-  static constexpr int CHUNKS = GB / 16;
-  static constexpr int CPT = (CHUNKS + 255) / 256;       // 16-byte chunks per thread
+  static constexpr int GB = KREC + VREC;                 // bytes per group (K record | V record)
+  static constexpr int QB = D / 16;                      // q~ operand bytes per producer lane
+};
+
+template <int D, int GQ>
+struct alignas(16) WaveLds {
+  alignas(16) uint8_t ql[GQ][3][D];       // q~ limbs, QK A-operand order
+  alignas(16) uint8_t wl[GQ][3][kGroup];  // w limbs, PV A-operand order
 };
 
 template <int D, int KB, int VB, int GQ>
 struct alignas(16) RecSmem {
-  alignas(16) uint8_t buf[2][RecGeom<D, KB, VB>::GB];  // staged K record | V record
-  alignas(16) uint8_t ql[GQ][3][D];                    // q~ limbs, operand order
-  alignas(16) uint8_t wl[GQ][3][kGroup];               // w limbs, operand order
-  float qx[GQ][D];                                     // scaled query, rotated in place
-  float e[GQ];                                         // q~ maximum per head (this group)
-  float pmax[kWaves][GQ];                              // per-wave partial maxima
-  float lsum[kWaves][GQ];
+  WaveLds<D, GQ> wv[kWaves];
+  float qx[GQ][D];              // scaled query, rotated in place
+  float mm[kWaves][GQ];         // per-wave partial maxima
+  float ll[kWaves][GQ];         // per-wave partial sums
+  float oo[kWaves][GQ][D];      // per-wave partial outputs (rotated frame)
 };
 
 template <int D, int GQ>
@@ -114,52 +121,158 @@ __device__ __forceinline__ void store_partial_ml(const DecodeArgs& a, int b, int
 }
 
 // ---------------------------------------------------------------------------
-// Record split (workgroup-cooperative)
+// Record split: four independent waves, each streaming whole groups.
 // ---------------------------------------------------------------------------
+
+// One group's operands as one lane holds them, loaded straight from the
+// record in MFMA operand order (loop-invariant per-lane offsets):
+//   k[nt]  K codes of token tok(nt, n), channel blocks of lane group G;
+//   v[ct]  V codes of channel NCT*n + ct, token blocks 2G, 2G+1;
+//   sk/sv  s^K, s^V of the lane's eight tokens tok(0..7, n): half 2(nt&3) +
+//          (nt>>2) of the four dwords;
+//   ck     c^K of the q~ producer's channels; cv  c^V of channels NCT*n + ct.
+template <int D, int KB, int VB>
+struct Stage {
+  using Gm = RecGeom<D, KB, VB>;
+  uint32_t k[Gm::NTT][Gm::LBK / 4];
+  uint32_t v[Gm::NCT][Gm::LBV / 4];
+  uint32_t sk[4], sv[4];
+  uint32_t ck[Gm::QB / 2];
+  uint32_t cv[Gm::NCT / 2];
+};
+
+template <int N>
+__device__ __forceinline__ void load_dw(uint32_t (&dst)[N], __amdgpu_buffer_rsrc_t r, int off) {
+  static_assert(N % 2 == 0 || N == 1, "");
+  if constexpr (N == 1) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (N == 2) {
+    const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = x.x;
+    dst[1] = x.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+      dst[4 * i] = x.x;
+      dst[4 * i + 1] = x.y;
+      dst[4 * i + 2] = x.z;
+      dst[4 * i + 3] = x.w;
+    }
+  }
+}
+
+__device__ __forceinline__ float half_of(const uint32_t* w, int i) {
+  return h2f((uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu)));
+}
+
 template <int D, int KB, int VB, int GQ>
 __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, int b, int kvh, int split,
                              int nseq) {
   using Gm = RecGeom<D, KB, VB>;
-  constexpr int KS = Gm::KS, CTW = Gm::CTW, CPT = Gm::CPT;
+  using St = Stage<D, KB, VB>;
+  constexpr int KS = Gm::KS, NCT = Gm::NCT, NTT = Gm::NTT, QB = Gm::QB;
   constexpr int LK = (1 << KB) - 1, LV = (1 << VB) - 1;
   constexpr float QMAX = top_limb(D, LK);
   constexpr float WMAX = top_limb(kGroup, LV);
-  constexpr int QPL = D / 64;  // q~ values produced per lane (wave h < GQ)
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int G = l >> 4, n = l & 15;
-  const bool hvalid = G < GQ;
+  const bool hvalid = G < GQ;         // QK/PV output row of this lane is head G
   const int hm = n >> 2, im = n & 3;  // A-operand row of this lane: (head, limb)
   const bool arow_valid = hm < GQ && im < 3;
+  WaveLds<D, GQ>& wv = sm.wv[w];
 
   const uint8_t* recs = a.c.records + (((int64_t)b * a.c.hkv + kvh) * a.c.max_groups) * a.c.group_bytes;
-  const int g0 = split * a.groups_per_split;
-  const int gcap = min(g0 + a.groups_per_split, a.c.max_groups);  // slots that exist
   const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
-  const int g1 = min(gcap, n_groups);
+  const int gw0 = split * a.groups_per_split + w * a.groups_per_wave;
+  const int ga = min(gw0, n_groups);
+  const int gb = min(gw0 + a.groups_per_wave, n_groups);
 
-  // The first group's stage loads go out before anything else (the slot
-  // exists, so the load is safe before seq_len decides whether it is used).
-  v4u stage[CPT];
-  auto load_stage = [&](int g) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(recs + (int64_t)g * a.c.group_bytes, Gm::GB);
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) stage[k] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + 256 * k), 0, 0);
+  // Per-lane byte offsets within a group (loop-invariant).
+  // Tokens tok(0..7, n) are tok0 + 2(nt&3) + (nt>>2) with
+  // tok0 = 16(n/2) + 8(n&1) (4-bit V), or tok0 + 4(nt&3) + (nt>>2) with
+  // tok0 = 16(n/2) + 2(n&1) (2-bit V): a lane base plus a constant.
+  const int tok0 = VB == 4 ? 16 * (n >> 1) + 8 * (n & 1) : 16 * (n >> 1) + 2 * (n & 1);
+  const int kbase = tok0 * Gm::KROW + G * Gm::LBK;
+  auto kofs = [&](int nt) { return kbase + (VB == 4 ? 2 * (nt & 3) + (nt >> 2) : 4 * (nt & 3) + (nt >> 2)) * Gm::KROW; };
+  const int skofs = Gm::KCODE + 2 * tok0;
+  const int svofs = Gm::KREC + Gm::VCODE + 2 * tok0;
+  // q~ producer lane: head hq = l/16, operand bytes [QB*j, QB*j + QB), j = l%16.
+  const int hq = l >> 4, j = l & 15;
+  int ckofs;
+  if constexpr (QB == 8)
+    ckofs = Gm::KCODE + 2 * kGroup + 2 * (16 * (j >> 1) + (KB == 4 ? 8 * (j & 1) : 2 * (j & 1)));
+  else
+    ckofs = Gm::KCODE + 2 * kGroup + 2 * (16 * j);
+  const int cvofs = Gm::KREC + Gm::VCODE + 2 * kGroup + 2 * NCT * n;
+  const int vbase = Gm::KREC + NCT * n * Gm::VROW + G * Gm::LBV;
+  auto vofs = [&](int ct) { return vbase + ct * Gm::VROW; };
+
+  // Wave-uniform buffer range of group g; an unused range is empty, so its
+  // loads return zero without touching memory and every path issues the
+  // same loads.
+  auto rsrc_of = [&](int g, bool on) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(recs + (int64_t)(on ? g : 0) * a.c.group_bytes);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const int bytes = __builtin_amdgcn_readfirstlane(on ? Gm::GB : 0);
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), bytes);
   };
-  auto store_stage = [&](uint8_t* dst) {
+  // K part (c^K first: it is needed first), V part (s^V first).
+  auto load_k = [&](St& S, int g, bool on) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(g, on);
+    if constexpr (QB == 8 && KB == 2) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k)
-      if (tid + 256 * k < Gm::CHUNKS) *reinterpret_cast<v4u*>(dst + 16 * (tid + 256 * k)) = stage[k];
+      for (int k = 0; k < 4; ++k) S.ck[k] = __builtin_amdgcn_raw_buffer_load_b32(r, ckofs + 8 * k, 0, 0);
+    } else {
+      load_dw(S.ck, r, ckofs);
+    }
+    if constexpr (VB == 4) {
+      load_dw(S.sk, r, skofs);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) S.sk[k] = __builtin_amdgcn_raw_buffer_load_b32(r, skofs + 8 * k, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTT; ++nt) load_dw(S.k[nt], r, kofs(nt));
   };
-  if (g0 < gcap) load_stage(g0);
+  auto load_v = [&](St& S, int g, bool on) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(g, on);
+    if constexpr (VB == 4) {
+      load_dw(S.sv, r, svofs);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) S.sv[k] = __builtin_amdgcn_raw_buffer_load_b32(r, svofs + 8 * k, 0, 0);
+    }
+    load_dw(S.cv, r, cvofs);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) load_dw(S.v[ct], r, vofs(ct));
+  };
+
+  // The query's loads go out first: loads complete in issue order, so waiting
+  // for the query must not also wait for the group loads behind it.
+  constexpr int QPT = (GQ * D + 255) / 256;
+  __half qh[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    qh[i] = idx < GQ * D ? a.q[((int64_t)b * a.hq + kvh * GQ) * D + idx] : __half(0.f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  St SA;
+  load_k(SA, ga, ga < gb);
+  load_v(SA, ga, ga < gb);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Scaled query (log2 domain) of the GQ heads, rotated: qx <- qx H_D.
-  for (int idx = tid; idx < GQ * D; idx += 256) {
-    const int h = idx / D, j = idx % D;
-    sm.qx[h][j] = __half2float(a.q[((int64_t)b * a.hq + kvh * GQ + h) * D + j]) * a.scale * kLog2e;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < GQ * D) sm.qx[idx / D][idx % D] = __half2float(qh[i]) * a.scale * kLog2e;
   }
   __syncthreads();
   for (int s = 1; s < D; s <<= 1) {
@@ -172,70 +285,71 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
     }
     __syncthreads();
   }
-  // q~ producer (wave w < GQ, head w): operand bytes [QPL*l, QPL*l + QPL).
+  // q~ producer values: operand byte i of lane (hq, j) is channel
+  // 16 cb + unpack_index<KB>(p), its c^K is half ckh(i) of S.ck.
   const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
-  float qr[QPL];
-  int qch[QPL];
+  const bool qvalid = hq < GQ;
+  float qr[QB];
 #pragma unroll
-  for (int e = 0; e < QPL; ++e) {
-    const int ob = QPL * l + e;
-    qch[e] = 16 * (ob >> 4) + unpack_index<KB>(ob & 15);
-    qr[e] = w < GQ ? sm.qx[w][qch[e]] * rs : 0.f;
+  for (int i = 0; i < QB; ++i) {
+    const int ch = QB == 8 ? 16 * (j >> 1) + unpack_index<KB>(8 * (j & 1) + i) : 16 * j + unpack_index<KB>(i);
+    qr[i] = qvalid ? sm.qx[hq][ch] * rs : 0.f;
   }
-  if (g0 < g1) store_stage(sm.buf[0]);
-  __syncthreads();
+  auto ckh = [](int i) { return QB == 8 ? 2 * (i & 3) + (i >> 2) : unpack_index<KB>(i); };
 
-  float m_run = -INFINITY, l_run = 0.f;  // head G (replicated in every wave)
-  float o_acc[CTW];
+  float m_run = -INFINITY, l_run = 0.f;  // head G
+  float o_acc[NCT];                      // head G, channel NCT*n + ct
 #pragma unroll
-  for (int c = 0; c < CTW; ++c) o_acc[c] = 0.f;
+  for (int c = 0; c < NCT; ++c) o_acc[c] = 0.f;
 
-  for (int g = g0, it = 0; g < g1; ++g, ++it) {
-    const uint8_t* cur = sm.buf[it & 1];
-    const bool more = g + 1 < g1;
-    if (more) load_stage(g + 1);
-    const uint16_t* sk16 = reinterpret_cast<const uint16_t*>(cur + Gm::KCODE);
-    const uint16_t* ck16 = sk16 + kGroup;
-    const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(cur + Gm::KREC + Gm::VCODE);
-    const uint16_t* cv16 = sv16 + kGroup;
-
-    // (A) q~ limbs of head w.
-    if (w < GQ) {
-      float y[QPL];
-      float ym = 0.f;
+  // One group from stage S; each half of the stage is refilled with group gn
+  // as soon as it has been consumed (K part after QK, V part after PV), so
+  // the next group's loads overlap most of this group's work.
+  auto process = [&](St& S, int gn) {
+    const bool on = gn < gb;
+    // q~ limbs of head hq with E = max |q~| over the head's channels (one
+    // DPP row per head).
+    float y[QB];
+    float ym = 0.f;
 #pragma unroll
-      for (int e = 0; e < QPL; ++e) {
-        y[e] = qr[e] * h2f(ck16[qch[e]]);
-        ym = fmaxf(ym, fabsf(y[e]));
-      }
-      const float E = wave_max(ym);
-      const float inv = E > 0.f ? QMAX * __builtin_amdgcn_rcpf(E) : 0.f;
-      float f0[QPL], f1[QPL], f2[QPL];
-#pragma unroll
-      for (int e = 0; e < QPL; ++e) limbs_r128(y[e], inv, f0[e], f1[e], f2[e]);
-      uint8_t* base = &sm.ql[w][0][QPL * l];
-      if constexpr (QPL == 2) {
-        const uint32_t b0 = __builtin_amdgcn_perm(__float_as_uint(f0[1]), __float_as_uint(f0[0]), 0x0c0c0400u);
-        const uint32_t b1 = __builtin_amdgcn_perm(__float_as_uint(f1[1]), __float_as_uint(f1[0]), 0x0c0c0400u);
-        const uint32_t b2 = __builtin_amdgcn_perm(__float_as_uint(f2[1]), __float_as_uint(f2[0]), 0x0c0c0400u);
-        *reinterpret_cast<uint16_t*>(base) = (uint16_t)b0;
-        *reinterpret_cast<uint16_t*>(base + D) = (uint16_t)b1;
-        *reinterpret_cast<uint16_t*>(base + 2 * D) = (uint16_t)b2;
-      } else {
-        *reinterpret_cast<uint32_t*>(base) = pack_low_bytes(f0[0], f0[1], f0[2], f0[3]);
-        *reinterpret_cast<uint32_t*>(base + D) = pack_low_bytes(f1[0], f1[1], f1[2], f1[3]);
-        *reinterpret_cast<uint32_t*>(base + 2 * D) = pack_low_bytes(f2[0], f2[1], f2[2], f2[3]);
-      }
-      if (l == 0) sm.e[w] = E;
+    for (int i = 0; i < QB; ++i) {
+      y[i] = qr[i] * half_of(S.ck, ckh(i));
+      ym = fmaxf(ym, fabsf(y[i]));
     }
-    __syncthreads();  // B1: q~ limbs ready
+    const float E = row16_max(ym);  // row G == head G: also the QK scale of this lane
+    {
+      const float inv = E > 0.f ? QMAX * __builtin_amdgcn_rcpf(E) : 0.f;
+      uint32_t b0[QB / 4], b1[QB / 4], b2[QB / 4];
+#pragma unroll
+      for (int i = 0; i < QB / 4; ++i) {
+        float f0[4], f1[4], f2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) limbs_r128(y[4 * i + e], inv, f0[e], f1[e], f2[e]);
+        b0[i] = pack_low_bytes(f0[0], f0[1], f0[2], f0[3]);
+        b1[i] = pack_low_bytes(f1[0], f1[1], f1[2], f1[3]);
+        b2[i] = pack_low_bytes(f2[0], f2[1], f2[2], f2[3]);
+      }
+      if (qvalid) {
+        uint8_t* base = &wv.ql[hq][0][QB * j];
+        if constexpr (QB == 8) {
+          *reinterpret_cast<v2u*>(base) = v2u{b0[0], b0[1]};
+          *reinterpret_cast<v2u*>(base + D) = v2u{b1[0], b1[1]};
+          *reinterpret_cast<v2u*>(base + 2 * D) = v2u{b2[0], b2[1]};
+        } else {
+          *reinterpret_cast<v4u*>(base) = v4u{b0[0], b0[1], b0[2], b0[3]};
+          *reinterpret_cast<v4u*>(base + D) = v4u{b1[0], b1[1], b1[2], b1[3]};
+          *reinterpret_cast<v4u*>(base + 2 * D) = v4u{b2[0], b2[1], b2[2], b2[3]};
+        }
+      }
+    }
+    wave_sync();
 
-    // (B) QK for token tiles 2w, 2w+1.
+    // QK over the eight token tiles.
     v4i aq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (arow_valid) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ql[hm][im][16 * (G * KS + s)]);
+        const uint4 v = *reinterpret_cast<const uint4*>(&wv.ql[hm][im][16 * (G * KS + s)]);
         aq[s] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
       } else {
         aq[s] = v4i{0, 0, 0, 0};
@@ -246,79 +360,68 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
     for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], ones, sacc, 0, 0, 0);
     const uint32_t negls =
         0u - (uint32_t)LK * (((uint32_t)sacc[0] << 14) + ((uint32_t)sacc[1] << 7) + (uint32_t)sacc[2]);
-    const float kscale = (hvalid ? sm.e[G] : 0.f) * (1.0f / (QMAX * 32768.0f));
-    float logit[2];
+    const float kscale = E * (1.0f / (QMAX * 32768.0f));
+    float logit[NTT];
     float lmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int nt = 2 * w + t;
-      const int tok = tok_of<VB>(nt, n);
-      const uint8_t* kp = cur + tok * Gm::KROW + G * Gm::LBK;
-      uint32_t kw[Gm::LBK / 4];
-#pragma unroll
-      for (int k = 0; k < Gm::LBK / 4; ++k) kw[k] = reinterpret_cast<const uint32_t*>(kp)[k];
+    for (int nt = 0; nt < NTT; ++nt) {
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack16<KB>(&kw[s * (KB / 2)]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack16<KB>(&S.k[nt][s * (KB / 2)]), acc, 0, 0, 0);
       const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
       const int yv = (int)((x << 1) + negls);
-      logit[t] = hvalid ? (float)yv * (h2f(sk16[tok]) * kscale) : -INFINITY;
-      lmax = fmaxf(lmax, logit[t]);
+      logit[nt] = hvalid ? (float)yv * (half_of(S.sk, 2 * (nt & 3) + (nt >> 2)) * kscale) : -INFINITY;
+      lmax = fmaxf(lmax, logit[nt]);
     }
-    lmax = row16_max(lmax);
-    if (n == 0 && hvalid) sm.pmax[w][G] = lmax;
-    __syncthreads();  // B2: logit maxima
-    float gmax = -INFINITY;
-    if (hvalid) {
-#pragma unroll
-      for (int k = 0; k < kWaves; ++k) gmax = fmaxf(gmax, sm.pmax[k][G]);
-    }
+    load_k(S, gn, on);
+
+    // Softmax update; w = p * s^V with its exact per-head maximum W.
+    const float gmax = row16_max(lmax);
     const float m_new = fmaxf(m_run, gmax);
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    float wv[2];
-    float psum = 0.f, wmax = 0.f;
+    float wv_[NTT];
+    float psum = 0.f, wm = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float p = hvalid ? __builtin_amdgcn_exp2f(logit[t] - m_new) : 0.f;
+    for (int nt = 0; nt < NTT; ++nt) {
+      const float p = hvalid ? __builtin_amdgcn_exp2f(logit[nt] - m_new) : 0.f;
       psum += p;
-      wv[t] = p * h2f(sv16[tok_of<VB>(2 * w + t, n)]);
-      wmax = fmaxf(wmax, wv[t]);
+      wv_[nt] = p * half_of(S.sv, 2 * (nt & 3) + (nt >> 2));
+      wm = fmaxf(wm, wv_[nt]);
     }
     l_run = fmaf(l_run, alpha, psum);
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) o_acc[c] *= alpha;
-    wmax = row16_max(wmax);
-    __syncthreads();  // everyone has read pmax (reused below)
-    if (n == 0 && hvalid) sm.pmax[w][G] = wmax;
-    __syncthreads();  // B3: w maxima
-    float W = 0.f;
-    if (hvalid) {
+    for (int c = 0; c < NCT; ++c) o_acc[c] *= alpha;
+    const float W = row16_max(wm);
+    {
+      const float winv = W > 0.f ? WMAX * __builtin_amdgcn_rcpf(W) : 0.f;
+      uint32_t b0[2], b1[2], b2[2];
 #pragma unroll
-      for (int k = 0; k < kWaves; ++k) W = fmaxf(W, sm.pmax[k][G]);
-    }
-    const float winv = W > 0.f ? WMAX * __builtin_amdgcn_rcpf(W) : 0.f;
-    if (hvalid) {
-      float f0[2], f1[2], f2[2];
+      for (int hh = 0; hh < 2; ++hh) {
+        float f0[4], f1[4], f2[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) limbs_r128(wv[t], winv, f0[t], f1[t], f2[t]);
-      uint8_t* base = &sm.wl[G][0][8 * n + 2 * w];
-      *reinterpret_cast<uint16_t*>(base) =
-          (uint16_t)__builtin_amdgcn_perm(__float_as_uint(f0[1]), __float_as_uint(f0[0]), 0x0c0c0400u);
-      *reinterpret_cast<uint16_t*>(base + kGroup) =
-          (uint16_t)__builtin_amdgcn_perm(__float_as_uint(f1[1]), __float_as_uint(f1[0]), 0x0c0c0400u);
-      *reinterpret_cast<uint16_t*>(base + 2 * kGroup) =
-          (uint16_t)__builtin_amdgcn_perm(__float_as_uint(f2[1]), __float_as_uint(f2[0]), 0x0c0c0400u);
+        for (int e = 0; e < 4; ++e) limbs_r128(wv_[4 * hh + e], winv, f0[e], f1[e], f2[e]);
+        b0[hh] = pack_low_bytes(f0[0], f0[1], f0[2], f0[3]);
+        b1[hh] = pack_low_bytes(f1[0], f1[1], f1[2], f1[3]);
+        b2[hh] = pack_low_bytes(f2[0], f2[1], f2[2], f2[3]);
+      }
+      if (hvalid) {
+        // Token tok(nt, n) sits at PV operand byte 8n + nt.
+        uint8_t* base = &wv.wl[G][0][8 * n];
+        *reinterpret_cast<v2u*>(base) = v2u{b0[0], b0[1]};
+        *reinterpret_cast<v2u*>(base + kGroup) = v2u{b1[0], b1[1]};
+        *reinterpret_cast<v2u*>(base + 2 * kGroup) = v2u{b2[0], b2[1]};
+      }
     }
-    __syncthreads();  // B4: w limbs ready
+    wave_sync();
 
-    // (E) PV for this wave's channel tiles.
+    // PV over the channel tiles.
     v4i aw[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (arow_valid) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&sm.wl[hm][im][16 * (2 * G + s)]);
+        const uint4 v = *reinterpret_cast<const uint4*>(&wv.wl[hm][im][16 * (2 * G + s)]);
         aw[s] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
       } else {
         aw[s] = v4i{0, 0, 0, 0};
@@ -331,40 +434,51 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
         0u - (uint32_t)LV * (((uint32_t)tacc[0] << 14) + ((uint32_t)tacc[1] << 7) + (uint32_t)tacc[2]);
     const float vscale = W * (1.0f / (WMAX * 32768.0f));
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) {
-      const int ct = w * CTW + c;
-      const uint8_t* vp = cur + Gm::KREC + (16 * ct + n) * Gm::VROW + G * Gm::LBV;
-      uint32_t vw[Gm::LBV / 4];
-#pragma unroll
-      for (int k = 0; k < Gm::LBV / 4; ++k) vw[k] = reinterpret_cast<const uint32_t*>(vp)[k];
+    for (int ct = 0; ct < NCT; ++ct) {
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], unpack16<VB>(&vw[s * (VB / 2)]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], unpack16<VB>(&S.v[ct][s * (VB / 2)]), acc, 0, 0, 0);
       const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
       const int yv = (int)((x << 1) + neglt);
-      o_acc[c] = fmaf((float)yv * vscale, h2f(cv16[16 * ct + n]), o_acc[c]);
+      o_acc[ct] = fmaf((float)yv * vscale, half_of(S.cv, ct), o_acc[ct]);
     }
-    if (more) store_stage(sm.buf[(it + 1) & 1]);
-    __syncthreads();  // B0: next group staged; LDS areas free for reuse
-  }
+    load_v(S, gn, on);
+    wave_sync();  // this group's limbs have been read before the next group writes
+  };
 
-  // Partial of this split: m (replicated), l (sum over waves), o (disjoint
-  // channel tiles per wave), straight to the workspace.
+  for (int g = ga; g < gb; ++g) process(SA, g + 1);
+
+  // Merge the four waves' partials (m replicated per head; l summed over the
+  // row; o over disjoint channels) and write this split's partial.
   const float lw = row16_sum(l_run);
-  if (n == 0 && hvalid) sm.lsum[w][G] = lw;
-  __syncthreads();
   if (hvalid) {
-    const int hq_idx = kvh * GQ + G;
-    const int64_t row = ((int64_t)b * a.hq + hq_idx) * a.nsplit + split;
-#pragma unroll
-    for (int c = 0; c < CTW; ++c) a.ws_o[row * D + 16 * (w * CTW + c) + n] = o_acc[c];
-    if (w == 0 && n == 0) {
-      float L = 0.f;
-#pragma unroll
-      for (int k = 0; k < kWaves; ++k) L += sm.lsum[k][G];
-      store_partial_ml(a, b, hq_idx, split, m_run, L);
+    if (n == 0) {
+      sm.mm[w][G] = m_run;
+      sm.ll[w][G] = lw;
     }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) sm.oo[w][G][NCT * n + ct] = o_acc[ct];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GQ * D; idx += 256) {
+    const int h = idx / D, ch = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) M = fmaxf(M, sm.mm[k][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        const float mw = sm.mm[k][h];
+        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        L = fmaf(f, sm.ll[k][h], L);
+        O = fmaf(f, sm.oo[k][h][ch], O);
+      }
+    }
+    const int64_t row = ((int64_t)b * a.hq + kvh * GQ + h) * a.nsplit + split;
+    a.ws_o[row * D + ch] = O;
+    if (ch == 0) store_partial_ml(a, b, kvh * GQ + h, split, M, L);
   }
 }
 
@@ -381,15 +495,44 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int quarter = l >> 4, tl = l & 15;
-  for (int idx = tid; idx < GQ * D; idx += 256) {
-    const int h = idx / D, j = idx % D;
-    sm.qx[h][j] = __half2float(a.q[((int64_t)b * a.hq + kvh * GQ + h) * D + j]) * a.scale * kLog2e;
-  }
-  __syncthreads();
   const int n_sink = min(n, kSink);
   const int tau = n > kSink ? (n - kSink) % kGroup : 0;
   const int n_exact = max(0, n_sink + tau);
   const int64_t bh = (int64_t)b * a.c.hkv + kvh;
+
+  // Query loads first, then both rounds' K and V quarter rows (an invalid
+  // token reads sink row 0, which always exists, and is masked later).
+  constexpr int QPT = (GQ * D + 255) / 256;
+  __half qh[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    qh[i] = idx < GQ * D ? a.q[((int64_t)b * a.hq + kvh * GQ) * D + idx] : __half(0.f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 kr[2][QD / 8], vr[2][QD / 8];
+  bool valid[2];
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const int e = kGroup * es + 32 * w + kExactTok * round + tl;
+    valid[round] = e < n_exact;
+    const bool in_tail = valid[round] && e >= n_sink;
+    const int64_t row = bh * kGroup + (valid[round] ? (in_tail ? e - n_sink : e) : 0);
+    const uint4* kp = reinterpret_cast<const uint4*>((in_tail ? a.c.tail_k : a.c.sink_k) + row * D + quarter * QD);
+    const uint4* vp = reinterpret_cast<const uint4*>((in_tail ? a.c.tail_v : a.c.sink_v) + row * D + quarter * QD);
+#pragma unroll
+    for (int c = 0; c < QD / 8; ++c) {
+      kr[round][c] = kp[c];
+      vr[round][c] = vp[c];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < GQ * D) sm.qx[idx / D][idx % D] = __half2float(qh[i]) * a.scale * kLog2e;
+  }
+  __syncthreads();
 
   float m_run[GQ], l_run[GQ], o[GQ][CPLX];
 #pragma unroll
@@ -399,62 +542,49 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
 #pragma unroll
     for (int c = 0; c < CPLX; ++c) o[h][c] = 0.f;
   }
+#pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int e0 = kGroup * es + 32 * w + kExactTok * round;
-    const int e = e0 + tl;
-    const bool valid = e < n_exact;
+    const bool ok = valid[round];
     float dot[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
     uint16_t* vrow = &sm.v[w][tl][quarter * QD];
-    if (valid) {
-      const size_t row = e < n_sink ? (size_t)(bh * kGroup + e) : (size_t)(bh * kGroup + (e - n_sink));
-      const uint4* kp =
-          reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_k : a.c.tail_k) + row * D + quarter * QD);
-      const uint4* vp =
-          reinterpret_cast<const uint4*>((e < n_sink ? a.c.sink_v : a.c.tail_v) + row * D + quarter * QD);
-      uint4 kr[QD / 8], vr[QD / 8];
 #pragma unroll
-      for (int c = 0; c < QD / 8; ++c) {
-        kr[c] = kp[c];
-        vr[c] = vp[c];
+    for (int c = 0; c < QD / 8; ++c)
+      reinterpret_cast<uint4*>(vrow)[c] = ok ? vr[round][c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < QD / 8; ++c) {
+      const uint32_t ws[4] = {kr[round][c].x, kr[round][c].y, kr[round][c].z, kr[round][c].w};
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        const float4 qa = *reinterpret_cast<const float4*>(&sm.qx[h][quarter * QD + 8 * c]);
+        const float4 qb = *reinterpret_cast<const float4*>(&sm.qx[h][quarter * QD + 8 * c + 4]);
+        dot[h] = fmaf(qa.x, h2f((uint16_t)(ws[0] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qa.y, h2f((uint16_t)(ws[0] >> 16)), dot[h]);
+        dot[h] = fmaf(qa.z, h2f((uint16_t)(ws[1] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qa.w, h2f((uint16_t)(ws[1] >> 16)), dot[h]);
+        dot[h] = fmaf(qb.x, h2f((uint16_t)(ws[2] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qb.y, h2f((uint16_t)(ws[2] >> 16)), dot[h]);
+        dot[h] = fmaf(qb.z, h2f((uint16_t)(ws[3] & 0xFFFFu)), dot[h]);
+        dot[h] = fmaf(qb.w, h2f((uint16_t)(ws[3] >> 16)), dot[h]);
       }
-#pragma unroll
-      for (int c = 0; c < QD / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = vr[c];
-#pragma unroll
-      for (int c = 0; c < QD / 8; ++c) {
-        const uint32_t ws[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-          const float4 qa = *reinterpret_cast<const float4*>(&sm.qx[h][quarter * QD + 8 * c]);
-          const float4 qb = *reinterpret_cast<const float4*>(&sm.qx[h][quarter * QD + 8 * c + 4]);
-          dot[h] = fmaf(qa.x, h2f((uint16_t)(ws[0] & 0xFFFFu)), dot[h]);
-          dot[h] = fmaf(qa.y, h2f((uint16_t)(ws[0] >> 16)), dot[h]);
-          dot[h] = fmaf(qa.z, h2f((uint16_t)(ws[1] & 0xFFFFu)), dot[h]);
-          dot[h] = fmaf(qa.w, h2f((uint16_t)(ws[1] >> 16)), dot[h]);
-          dot[h] = fmaf(qb.x, h2f((uint16_t)(ws[2] & 0xFFFFu)), dot[h]);
-          dot[h] = fmaf(qb.y, h2f((uint16_t)(ws[2] >> 16)), dot[h]);
-          dot[h] = fmaf(qb.z, h2f((uint16_t)(ws[3] & 0xFFFFu)), dot[h]);
-          dot[h] = fmaf(qb.w, h2f((uint16_t)(ws[3] >> 16)), dot[h]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < QD / 8; ++c) reinterpret_cast<uint4*>(vrow)[c] = make_uint4(0, 0, 0, 0);
     }
-    float pt[GQ];
+    const bool valid_r = ok;
+  float pt[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      float lg = dot[h];
-      lg += __shfl_xor(lg, 16, 64);
-      lg += __shfl_xor(lg, 32, 64);
-      lg = valid ? lg : -INFINITY;
-      const float rmax = wave_max(lg);
+      // The four quarters of a row sum to the logit, after which every DPP
+      // row holds the same 16 logits: row reductions give the round's
+      // maximum and sum.
+      float lg = xor32_sum(xor16_sum(dot[h]));
+      lg = valid_r ? lg : -INFINITY;
+      const float rmax = row16_max(lg);
       const float m_new = fmaxf(m_run[h], rmax);
       const float alpha = (m_run[h] == -INFINITY) ? 0.f : exp2f(m_run[h] - m_new);
-      const float p = (valid && m_new != -INFINITY) ? exp2f(lg - m_new) : 0.f;
+      const float p = (valid_r && m_new != -INFINITY) ? exp2f(lg - m_new) : 0.f;
       pt[h] = p;
-      l_run[h] = l_run[h] * alpha + wave_sum(quarter == 0 ? p : 0.f);
+      l_run[h] = l_run[h] * alpha + row16_sum(p);
       m_run[h] = m_new;
 #pragma unroll
       for (int c = 0; c < CPLX; ++c) o[h][c] *= alpha;
@@ -527,125 +657,183 @@ union DecodeSmemU {
 template <int D, int KB, int VB, int GQ>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecodeSmemU<D, KB, VB, GQ> sm;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // The exact splits (workgroups 0 and 1) go first in dispatch order; their
+  // partials follow the record splits' in the workspace.
+  const int nex = a.nsplit - a.n_rec_splits;
+  const int bx = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int n = a.c.seq_len[b];
-  if (split < a.n_rec_splits)
-    record_split<D, KB, VB, GQ>(sm.rec, a, b, kvh, split, n);
+  if (bx >= nex)
+    record_split<D, KB, VB, GQ>(sm.rec, a, b, kvh, bx - nex, n);
   else
-    exact_split<D, GQ>(sm.ex, a, b, kvh, split - a.n_rec_splits, split, n);
+    exact_split<D, GQ>(sm.ex, a, b, kvh, bx, a.n_rec_splits + bx, n);
 }
 
 // One workgroup (256 threads) per (query head, request): log-sum-exp merge of
-// all splits, one inverse Hadamard of the record part, normalization.
+// all splits, one inverse Hadamard of the record part, normalization.  Every
+// wave finds the global maximum M and the normalizer L itself; wave w sums
+// the weighted partial outputs of splits w, w+4, ... with lane l holding
+// channels P*l .. P*l+P-1; one barrier joins the four sums.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int MAXS = 1024;  // splits handled per pass of the weight table
-  __shared__ float wgt[MAXS];
-  __shared__ float red[256];
-  __shared__ float orot[D];
-  __shared__ float oex[D];
+  constexpr int P = D / 64;
+  __shared__ float orec[kWaves][D];
+  __shared__ float oex[kWaves][D];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int64_t base = ((int64_t)b * a.hq + hq) * a.nsplit;
-  float m = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += 256) m = fmaxf(m, a.ws_ml[2 * (base + s)]);
-  red[tid] = m;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float lsum = 0.f;
-  for (int idx = tid; idx < D; idx += 256) {
-    orot[idx] = 0.f;
-    oex[idx] = 0.f;
-  }
-  constexpr int P = 256 / D;  // threads per channel
-  const int j = tid % D, part = tid / D;
-  float accr = 0.f, acce = 0.f;
-  for (int s0 = 0; s0 < a.nsplit; s0 += MAXS) {
-    const int cnt = min(MAXS, a.nsplit - s0);
-    __syncthreads();
-    for (int s = tid; s < cnt; s += 256) {
-      const float ms = a.ws_ml[2 * (base + s0 + s)];
-      const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      wgt[s] = f;
-      lsum = fmaf(f, a.ws_ml[2 * (base + s0 + s) + 1], lsum);
+  const int w = tid >> 6, l = tid & 63;
+  const int ns = a.nsplit, nrec = a.n_rec_splits;
+  const int64_t base = ((int64_t)b * a.hq + hq) * ns;
+  const float* ml = a.ws_ml + 2 * base;
+
+  float mloc = -INFINITY;
+  for (int s = l; s < ns; s += kWave) mloc = fmaxf(mloc, ml[2 * s]);
+  const float M = wave_max_f(mloc);
+  float lloc = 0.f;
+  if (M != -INFINITY) {
+    for (int s = l; s < ns; s += kWave) {
+      const float m = ml[2 * s];
+      lloc += m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * s + 1];
     }
-    __syncthreads();
-    int s = part;
-    for (; s + 7 * P < cnt; s += 8 * P) {
-      float v[8];
+  }
+  const float L = wave_sum_f(lloc);
+
+  float ar[P], ae[P];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.ws_o[(base + s0 + s + u * P) * D + j];
+  for (int i = 0; i < P; ++i) ar[i] = ae[i] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 8
+    for (int s = w; s < ns; s += kWaves) {
+      const float m = ml[2 * s];
+      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      const float* o = a.ws_o + (base + s) * D + P * l;
+      float ov[P];
+      if constexpr (P == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(o);
+        ov[0] = x.x;
+        ov[1] = x.y;
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(o);
+        ov[0] = x.x;
+        ov[1] = x.y;
+        ov[2] = x.z;
+        ov[3] = x.w;
+      }
+      if (s < nrec) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (s0 + s + u * P < a.n_rec_splits)
-          accr = fmaf(wgt[s + u * P], v[u], accr);
-        else
-          acce = fmaf(wgt[s + u * P], v[u], acce);
+        for (int i = 0; i < P; ++i) ar[i] = fmaf(f, ov[i], ar[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) ae[i] = fmaf(f, ov[i], ae[i]);
       }
     }
-    for (; s < cnt; s += P) {
-      const float v = a.ws_o[(base + s0 + s) * D + j];
-      if (s0 + s < a.n_rec_splits)
-        accr = fmaf(wgt[s], v, accr);
-      else
-        acce = fmaf(wgt[s], v, acce);
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    orec[w][P * l + i] = ar[i];
+    oex[w][P * l + i] = ae[i];
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float x[P], e[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    x[i] = (orec[0][P * l + i] + orec[1][P * l + i]) + (orec[2][P * l + i] + orec[3][P * l + i]);
+    e[i] = (oex[0][P * l + i] + oex[1][P * l + i]) + (oex[2][P * l + i] + oex[3][P * l + i]);
+  }
+  // Inverse rotation of the record part (H symmetric): channel c = P*l + i;
+  // butterflies over the bits of i in registers, over the bits of l across
+  // lanes.
+#pragma unroll
+  for (int st = 1; st < P; st <<= 1) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (!(i & st)) {
+        const float u = x[i], v = x[i + st];
+        x[i] = u + v;
+        x[i + st] = u - v;
+      }
     }
   }
-  red[tid] = lsum;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float L = red[0];
-  atomicAdd(&orot[j], accr);
-  atomicAdd(&oex[j], acce);
-  __syncthreads();
-  // Inverse rotation of the record part (H symmetric): orot <- orot H.
-  for (int st = 1; st < D; st <<= 1) {
-    float x = 0.f, y = 0.f;
-    if (tid < D) {
-      x = orot[tid];
-      y = orot[tid ^ st];
+#pragma unroll
+  for (int st = 1; st < kWave; st <<= 1) {
+    const bool hi = l & st;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const float pv = __shfl_xor(x[i], st, kWave);
+      x[i] = hi ? pv - x[i] : x[i] + pv;
     }
-    __syncthreads();
-    if (tid < D) orot[tid] = (tid & st) ? y - x : x + y;
-    __syncthreads();
   }
-  if (tid < D) {
-    const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
-    const float o = L > 0.f ? (orot[tid] * rs + oex[tid]) / L : 0.f;
-    a.out[((int64_t)b * a.hq + hq) * D + tid] = o;
-  }
+  const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  float* out = a.out + ((int64_t)b * a.hq + hq) * D + P * l;
+#pragma unroll
+  for (int i = 0; i < P; ++i) out[i] = (x[i] * rs + e[i]) * inv;
 }
 
-DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups) {
+DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs) {
   DecodePlan p;
-  // About four workgroups per CU on 256 CUs, each walking a contiguous range
-  // of groups of one (request, KV head).
+  // Each record workgroup is four independent waves walking consecutive runs
+  // of groups_per_wave groups of one (request, KV head).  The whole grid
+  // (record and exact workgroups) should be resident at once, so the smallest
+  // run length whose grid fits `resident_wgs` maximises parallelism.
   const int64_t pairs = (int64_t)batch * hkv;
-  const int64_t target = 1024;
+  const int64_t target = resident_wgs;
   p.n_exact_splits = 2;  // exact tokens [0,128) and [128,256)
-  int gps = 1;
+  int gpw = 1;
   if (max_groups > 0) {
-    while (gps < max_groups) {
-      const int64_t splits = (max_groups + gps - 1) / gps;
+    while (4 * gpw < max_groups) {
+      const int64_t splits = (max_groups + 4 * gpw - 1) / (4 * gpw);
       if (pairs * (splits + p.n_exact_splits) <= target) break;
-      ++gps;
+      ++gpw;
     }
   }
-  p.groups_per_split = gps;
-  p.groups_per_wave = gps;
-  p.n_rec_splits = max_groups > 0 ? (max_groups + gps - 1) / gps : 0;
+  p.groups_per_wave = gpw;
+  p.groups_per_split = 4 * gpw;
+  p.n_rec_splits = max_groups > 0 ? (max_groups + 4 * gpw - 1) / (4 * gpw) : 0;
   p.nsplit = p.n_rec_splits + p.n_exact_splits;
   const size_t rows = (size_t)batch * hq * p.nsplit;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
   p.ws_bytes = o_bytes + ((rows * 2 * sizeof(float) + 255) & ~(size_t)255);
   return p;
+}
+
+template <int D, int KB, int VB, int GQ>
+static int resident_t(int dev) {
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, KB, VB, GQ>, 256, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return per_cu * cus;
+}
+
+template <int D, int KB, int VB>
+static int resident_g(int gq, int dev) {
+  return gq == 1 ? resident_t<D, KB, VB, 1>(dev) : gq == 2 ? resident_t<D, KB, VB, 2>(dev) : resident_t<D, KB, VB, 4>(dev);
+}
+
+int decode_resident_wgs(int D, int kb, int vb, int gq) {
+  // Cached per device and kernel instance: [device][D][kb][vb][gq].
+  static std::atomic<int> cache[16][2][2][2][3];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxResidentWgs;
+  const int di = D == 128 ? 0 : 1, ki = kb == 2 ? 0 : 1, vi = vb == 2 ? 0 : 1, gi = gq == 1 ? 0 : gq == 2 ? 1 : 2;
+  std::atomic<int>* slot = dev < 16 ? &cache[dev][di][ki][vi][gi] : nullptr;
+  int r = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (r > 0) return r;
+  if (D == 128) {
+    if (kb == 2 && vb == 2) r = resident_g<128, 2, 2>(gq, dev);
+    else if (kb == 2) r = resident_g<128, 2, 4>(gq, dev);
+    else if (vb == 2) r = resident_g<128, 4, 2>(gq, dev);
+    else r = resident_g<128, 4, 4>(gq, dev);
+  } else {
+    if (kb == 2 && vb == 2) r = resident_g<256, 2, 2>(gq, dev);
+    else if (kb == 2) r = resident_g<256, 2, 4>(gq, dev);
+    else if (vb == 2) r = resident_g<256, 4, 2>(gq, dev);
+    else r = resident_g<256, 4, 4>(gq, dev);
+  }
+  r = r > 0 ? std::min(r, kMaxResidentWgs) : kMaxResidentWgs;
+  if (slot) slot->store(r, std::memory_order_relaxed);
+  return r;
 }
 
 template <int D, int KB, int VB, int GQ>

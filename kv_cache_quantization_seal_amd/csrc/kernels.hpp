@@ -76,7 +76,13 @@ struct DecodePlan {
   size_t ws_bytes;
 };
 
-DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups);
+// Workgroups of the split kernel that can be resident at once is at most
+// this (the workspace query, which has no device, plans with it).
+constexpr int kMaxResidentWgs = 4096;
+
+DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs);
+// Resident split workgroups on the current device for this configuration.
+int decode_resident_wgs(int D, int kb, int vb, int gq);
 
 hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* dst, int64_t stride, float* dbg, int n,
                              int iters, hipStream_t st);

@@ -110,7 +110,11 @@ size_t kvarn_group_bytes(const kvarn_config* cfg) {
 
 size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t max_groups) {
   if (check_cfg(cfg) != KVARN_OK || batch <= 0 || max_groups < 0) return 0;
-  return kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch, max_groups).ws_bytes;
+  // Planned for the most resident workgroups any device allows: a launch
+  // plans for fewer, hence fewer splits and no more workspace.
+  return kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch, max_groups,
+                            kvarn::kMaxResidentWgs)
+      .ws_bytes;
 }
 
 const char* kvarn_last_error(void) { return g_err; }
@@ -221,8 +225,10 @@ static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* ca
   if ((phases & 2) && !out) return fail(KVARN_EINVAL, "out must be non-NULL");
   if ((q && !aligned(q, 16)) || (out && !aligned(out, 16)))
     return fail(KVARN_EINVAL, "q and out must be 16-byte aligned");
-  const kvarn::DecodePlan p =
-      kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch, cache->max_groups);
+  const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
+                                                  cfg->num_q_heads / cfg->num_kv_heads);
+  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
+                                                 cache->max_groups, resident);
   if (!workspace || ws_bytes < p.ws_bytes)
     return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, p.ws_bytes);
   if (!aligned(workspace, 256)) return fail(KVARN_EINVAL, "workspace must be 256-byte aligned");
