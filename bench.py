@@ -47,18 +47,111 @@ def parse():
     ap.add_argument("--cpu-seal-groups", type=int, default=48)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run this many eager steps only (for rocprofv3) and exit")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 8 device-to-device copies of MIB MiB (a plain copy kernel of known "
+                         "size, the reference for the HBM counters) and exit")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIRS"),
+                    help="summarize rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --profile-steps and of "
+                         "--copy-calibration (COPY_DIRS = 'fetch_dir,write_dir') into profiles/ and exit")
     return ap.parse_args()
 
 
 def algorithmic_decode_bytes(wl, lens, k_rec, v_rec):
-    """Bytes one decode launch must move: records + exact fp16 rows + q + out."""
+    """Bytes the split kernel must move per launch: every sealed record once,
+    the exact fp16 sink and tail rows (K and V), and the query."""
     total = 0
     for n in lens:
         g = max(0, (n - 128) // 128)
         exact = min(n, 128) + (n - 128 - 128 * g if n > 128 else 0)
         total += wl.num_kv_heads * (g * (k_rec + v_rec) + exact * wl.head_dim * 2 * 2)
-    total += wl.batch * wl.num_q_heads * wl.head_dim * (2 + 4)
+    total += wl.batch * wl.num_q_heads * wl.head_dim * 2
     return total
+
+
+def decode_source_sha():
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(here, "kv_cache_quantization_seal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"decode_split_kernel_{workload}_hbm_traffic.txt")
+
+
+def read_traffic(workload):
+    """Measured HBM bytes per split-kernel launch, if the counters were taken
+    on the current kernel source; else None."""
+    try:
+        kv = {}
+        with open(traffic_file(workload)) as fh:
+            for line in fh:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("decode_source_sha") != decode_source_sha():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _pmc_rows(d, counter, kernel_substr):
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter and kernel_substr in r.get("Kernel_Name", ""):
+                    vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic_summary(args):
+    """Scale the decode kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
+    what the same counters read for a plain copy of known size."""
+    fetch_dir, write_dir, copy_dirs = args.traffic_summary
+    cfetch_dir, cwrite_dir = copy_dirs.split(",")
+    from kv_cache_quantization_seal_amd import synth, kvarn as K
+    wl = synth.WORKLOADS[args.workload]
+    copy_bytes = args.copy_calibration * 2**20
+    if copy_bytes <= 0:
+        sys.exit("--traffic-summary needs --copy-calibration MIB (the size the copy runs used)")
+    cf = _pmc_rows(cfetch_dir, "FETCH_SIZE", "copy")
+    cw = _pmc_rows(cwrite_dir, "WRITE_SIZE", "copy")
+    df = _pmc_rows(fetch_dir, "FETCH_SIZE", "decode_split_kernel")
+    dw = _pmc_rows(write_dir, "WRITE_SIZE", "decode_split_kernel")
+    if not (cf and cw and df and dw):
+        sys.exit("missing counter rows (copy fetch/write, decode fetch/write): "
+                 f"{len(cf)} {len(cw)} {len(df)} {len(dw)}")
+    # Per copy dispatch the kernel reads and writes copy_bytes.
+    f_scale = copy_bytes / (np.median(cf) * 1024)
+    w_scale = copy_bytes / (np.median(cw) * 1024)
+    fetch = np.median(df) * 1024 * f_scale
+    write = np.median(dw) * 1024 * w_scale
+    lens = [wl.start_len(b) for b in range(wl.batch)]
+    alg = algorithmic_decode_bytes(wl, lens, K.record_bytes(wl.head_dim, wl.k_bits),
+                                   K.record_bytes(wl.head_dim, wl.v_bits))
+    with open(traffic_file(wl.name), "w") as fh:
+        fh.write(f"# HBM traffic of decode_split_kernel, workload {wl.name}, from rocprofv3 --pmc\n")
+        fh.write("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by\n")
+        fh.write(f"# bytes / counter of a plain {args.copy_calibration} MiB device copy run the same way.\n")
+        fh.write(f"decode_source_sha = {decode_source_sha()}\n")
+        fh.write(f"copy_bytes = {copy_bytes}\n")
+        fh.write(f"copy_fetch_kib = {np.median(cf):.1f}\ncopy_write_kib = {np.median(cw):.1f}\n")
+        fh.write(f"fetch_scale = {f_scale:.4f}\nwrite_scale = {w_scale:.4f}\n")
+        fh.write(f"decode_fetch_kib = {np.median(df):.1f}  (dispatches {len(df)})\n")
+        fh.write(f"decode_write_kib = {np.median(dw):.1f}  (dispatches {len(dw)})\n")
+        fh.write(f"fetch_bytes_per_launch = {fetch:.0f}\nwrite_bytes_per_launch = {write:.0f}\n")
+        fh.write(f"traffic_bytes_per_launch = {fetch + write:.0f}\n")
+        fh.write(f"algorithmic_bytes_per_launch = {alg}\n")
+        fh.write(f"traffic_over_algorithmic = {(fetch + write) / alg:.3f}\n")
+    print(open(traffic_file(wl.name)).read())
 
 
 def cpu_baseline(wl, k_stream0, v_stream0, q0, n_seal_groups):
@@ -108,9 +201,23 @@ def main():
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the KVarN hot path here is built and measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
     import torch
     from kv_cache_quantization_seal_amd import kvarn as K
     from kv_cache_quantization_seal_amd import synth
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 8 copies of {n} bytes", file=sys.stderr, flush=True)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
@@ -232,28 +339,33 @@ def main():
     steps_per_s = args.steps / t_total
     value = B * steps_per_s
 
-    # ---- live timing of the dominant kernel (the fused decode kernel) -----
-    reset()
-    torch.cuda.synchronize()
-    reps = 8 * ncopy
-    gk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gk, stream=stream):
-        for r in range(reps):
-            caches[r % ncopy].decode_attn(q_all[0], out=outs[r % ncopy])
-    torch.cuda.synchronize()
-    gk.replay()  # warm
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        gk.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    t_kernel = ev0.elapsed_time(ev1) / 1e3 / reps
+    # ---- live timing of the dominant kernel (the split kernel) and the combine
+    def time_graph(fn):
+        reset()
+        torch.cuda.synchronize()
+        reps = 8 * ncopy
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk, stream=stream):
+            for r in range(reps):
+                fn(r)
+        torch.cuda.synchronize()
+        gk.replay()  # warm
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            gk.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / reps
+
+    t_kernel = time_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]))
+    t_combine = time_graph(lambda r: caches[r % ncopy].decode_combine(outs[r % ncopy]))
     bytes_launch = algorithmic_decode_bytes(wl, lens0, k_rec, v_rec)
     achieved = bytes_launch / t_kernel
-    print(f"[bench] decode kernel: {t_kernel * 1e6:.2f} us/launch, {achieved / 1e12:.2f} TB/s "
-          f"({achieved / HBM_PEAK * 100:.1f}% of HBM); step {t_total / args.steps * 1e6:.2f} us",
-          file=sys.stderr, flush=True)
+    traffic = read_traffic(wl.name)
+    print(f"[bench] decode split kernel: {t_kernel * 1e6:.2f} us/launch, {achieved / 1e12:.2f} TB/s "
+          f"({achieved / HBM_PEAK * 100:.1f}% of HBM); combine {t_combine * 1e6:.2f} us; "
+          f"step {t_total / args.steps * 1e6:.2f} us", file=sys.stderr, flush=True)
 
     line = {
         "metric": "quantized decode-attn tokens/s + % HBM peak; seal_group groups/s (1 MI355X)",
@@ -272,9 +384,9 @@ def main():
                    "context": lens0[0], "k_bits": wl.k_bits, "v_bits": wl.v_bits, "layer_caches": ncopy,
                    "step": "append + seal-if-due + decode attention (one layer)"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": None,
+                     "frac": achieved / HBM_PEAK, "traffic": traffic,
                      "kernel": "decode_split_kernel", "bytes_per_launch": bytes_launch,
-                     "us_per_launch": t_kernel * 1e6},
+                     "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6},
         "seal": seal,
     }
     if not args.no_cpu:

@@ -144,3 +144,41 @@ def gaussian_tile(seed: int, tokens: int, dim: int, n_out: int = 4, m_out: float
         x[:, rng.choice(dim, n_out, replace=False)] *= m_out
     x *= rng.lognormal(0.0, TOKEN_SIGMA, size=(tokens, 1))
     return x.astype(np.float16)
+
+
+def kv_streams_device(wl: Workload, length: int, device, pairs_from_host=()):
+    """fp16 K and V of every (request, KV head) at once: [B][Hkv][length][D].
+
+    Same recipe as ``kv_stream`` (outlier channels, lognormal token norms,
+    NeoX RoPE with theta 1e6), drawn on the device from a torch generator
+    seeded per (workload, request, head), so a full-size cache is built in
+    seconds.  These values are not the host stream's; the pairs listed in
+    ``pairs_from_host`` are filled from ``kv_stream`` instead, so the oracle
+    can be run on exactly those.
+    """
+    import torch
+    B, H, d = wl.batch, wl.num_kv_heads, wl.head_dim
+    K = torch.empty((B, H, length, d), dtype=torch.float16, device=device)
+    V = torch.empty_like(K)
+    half = d // 2
+    inv_freq = ROPE_THETA ** (-torch.arange(half, dtype=torch.float64, device=device) * 2.0 / d)
+    ang = torch.arange(length, dtype=torch.float64, device=device)[:, None] * inv_freq[None, :]
+    cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
+    gen = torch.Generator(device=device)
+    for b in range(B):
+        for h in range(H):
+            gen.manual_seed(((wl.seed * 1000003 + wl.wid) * 1000003 + b) * 1000003 + h)
+            k = torch.randn((length, d), generator=gen, device=device)
+            out = torch.randperm(d, generator=gen, device=device)[:wl.n_out]
+            k[:, out] *= wl.m_out
+            k *= torch.exp(TOKEN_SIGMA * torch.randn((length, 1), generator=gen, device=device))
+            k1, k2 = k[:, :half], k[:, half:]
+            K[b, h] = torch.cat([k1 * cos - k2 * sin, k2 * cos + k1 * sin], dim=-1).half()
+            v = torch.randn((length, d), generator=gen, device=device)
+            v *= torch.exp(TOKEN_SIGMA * torch.randn((length, 1), generator=gen, device=device))
+            V[b, h] = v.half()
+    for b, h in pairs_from_host:
+        k, v = kv_stream(wl, b, h, length)
+        K[b, h] = torch.from_numpy(k).to(device)
+        V[b, h] = torch.from_numpy(v).to(device)
+    return K, V

@@ -1,0 +1,76 @@
+"""Full-size sampled parity: every workload at its real shape and batch, in
+the launch configuration the benchmark times.
+
+The whole cache is built on the GPU (bulk prefill seal of every pair); the
+oracle then checks sampled (request, KV head) pairs end to end from the same
+fp16 streams: its own seal of every group and its own decode attention,
+against the GPU's decode output (2e-3 max-abs), and the GPU records of a
+few sampled groups against the oracle's seal of those tiles (packing
+bit-exact, codes and scales per the tile rules).  The Qwen3-4B shape also
+runs its pseudo-decode: 128 steps of append-one-token, seal-if-due and
+attend, over which every request seals one more group.
+
+Pairs that are not sampled hold data from the device-side generator (same
+recipe, different draws); attention per pair is independent of the others.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_seal_amd import kvarn as K
+from kv_cache_quantization_seal_amd import synth
+from oracle import kvarn_oracle as O
+from tests.gpu_util import ATTN_ATOL, check_sealed_tile
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (sampled pairs, pseudo-decode steps)
+    "llama31_8b_32k": ([(0, 0), (0, 7)], 0),
+    "qwen3_4b_16k_b16": ([(0, 0), (15, 7)], 128),
+    "phi4_14b_32k_b8": ([(0, 0), (7, 9)], 0),
+    "longctx_d256_64k_b4": ([(3, 15)], 0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_full_size_sampled(name):
+    wl = synth.WORKLOADS[name]
+    pairs, steps = CASES[name]
+    B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    gq = hq // hkv
+    dev = torch.device("cuda:0")
+    lens0 = [wl.start_len(b) for b in range(B)]
+    length = max(lens0) + steps + 1
+    Kd, Vd = synth.kv_streams_device(wl, length, dev, pairs_from_host=pairs)
+    max_groups = (max(lens0) + steps - 128) // 128 + 1
+    cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
+    cache = K.KVarNCache(cfg, B, max_groups, device=dev)
+    cache.prefill(Kd, Vd, lens0)
+    for s in range(steps):
+        idx = torch.tensor([n + s for n in lens0], device=dev)
+        knew = Kd[torch.arange(B, device=dev), :, idx].contiguous()   # [B][Hkv][D]
+        vnew = Vd[torch.arange(B, device=dev), :, idx].contiguous()
+        cache.append(knew, vnew)
+        cache.seal_group()
+    lens = [n + steps for n in lens0]
+    q = np.stack([synth.queries(wl, b, 1)[0] for b in range(B)])
+    out = cache.decode_attn(torch.from_numpy(q).to(dev)).cpu().numpy()
+    assert list(cache.seq_len.cpu().numpy()) == lens
+
+    worst = 0.0
+    for b, h in pairs:
+        k, v = synth.kv_stream(wl, b, h, length)
+        n = lens[b]
+        st = O.state_from_stream(k[:n], v[:n], wl.k_bits, wl.v_bits)
+        ref = O.decode_attention(q[b, h * gq:(h + 1) * gq], [st], 1)
+        err = float(np.abs(out[b, h * gq:(h + 1) * gq] - ref).max())
+        worst = max(worst, err)
+        ng = (n - 128) // 128
+        for g in sorted({0, ng // 2, ng - 1}):
+            lo = 128 + 128 * g
+            for kind, x, bits in (("k", k, wl.k_bits), ("v", v, wl.v_bits)):
+                rec = bytes(cache.record(b, h, g, kind).cpu().numpy())
+                check_sealed_tile(rec, None, O.seal_tile(x[lo:lo + 128], bits), d, bits, kind)
+    print(f"{name}: sampled pairs {pairs}, decode max abs err {worst:.3e}")
+    assert worst <= ATTN_ATOL
