@@ -23,32 +23,56 @@
 // needs c and X_r: s_t = 2 max_j |X_r,tj / c_j| / (2^b - 1) and
 // code = rne(X_r,tj / c_j / s_t + mid).
 //
-// Data layout in the workgroup (2*D threads, D/32 waves):
-//   row role: wave w owns token t = 64*(w / (D/64)) + lane and the 64 channels
-//             of block w % (D/64)  -> A_row[64] in VGPRs;
-//   col role: wave w owns channel j = 64*(w / 2) + lane and the 64 tokens of
-//             half w % 2             -> A_col[64] in VGPRs;
-//   LDS holds X_r (fp32, row pitch D+4) plus the factor vectors.  Each
-//   half-step is 64 register FMAs per thread against an LDS-broadcast vector,
-//   a partial-sum exchange and one owner-computed division.
+// Data layout in the workgroup (2*D threads, D/32 waves), after the rotation:
+//   row role: lane l of wave w owns tokens 4*tq .. 4*tq+3 and channels
+//             16*cb .. 16*cb+15 (tq = RPW*w + l / RL, cb = l % RL, RL = D/16
+//             lanes per token quad) -> A_row[4][16] in VGPRs;
+//   col role: lane l of wave w owns channels 4*cq .. 4*cq+3 and tokens
+//             16*tb .. 16*tb+15 (cq = 8*w + l / 8, tb = l % 8)
+//             -> A_col[16][4] in VGPRs.
+//   LDS holds X_r (fp32, row pitch D+4) plus the factor vectors.  A half-step
+//   reads 16 factors from LDS (four 128-bit broadcasts) for 64 register FMAs;
+//   the partial sums of a token quad (channel quad) sit in RL (8) adjacent
+//   lanes and meet through DPP; the first lane publishes the four new
+//   factors.  One barrier per half-step.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace kvarn {
 
 template <int D>
-struct SealSmem {
+struct alignas(16) SealSmem {
   static constexpr int kPitch = D + 4;
   static constexpr int kBlocks = D / 64;
   float x[kGroup * kPitch];
   float u[D];                 // 1 / c_j^2
   float v[kGroup];            // 1 / r_t^2
-  float part[kBlocks][kGroup];  // row partials (sums, then maxima)
-  float qcol[2][D];           // column partials
   float c2[D];                // c_j^2
   float cinv[D];              // 1 / c_j
   float inv[kGroup];          // per-token inverse step (2^b - 1) / (2 M_t)
 };
+
+// Sum / maximum over the 8 lanes 8k .. 8k+7 (every lane receives it).
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  return v;
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return v;
+}
+template <int RL>
+__device__ __forceinline__ float sum_rl(float v) {
+  return RL == 8 ? sum8(v) : row16_sum(v);
+}
+template <int RL>
+__device__ __forceinline__ float max_rl(float v) {
+  return RL == 8 ? max8(v) : row16_max(v);
+}
 
 template <int D, int BITS, bool TOKEN_MAJOR>
 __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_t* __restrict__ rec,
@@ -58,16 +82,17 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
   constexpr int LEVELS = (1 << BITS) - 1;
   constexpr float MID = 0.5f * LEVELS;
   constexpr int CODE_BYTES = kGroup * D * BITS / 8;
+  constexpr int RL = D / 16;          // row role: lanes per token quad
+  constexpr int RPW = 64 / RL;        // row role: token quads per wave
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  const int rb = w % NB;            // row role: channel block
-  const int t = 64 * (w / NB) + lane;  // row role: token
-  const int ca = w & 1;             // col role: token half
-  const int j = 64 * (w >> 1) + lane;  // col role: channel
 
-  float x[64];
+  // ---- rotation: thread (token tl, 64-channel block bl) ------------------
   {
-    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)t * D + 64 * rb);
+    const int bl = w % NB;
+    const int tl = 64 * (w / NB) + lane;
+    float x[64];
+    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)tl * D + 64 * bl);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint4 q = p[k];
@@ -78,158 +103,229 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
         x[8 * k + 2 * e + 1] = h2f((uint16_t)(ws[e] >> 16));
       }
     }
+    rotate_row_slice<D, P>(x, sm.x, tl, bl);
+    const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;  // 1/sqrt(D)
+    float* xrow = sm.x + tl * P + 64 * bl;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      *reinterpret_cast<float4*>(xrow + 4 * k) =
+          make_float4(x[4 * k] * rs, x[4 * k + 1] * rs, x[4 * k + 2] * rs, x[4 * k + 3] * rs);
   }
-  float* xrow = sm.x + t * P + 64 * rb;
-  rotate_row_slice<D, P>(x, sm.x, t, rb);
-  const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;  // 1/sqrt(D)
-#pragma unroll
-  for (int i = 0; i < 64; ++i) x[i] *= rs;
-#pragma unroll
-  for (int k = 0; k < 16; ++k)
-    *reinterpret_cast<float4*>(xrow + 4 * k) = make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
-  // x now becomes A_row = X_r^2.
-#pragma unroll
-  for (int i = 0; i < 64; ++i) x[i] *= x[i];
-  if (ca == 0) {
-    sm.u[j] = 1.0f;
-    sm.c2[j] = 1.0f;
+  if (tid < D) {
+    sm.u[tid] = 1.0f;
+    sm.c2[tid] = 1.0f;
   }
   __syncthreads();
-  float acol[64];
+
+  // ---- A = X_r^2 blocks --------------------------------------------------
+  const int tq = RPW * w + lane / RL, cb = lane % RL;  // row role
+  const int cq = 8 * w + (lane >> 3), tb = lane & 7;   // col role
+  float ar[4][16], ac[16][4];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const float a = sm.x[(64 * ca + i) * P + j];
-    acol[i] = a * a;
+  for (int r = 0; r < 4; ++r) {
+    const float* xr = sm.x + (4 * tq + r) * P + 16 * cb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(xr + 4 * k);
+      ar[r][4 * k] = a.x * a.x;
+      ar[r][4 * k + 1] = a.y * a.y;
+      ar[r][4 * k + 2] = a.z * a.z;
+      ar[r][4 * k + 3] = a.w * a.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 a = *reinterpret_cast<const float4*>(sm.x + (16 * tb + i) * P + 4 * cq);
+    ac[i][0] = a.x * a.x;
+    ac[i][1] = a.y * a.y;
+    ac[i][2] = a.z * a.z;
+    ac[i][3] = a.w * a.w;
   }
 
   for (int it = 0; it < iters; ++it) {
     // Token step: r_t^2 = mean_j A_tj u_j.
     {
-      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-      const float* ub = sm.u + 64 * rb;
+      float uv[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float4 q = *reinterpret_cast<const float4*>(ub + 4 * k);
-        p0 = fmaf(x[4 * k], q.x, p0);
-        p1 = fmaf(x[4 * k + 1], q.y, p1);
-        p2 = fmaf(x[4 * k + 2], q.z, p2);
-        p3 = fmaf(x[4 * k + 3], q.w, p3);
+      for (int k = 0; k < 4; ++k) {
+        const float4 q = *reinterpret_cast<const float4*>(sm.u + 16 * cb + 4 * k);
+        uv[4 * k] = q.x;
+        uv[4 * k + 1] = q.y;
+        uv[4 * k + 2] = q.z;
+        uv[4 * k + 3] = q.w;
       }
-      sm.part[rb][t] = (p0 + p1) + (p2 + p3);
-    }
-    __syncthreads();
-    if (rb == 0) {
-      float tot = sm.part[0][t];
+      float tot[4];
 #pragma unroll
-      for (int o = 1; o < NB; ++o) tot += sm.part[o][t];
-      sm.v[t] = tot > 0.f ? (float)D / tot : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; c += 2) {
+          p0 = fmaf(ar[r][c], uv[c], p0);
+          p1 = fmaf(ar[r][c + 1], uv[c + 1], p1);
+        }
+        tot[r] = sum_rl<RL>(p0 + p1);
+      }
+      if (cb == 0) {
+        float4 vv;
+        vv.x = tot[0] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[0]) : 0.f;
+        vv.y = tot[1] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[1]) : 0.f;
+        vv.z = tot[2] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[2]) : 0.f;
+        vv.w = tot[3] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[3]) : 0.f;
+        *reinterpret_cast<float4*>(sm.v + 4 * tq) = vv;
+      }
     }
     __syncthreads();
     // Channel step: c_j^2 = mean_t A_tj v_t.
     {
-      float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
-      const float* vb = sm.v + 64 * ca;
+      float vt[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float4 q = *reinterpret_cast<const float4*>(vb + 4 * k);
-        q0 = fmaf(acol[4 * k], q.x, q0);
-        q1 = fmaf(acol[4 * k + 1], q.y, q1);
-        q2 = fmaf(acol[4 * k + 2], q.z, q2);
-        q3 = fmaf(acol[4 * k + 3], q.w, q3);
+      for (int k = 0; k < 4; ++k) {
+        const float4 q = *reinterpret_cast<const float4*>(sm.v + 16 * tb + 4 * k);
+        vt[4 * k] = q.x;
+        vt[4 * k + 1] = q.y;
+        vt[4 * k + 2] = q.z;
+        vt[4 * k + 3] = q.w;
       }
-      sm.qcol[ca][j] = (q0 + q1) + (q2 + q3);
-    }
-    __syncthreads();
-    if (ca == 0) {
-      const float tot = sm.qcol[0][j] + sm.qcol[1][j];
-      if (tot > 0.f) {
-        sm.c2[j] = tot * (1.0f / kGroup);
-        sm.u[j] = (float)kGroup / tot;
-      } else {
-        sm.u[j] = 0.f;
+      float tot[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          q0 = fmaf(ac[i][c], vt[i], q0);
+          q1 = fmaf(ac[i + 1][c], vt[i + 1], q1);
+        }
+        tot[c] = sum8(q0 + q1);
+      }
+      if (tb == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (tot[c] > 0.f) {
+            sm.c2[4 * cq + c] = tot[c] * (1.0f / kGroup);
+            sm.u[4 * cq + c] = (float)kGroup * __builtin_amdgcn_rcpf(tot[c]);
+          } else {
+            sm.u[4 * cq + c] = 0.f;
+          }
+        }
       }
     }
     __syncthreads();
   }
 
-  // Channel scales.
-  if (ca == 0) {
-    const float c = sqrtf(sm.c2[j]);
-    sm.cinv[j] = 1.0f / c;
-    reinterpret_cast<uint16_t*>(rec + CODE_BYTES + 2 * kGroup)[j] = f2h_rne(c);
-    if (dbg) dbg[kGroup + j] = c;
+  // ---- channel scales ----------------------------------------------------
+  if (tid < D) {
+    const float c = sqrtf(sm.c2[tid]);
+    sm.cinv[tid] = 1.0f / c;
+    reinterpret_cast<uint16_t*>(rec + CODE_BYTES + 2 * kGroup)[tid] = f2h_rne(c);
+    if (dbg) dbg[kGroup + tid] = c;
   }
   __syncthreads();
-  // Token scales from the largest |X_r / c| of each token.
-  float z[64];
-  float mx = 0.f;
+
+  // ---- token scales from the largest |X_r / c| of each token (row role) ---
+  float zr[4][16];
+  float inv[4];
   {
-    const float* cb = sm.cinv + 64 * rb;
+    float ci[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(xrow + 4 * k);
-      const float4 ci = *reinterpret_cast<const float4*>(cb + 4 * k);
-      z[4 * k] = a.x * ci.x;
-      z[4 * k + 1] = a.y * ci.y;
-      z[4 * k + 2] = a.z * ci.z;
-      z[4 * k + 3] = a.w * ci.w;
+    for (int k = 0; k < 4; ++k) {
+      const float4 q = *reinterpret_cast<const float4*>(sm.cinv + 16 * cb + 4 * k);
+      ci[4 * k] = q.x;
+      ci[4 * k + 1] = q.y;
+      ci[4 * k + 2] = q.z;
+      ci[4 * k + 3] = q.w;
     }
 #pragma unroll
-    for (int i = 0; i < 64; ++i) mx = fmaxf(mx, fabsf(z[i]));
-  }
-  if constexpr (NB > 1) {
-    sm.part[rb][t] = mx;
-    __syncthreads();
+    for (int r = 0; r < 4; ++r) {
+      const float* xr = sm.x + (4 * tq + r) * P + 16 * cb;
+      float mx = 0.f;
 #pragma unroll
-    for (int o = 0; o < NB; ++o) mx = fmaxf(mx, sm.part[o][t]);
-  }
-  const float inv = mx > 0.f ? (float)LEVELS / (2.0f * mx) : 0.f;
-  if (rb == 0) {
-    const float s = mx * (2.0f / LEVELS);
-    reinterpret_cast<uint16_t*>(rec + CODE_BYTES)[t] = f2h_rne(s);
-    if (dbg) dbg[t] = s;
-    sm.inv[t] = inv;
+      for (int k = 0; k < 4; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(xr + 4 * k);
+        zr[r][4 * k] = a.x * ci[4 * k];
+        zr[r][4 * k + 1] = a.y * ci[4 * k + 1];
+        zr[r][4 * k + 2] = a.z * ci[4 * k + 2];
+        zr[r][4 * k + 3] = a.w * ci[4 * k + 3];
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) mx = fmaxf(mx, fabsf(zr[r][c]));
+      mx = max_rl<RL>(mx);
+      inv[r] = mx > 0.f ? (float)LEVELS / (2.0f * mx) : 0.f;
+      if (cb == 0) {
+        const int t = 4 * tq + r;
+        const float sc = mx * (2.0f / LEVELS);
+        reinterpret_cast<uint16_t*>(rec + CODE_BYTES)[t] = f2h_rne(sc);
+        if (dbg) dbg[t] = sc;
+        sm.inv[t] = inv[r];
+      }
+    }
   }
   if constexpr (TOKEN_MAJOR) {
-    // K record: token t's codes for channels [64 rb, 64 rb + 64).
-    constexpr int WORDS = 64 * BITS / 32;
+    // K record: tokens 4tq .. 4tq+3, channels [16 cb, 16 cb + 16): one
+    // (2-bit) or two (4-bit) little-endian words per token.
+    constexpr int WORDS = 16 * BITS / 32;
     constexpr int PER = 32 / BITS;
-    uint32_t out[WORDS];
 #pragma unroll
-    for (int k = 0; k < WORDS; ++k) {
-      uint32_t word = 0;
+    for (int r = 0; r < 4; ++r) {
+      uint32_t out[WORDS];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float c = fminf(fmaxf(rintf(fmaf(z[k * PER + e], inv, MID)), 0.f), (float)LEVELS);
-        word |= (uint32_t)c << (BITS * e);
+      for (int k = 0; k < WORDS; ++k) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const float c = fminf(fmaxf(rintf(fmaf(zr[r][k * PER + e], inv[r], MID)), 0.f), (float)LEVELS);
+          word |= (uint32_t)c << (BITS * e);
+        }
+        out[k] = word;
       }
-      out[k] = word;
+      uint8_t* dst = rec + (size_t)(4 * tq + r) * (D * BITS / 8) + cb * (16 * BITS / 8);
+      if constexpr (WORDS == 1)
+        *reinterpret_cast<uint32_t*>(dst) = out[0];
+      else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
     }
-    uint4* dst = reinterpret_cast<uint4*>(rec + (size_t)t * (D * BITS / 8) + rb * (64 * BITS / 8));
-#pragma unroll
-    for (int k = 0; k < WORDS / 4; ++k) dst[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
   } else {
-    // V record: channel j's codes for tokens [64 ca, 64 ca + 64).
+    // V record: channels 4cq .. 4cq+3, tokens [16 tb, 16 tb + 16).
     __syncthreads();
-    constexpr int WORDS = 64 * BITS / 32;
+    constexpr int WORDS = 16 * BITS / 32;
     constexpr int PER = 32 / BITS;
-    const float ci = sm.cinv[j];
-    uint32_t out[WORDS];
+    const float4 ci = *reinterpret_cast<const float4*>(sm.cinv + 4 * cq);
+    float zc[16][4], iv[16];
 #pragma unroll
-    for (int k = 0; k < WORDS; ++k) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int tok = 64 * ca + k * PER + e;
-        const float zz = sm.x[tok * P + j] * ci;
-        const float c = fminf(fmaxf(rintf(fmaf(zz, sm.inv[tok], MID)), 0.f), (float)LEVELS);
-        word |= (uint32_t)c << (BITS * e);
-      }
-      out[k] = word;
+    for (int i = 0; i < 16; ++i) {
+      const float4 a = *reinterpret_cast<const float4*>(sm.x + (16 * tb + i) * P + 4 * cq);
+      zc[i][0] = a.x * ci.x;
+      zc[i][1] = a.y * ci.y;
+      zc[i][2] = a.z * ci.z;
+      zc[i][3] = a.w * ci.w;
     }
-    uint4* dst = reinterpret_cast<uint4*>(rec + (size_t)j * (kGroup * BITS / 8) + ca * (64 * BITS / 8));
 #pragma unroll
-    for (int k = 0; k < WORDS / 4; ++k) dst[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
+    for (int k = 0; k < 4; ++k) {
+      const float4 q = *reinterpret_cast<const float4*>(sm.inv + 16 * tb + 4 * k);
+      iv[4 * k] = q.x;
+      iv[4 * k + 1] = q.y;
+      iv[4 * k + 2] = q.z;
+      iv[4 * k + 3] = q.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t out[WORDS];
+#pragma unroll
+      for (int k = 0; k < WORDS; ++k) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int i = k * PER + e;
+          const float code = fminf(fmaxf(rintf(fmaf(zc[i][c], iv[i], MID)), 0.f), (float)LEVELS);
+          word |= (uint32_t)code << (BITS * e);
+        }
+        out[k] = word;
+      }
+      uint8_t* dst = rec + (size_t)(4 * cq + c) * (kGroup * BITS / 8) + tb * (16 * BITS / 8);
+      if constexpr (WORDS == 1)
+        *reinterpret_cast<uint32_t*>(dst) = out[0];
+      else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+    }
   }
 }
 
