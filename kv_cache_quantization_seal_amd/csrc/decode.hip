@@ -669,13 +669,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 }
 
 // One workgroup (256 threads) per (query head, request): log-sum-exp merge of
-// all splits, one inverse Hadamard of the record part, normalization.  Every
-// wave finds the global maximum M and the normalizer L itself; wave w sums
-// the weighted partial outputs of splits w, w+4, ... with lane l holding
-// channels P*l .. P*l+P-1; one barrier joins the four sums.
+// all splits, one inverse Hadamard of the record part, normalization.  The
+// partial outputs do not depend on the weights, so every load is issued at
+// once: lane l of every wave loads (max, sum) of splits l, l+64, ..., and wave
+// w the partial outputs of splits w, w+4, ... for channels P*l .. P*l+P-1.
+// Each wave then finds the maximum M and normalizer L itself, takes the
+// weight of split s from lane s % 64, and one barrier joins the four sums.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int P = D / 64;
+  constexpr int OPW = 20;  // partial outputs per wave in the first batch (80 splits)
   __shared__ float orec[kWaves][D];
   __shared__ float oex[kWaves][D];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -683,47 +686,72 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int ns = a.nsplit, nrec = a.n_rec_splits;
   const int64_t base = ((int64_t)b * a.hq + hq) * ns;
   const float* ml = a.ws_ml + 2 * base;
-
-  float mloc = -INFINITY;
-  for (int s = l; s < ns; s += kWave) mloc = fmaxf(mloc, ml[2 * s]);
-  const float M = wave_max_f(mloc);
-  float lloc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = l; s < ns; s += kWave) {
-      const float m = ml[2 * s];
-      lloc += m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * s + 1];
+  const float* ob = a.ws_o + base * D + P * l;
+  auto load_o = [&](int s, float (&v)[P]) {
+    const float* o = ob + (int64_t)s * D;
+    if constexpr (P == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(o);
+      v[0] = x.x;
+      v[1] = x.y;
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(o);
+      v[0] = x.x;
+      v[1] = x.y;
+      v[2] = x.z;
+      v[3] = x.w;
     }
-  }
-  const float L = wave_sum_f(lloc);
+  };
+
+  // First batch of this wave's partial outputs: splits w, w+4, ... (clamped
+  // to the last split; the extra loads are discarded).
+  float ov[OPW][P];
+#pragma unroll
+  for (int u = 0; u < OPW; ++u) load_o(min(w + kWaves * u, ns - 1), ov[u]);
+  // (max, sum) of splits l and l + 64 in lane l (then further passes).
+  float m0 = l < ns ? ml[2 * l] : -INFINITY, l0 = l < ns ? ml[2 * l + 1] : 0.f;
+  float m1 = l + kWave < ns ? ml[2 * (l + kWave)] : -INFINITY;
+  float l1 = l + kWave < ns ? ml[2 * (l + kWave) + 1] : 0.f;
+  float mloc = fmaxf(m0, m1);
+  for (int s = l + 2 * kWave; s < ns; s += kWave) mloc = fmaxf(mloc, ml[2 * s]);
+  const float M = wave_max_f(mloc);
 
   float ar[P], ae[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) ar[i] = ae[i] = 0.f;
+  float L = 0.f;
   if (M != -INFINITY) {
-#pragma unroll 8
-    for (int s = w; s < ns; s += kWaves) {
+    const float f0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+    const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    float lloc = fmaf(f0, l0, f1 * l1);
+    for (int s = l + 2 * kWave; s < ns; s += kWave) {
       const float m = ml[2 * s];
-      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      const float* o = a.ws_o + (base + s) * D + P * l;
-      float ov[P];
-      if constexpr (P == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(o);
-        ov[0] = x.x;
-        ov[1] = x.y;
-      } else {
-        const float4 x = *reinterpret_cast<const float4*>(o);
-        ov[0] = x.x;
-        ov[1] = x.y;
-        ov[2] = x.z;
-        ov[3] = x.w;
-      }
+      lloc += m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * s + 1];
+    }
+    L = wave_sum_f(lloc);
+    auto add = [&](int s, float f, const float (&v)[P]) {
       if (s < nrec) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) ar[i] = fmaf(f, ov[i], ar[i]);
+        for (int i = 0; i < P; ++i) ar[i] = fmaf(f, v[i], ar[i]);
       } else {
 #pragma unroll
-        for (int i = 0; i < P; ++i) ae[i] = fmaf(f, ov[i], ae[i]);
+        for (int i = 0; i < P; ++i) ae[i] = fmaf(f, v[i], ae[i]);
       }
+    };
+#pragma unroll
+    for (int u = 0; u < OPW; ++u) {
+      const int s = w + kWaves * u;
+      if (s < ns) {
+        // the weight of split s < 128 sits in lane s % 64 (f0 or f1)
+        const float f = lane_f(s < kWave ? f0 : f1, s & (kWave - 1));
+        add(s, f, ov[u]);
+      }
+    }
+    // Splits past the first batch (long contexts): weight from its own max.
+    for (int s = w + kWaves * OPW; s < ns; s += kWaves) {
+      const float m = ml[2 * s];
+      float v[P];
+      load_o(s, v);
+      add(s, m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M), v);
     }
   }
 #pragma unroll
