@@ -55,7 +55,12 @@ def test_full_size_sampled(name):
         cache.seal_group()
     lens = [n + steps for n in lens0]
     q = np.stack([synth.queries(wl, b, 1)[0] for b in range(B)])
-    out = cache.decode_attn(torch.from_numpy(q).to(dev)).cpu().numpy()
+    qd = torch.from_numpy(q).to(dev)
+    out = cache.decode_attn(qd).cpu().numpy()
+    # Decoding is a pure function of the cache: a second call gives the same
+    # bits (no state is carried from one launch to the next).
+    again = cache.decode_attn(qd).cpu().numpy()
+    assert np.array_equal(out, again)
     assert list(cache.seq_len.cpu().numpy()) == lens
 
     worst = 0.0
