@@ -180,13 +180,34 @@ __device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d)
 }
 
 
+// Workgroup barrier that orders LDS accesses only: global loads and stores
+// issued before it stay in flight (a full __syncthreads also makes this
+// wave's global stores visible, which on this target waits for every
+// outstanding global access, loads included).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Position of 16-byte group g (channels 4g .. 4g+3) within row t of an fp32
+// [128][P] LDS tile, P = 4 (mod 32) dwords.  LDS serves a 128-bit access
+// eight lanes at a time from 32 four-byte banks, so eight lanes are
+// conflict-free when their groups land on eight different bank quads.  With
+// the low three bits of g XORed by ((g >> 3) ^ (t >> 4)) & 7 that holds for
+// eight lanes reading 4-channel group k of sixteen-channel blocks 0..7 of one
+// row, for eight lanes reading one group of rows t, t+16, ..., t+112, and for
+// eight lanes of consecutive rows (the row pitch moves them one quad each).
+__device__ __forceinline__ int xgrp(int g, int t) { return g ^ (((g >> 3) ^ (t >> 4)) & 7); }
+
 // Natural-order Sylvester Hadamard transform (unnormalized) of token rows held
 // as 64-channel slices: thread (t, rb) holds channels [64 rb, 64 rb + 64) of
 // token t in x.  The butterflies over the six low channel-index bits run in
 // registers; for D > 64 the block-index bits are combined through LDS
-// (xs = [128][P] fp32 scratch, which this overwrites).  Contains barriers: all
-// threads of the block must call it.
-template <int D, int P>
+// (xs = [128][P] fp32 scratch, which this overwrites; with SWZ its 16-byte
+// groups sit at xgrp positions).  Contains barriers: all threads of the block
+// must call it.
+template <int D, int P, bool SWZ = false>
 __device__ __forceinline__ void rotate_row_slice(float (&x)[64], float* xs, int t, int rb) {
   constexpr int NB = D / 64;
 #pragma unroll
@@ -201,10 +222,10 @@ __device__ __forceinline__ void rotate_row_slice(float (&x)[64], float* xs, int 
     }
   }
   if constexpr (NB > 1) {
-    float* xrow = xs + t * P + 64 * rb;
+    auto grp = [&](int g) { return xs + t * P + 4 * (SWZ ? xgrp(g, t) : g); };
 #pragma unroll
     for (int k = 0; k < 16; ++k)
-      *reinterpret_cast<float4*>(xrow + 4 * k) = make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
+      *reinterpret_cast<float4*>(grp(16 * rb + k)) = make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
     __syncthreads();
     // y_{64 rb + i} = sum_o (-1)^popcount(rb & o) x_{64 o + i}
     const float own = (__popc(rb) & 1) ? -1.0f : 1.0f;
@@ -214,10 +235,9 @@ __device__ __forceinline__ void rotate_row_slice(float (&x)[64], float* xs, int 
     for (int o = 0; o < NB; ++o) {
       if (o == rb) continue;
       const float sg = (__popc(rb & o) & 1) ? -1.0f : 1.0f;
-      const float* other = xs + t * P + 64 * o;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float4 q = *reinterpret_cast<const float4*>(other + 4 * k);
+        const float4 q = *reinterpret_cast<const float4*>(grp(16 * o + k));
         x[4 * k] = fmaf(sg, q.x, x[4 * k]);
         x[4 * k + 1] = fmaf(sg, q.y, x[4 * k + 1]);
         x[4 * k + 2] = fmaf(sg, q.z, x[4 * k + 2]);

@@ -24,6 +24,9 @@ struct SealPrefillArgs {
   int max_groups;
   int b0;
   int iters;
+  int gmax;     // groups per (request, head) in this launch (set by the launcher)
+  int nbh;      // requests * KV heads in this launch (set by the launcher)
+  int n_tiles;  // 2 * nbh * gmax (set by the launcher)
   PrefillLens lens;
 };
 

@@ -196,6 +196,10 @@ kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, co
     hipError_t e = kvarn::launch_prefill_copy(cfg->head_dim, c, k, v, src_tokens, lens, b0, nb, st);
     if (e != hipSuccess) return hip_status(e, "kvarn_prefill copy launch");
     if (max_g > 0) {
+      // The seal launch walks 2 * nb * Hkv * max_g tiles with int indices.
+      if ((int64_t)2 * nb * c.hkv * max_g >= ((int64_t)1 << 30))
+        return fail(KVARN_ERANGE, "prefill of %d requests x %d KV heads x %d groups is too large for one call", nb,
+                    c.hkv, max_g);
       kvarn::SealPrefillArgs a;
       a.k = (const __half*)k;
       a.v = (const __half*)v;

@@ -23,34 +23,55 @@
 // needs c and X_r: s_t = 2 max_j |X_r,tj / c_j| / (2^b - 1) and
 // code = rne(X_r,tj / c_j / s_t + mid).
 //
-// Data layout in the workgroup (2*D threads, D/32 waves), after the rotation:
-//   row role: lane l of wave w owns tokens 4*tq .. 4*tq+3 and channels
-//             16*cb .. 16*cb+15 (tq = RPW*w + l / RL, cb = l % RL, RL = D/16
-//             lanes per token quad) -> A_row[4][16] in VGPRs;
-//   col role: lane l of wave w owns channels 4*cq .. 4*cq+3 and tokens
-//             16*tb .. 16*tb+15 (cq = 8*w + l / 8, tb = l % 8)
-//             -> A_col[16][4] in VGPRs.
-//   LDS holds X_r (fp32, row pitch D+4) plus the factor vectors.  A half-step
-//   reads 16 factors from LDS (four 128-bit broadcasts) for 64 register FMAs;
-//   the partial sums of a token quad (channel quad) sit in RL (8) adjacent
-//   lanes and meet through DPP; the first lane publishes the four new
-//   factors.  One barrier per half-step.
+// Data layout in the workgroup (4*D threads, D/16 waves):
+//   rotation: thread (token tid / NB, 32-channel block tid % NB), NB = D/32,
+//             loads its 64 bytes of the fp16 tile; butterflies over the five
+//             low channel bits run in registers, over the block bits across
+//             neighbouring lanes (DPP); X_r goes to LDS (fp32, row pitch D+4,
+//             16-byte groups swizzled so that every 128-bit access pattern
+//             below is free of bank conflicts).
+//   row role: lane l of wave w owns tokens 2*tp, 2*tp+1 and channels
+//             16*cb .. 16*cb+15 (tp = RPW*w + l / RL, cb = l % RL, RL = D/16
+//             lanes per token pair) -> A_row[2][16] in VGPRs;
+//   col role: lane l of wave w owns channels 2*cp, 2*cp+1 and tokens
+//             16*tb .. 16*tb+15 (cp = 8*w + l / 8, tb = l % 8)
+//             -> A_col[16][2] in VGPRs.
+//   A half-step reads 16 factors from LDS (four 128-bit reads of a skewed
+//   vector) for 32 register FMAs; the partial sums of a token pair (channel
+//   pair) sit in RL (8) adjacent lanes and meet through DPP; the first lane
+//   publishes the two new factors.  One barrier per half-step.  About 110
+//   VGPRs per lane and 70 KB (D 128) of LDS give two workgroups, four waves
+//   per SIMD, on a CU.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace kvarn {
 
+// Threads per workgroup = kSealThreadsPerD * D (one 128 x D tile).
+constexpr int kSealThreadsPerD = 4;
+
+// Factor vectors are stored skewed, element j at sk(j) = j + 4 (j >> 4):
+// sixteen-element runs start 20 dwords apart, so the eight lanes that read
+// runs 0..7 with one 128-bit access each hit eight different bank quads.
+__device__ __forceinline__ constexpr int sk(int j) { return j + 4 * (j >> 4); }
+
 template <int D>
 struct alignas(16) SealSmem {
   static constexpr int kPitch = D + 4;
   static constexpr int kBlocks = D / 64;
-  float x[kGroup * kPitch];
-  float u[D];                 // 1 / c_j^2
-  float v[kGroup];            // 1 / r_t^2
-  float c2[D];                // c_j^2
-  float cinv[D];              // 1 / c_j
-  float inv[kGroup];          // per-token inverse step (2^b - 1) / (2 M_t)
+  float x[kGroup * kPitch];    // X_r, 16-byte groups at xgrp positions
+  float u[D + D / 4];          // 1 / c_j^2 (skewed)
+  float v[kGroup + kGroup / 4];  // 1 / r_t^2 (skewed)
+  float c2[D];                 // c_j^2
+  float cinv[D + D / 4];       // 1 / c_j (skewed)
+  float inv[kGroup + kGroup / 4];  // per-token inverse step (2^b - 1) / (2 M_t) (skewed)
 };
+
+// Address of 16-byte group g of row t of the X_r tile.
+template <int D>
+__device__ __forceinline__ float* xg(SealSmem<D>& sm, int t, int g) {
+  return sm.x + t * SealSmem<D>::kPitch + 4 * xgrp(g, t);
+}
 
 // Sum / maximum over the 8 lanes 8k .. 8k+7 (every lane receives it).
 __device__ __forceinline__ float sum8(float v) {
@@ -74,59 +95,120 @@ __device__ __forceinline__ float max_rl(float v) {
   return RL == 8 ? max8(v) : row16_max(v);
 }
 
-template <int D, int BITS, bool TOKEN_MAJOR>
-__device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_t* __restrict__ rec,
-                                          float* __restrict__ dbg, int iters, SealSmem<D>& sm) {
-  constexpr int NB = D / 64;
-  constexpr int P = SealSmem<D>::kPitch;
-  constexpr int LEVELS = (1 << BITS) - 1;
-  constexpr float MID = 0.5f * LEVELS;
-  constexpr int CODE_BYTES = kGroup * D * BITS / 8;
-  constexpr int RL = D / 16;          // row role: lanes per token quad
-  constexpr int RPW = 64 / RL;        // row role: token quads per wave
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+// The 128 x D fp16 tile as thread (token tid / NB, 32-channel block tid % NB)
+// holds it, NB = D / 32: 64 bytes in four 16-byte pieces.
+template <int D>
+__device__ __forceinline__ void load_tile(uint4 (&raw)[4], const __half* __restrict__ src, int tid) {
+  constexpr int NB = D / 32;
+  const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)(tid / NB) * D + 32 * (tid % NB));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) raw[k] = p[k];
+}
 
-  // ---- rotation: thread (token tl, 64-channel block bl) ------------------
-  {
-    const int bl = w % NB;
-    const int tl = 64 * (w / NB) + lane;
-    float x[64];
-    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)tl * D + 64 * bl);
+// One Hadamard stage across the lanes whose block indices differ in bit M of
+// a 4-lane quad (M = 1, 2) or of an 8-lane group (M = 4): the lane with the
+// bit clear keeps x + x', the other x - x' negated, i.e. x' - ... computed as
+// x + s x' with s = -1; the negations are undone by the caller.
+template <int M>
+__device__ __forceinline__ void block_stage(float (&x)[32], bool upper) {
+  const float s = upper ? -1.0f : 1.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint4 q = p[k];
-      const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+  for (int i = 0; i < 32; ++i) {
+    const int v = __float_as_int(x[i]);
+    int o;
+    if constexpr (M == 1) {
+      o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+      o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    } else {
+      // Lanes 0-3 of each eight read lanes 4-7 (row_shl:4, banks 0 and 2),
+      // lanes 4-7 read lanes 0-3 (row_shr:4, banks 1 and 3).
+      o = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);
+      o = __builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false);
+    }
+    x[i] = fmaf(s, __int_as_float(o), x[i]);
+  }
+}
+
+// Rotation X_r = X H_D / sqrt(D) of the tile in `raw` into the LDS tile, then
+// the factor vectors reset.  Butterflies over the five low channel-index bits
+// run in registers, those over the block bits across neighbouring lanes.  A
+// lane whose block index has an odd number of set bits ends with its values
+// negated by those lane stages (each stage negates the lanes with its bit
+// set, and the negations commute with the later stages), which the final
+// scale undoes.  Ends with a barrier.
+template <int D>
+__device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& sm, int tid) {
+  constexpr int NB = D / 32;
+  const int tl = tid / NB, bl = tid % NB;
+  float x[32];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * k + 2 * e] = h2f((uint16_t)(ws[e] & 0xFFFFu));
-        x[8 * k + 2 * e + 1] = h2f((uint16_t)(ws[e] >> 16));
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t ws[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * k + 2 * e] = h2f((uint16_t)(ws[e] & 0xFFFFu));
+      x[8 * k + 2 * e + 1] = h2f((uint16_t)(ws[e] >> 16));
+    }
+  }
+#pragma unroll
+  for (int st = 1; st < 32; st <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & st)) {
+        const float a0 = x[i], a1 = x[i + st];
+        x[i] = a0 + a1;
+        x[i + st] = a0 - a1;
       }
     }
-    rotate_row_slice<D, P>(x, sm.x, tl, bl);
-    const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;  // 1/sqrt(D)
-    float* xrow = sm.x + tl * P + 64 * bl;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      *reinterpret_cast<float4*>(xrow + 4 * k) =
-          make_float4(x[4 * k] * rs, x[4 * k + 1] * rs, x[4 * k + 2] * rs, x[4 * k + 3] * rs);
   }
+  block_stage<1>(x, bl & 1);
+  block_stage<2>(x, bl & 2);
+  if constexpr (NB == 8) block_stage<4>(x, bl & 4);
+  const float rs = ((D == 128) ? 0.08838834764831845f : 0.0625f) * ((__popc(bl) & 1) ? -1.0f : 1.0f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    *reinterpret_cast<float4*>(xg(sm, tl, 8 * bl + k)) =
+        make_float4(x[4 * k] * rs, x[4 * k + 1] * rs, x[4 * k + 2] * rs, x[4 * k + 3] * rs);
   if (tid < D) {
-    sm.u[tid] = 1.0f;
+    sm.u[sk(tid)] = 1.0f;
     sm.c2[tid] = 1.0f;
   }
-  __syncthreads();
+  lds_barrier();
+}
 
-  // ---- A = X_r^2 blocks --------------------------------------------------
-  const int tq = RPW * w + lane / RL, cb = lane % RL;  // row role
-  const int cq = 8 * w + (lane >> 3), tb = lane & 7;   // col role
-  float ar[4][16], ac[16][4];
+// Lane roles after the rotation.  Row role: tokens 2tp, 2tp+1 and channels
+// 16cb .. 16cb+15, the RL = D/16 lanes of a token pair adjacent.  Column
+// role: channels 2cp, 2cp+1 and tokens 16tb .. 16tb+15, the eight lanes of a
+// channel pair adjacent.
+template <int D>
+struct SealRoles {
+  static constexpr int RL = D / 16;
+  static constexpr int RPW = 64 / RL;
+  int tp, cb, cp, tb;
+  __device__ explicit SealRoles(int tid) {
+    const int w = tid >> 6, lane = tid & 63;
+    tp = RPW * w + lane / RL;
+    cb = lane % RL;
+    cp = 8 * w + (lane >> 3);
+    tb = lane & 7;
+  }
+};
+
+// Sinkhorn iterations on the tile that seal_rotate left in LDS: A = X_r^2 in
+// both roles' register blocks, then `iters` token and channel steps.  Leaves
+// c_j^2 in sm.c2; ends with a barrier.
+template <int D>
+__device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid) {
+  constexpr int RL = SealRoles<D>::RL;
+  const SealRoles<D> ro(tid);
+  const int tp = ro.tp, cb = ro.cb, cp = ro.cp, tb = ro.tb;
+  float ar[2][16], ac[16][2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float* xr = sm.x + (4 * tq + r) * P + 16 * cb;
+  for (int r = 0; r < 2; ++r) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(xr + 4 * k);
+      const float4 a = *reinterpret_cast<const float4*>(xg(sm, 2 * tp + r, 4 * cb + k));
       ar[r][4 * k] = a.x * a.x;
       ar[r][4 * k + 1] = a.y * a.y;
       ar[r][4 * k + 2] = a.z * a.z;
@@ -135,11 +217,9 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float4 a = *reinterpret_cast<const float4*>(sm.x + (16 * tb + i) * P + 4 * cq);
+    const float2 a = *reinterpret_cast<const float2*>(xg(sm, 16 * tb + i, cp >> 1) + 2 * (cp & 1));
     ac[i][0] = a.x * a.x;
     ac[i][1] = a.y * a.y;
-    ac[i][2] = a.z * a.z;
-    ac[i][3] = a.w * a.w;
   }
 
   for (int it = 0; it < iters; ++it) {
@@ -148,15 +228,15 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
       float uv[16];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float4 q = *reinterpret_cast<const float4*>(sm.u + 16 * cb + 4 * k);
+        const float4 q = *reinterpret_cast<const float4*>(sm.u + 20 * cb + 4 * k);
         uv[4 * k] = q.x;
         uv[4 * k + 1] = q.y;
         uv[4 * k + 2] = q.z;
         uv[4 * k + 3] = q.w;
       }
-      float tot[4];
+      float tot[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 2; ++r) {
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int c = 0; c < 16; c += 2) {
@@ -166,29 +246,27 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
         tot[r] = sum_rl<RL>(p0 + p1);
       }
       if (cb == 0) {
-        float4 vv;
+        float2 vv;
         vv.x = tot[0] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[0]) : 0.f;
         vv.y = tot[1] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[1]) : 0.f;
-        vv.z = tot[2] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[2]) : 0.f;
-        vv.w = tot[3] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[3]) : 0.f;
-        *reinterpret_cast<float4*>(sm.v + 4 * tq) = vv;
+        *reinterpret_cast<float2*>(sm.v + sk(2 * tp)) = vv;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // Channel step: c_j^2 = mean_t A_tj v_t.
     {
       float vt[16];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float4 q = *reinterpret_cast<const float4*>(sm.v + 16 * tb + 4 * k);
+        const float4 q = *reinterpret_cast<const float4*>(sm.v + 20 * tb + 4 * k);
         vt[4 * k] = q.x;
         vt[4 * k + 1] = q.y;
         vt[4 * k + 2] = q.z;
         vt[4 * k + 3] = q.w;
       }
-      float tot[4];
+      float tot[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 2; ++c) {
         float q0 = 0.f, q1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -199,48 +277,65 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
       }
       if (tb == 0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
           if (tot[c] > 0.f) {
-            sm.c2[4 * cq + c] = tot[c] * (1.0f / kGroup);
-            sm.u[4 * cq + c] = (float)kGroup * __builtin_amdgcn_rcpf(tot[c]);
+            sm.c2[2 * cp + c] = tot[c] * (1.0f / kGroup);
+            sm.u[sk(2 * cp + c)] = (float)kGroup * __builtin_amdgcn_rcpf(tot[c]);
           } else {
-            sm.u[4 * cq + c] = 0.f;
+            sm.u[sk(2 * cp + c)] = 0.f;
           }
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
+}
+
+// Channel and token scales, round to nearest and packing of the tile that
+// seal_iterate left (X_r in LDS, c_j^2 in sm.c2) into record `rec`.  Every
+// global store comes last, after all of the phase's arithmetic: a store's
+// source registers may not be reused before it completes, and waiting for a
+// store also waits for every global load issued before it (one in-order
+// counter), which would expose the next tile's prefetch.
+template <int D, int BITS, bool TOKEN_MAJOR>
+__device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __restrict__ dbg, SealSmem<D>& sm,
+                                            int tid) {
+  constexpr int LEVELS = (1 << BITS) - 1;
+  constexpr float MID = 0.5f * LEVELS;
+  constexpr int CODE_BYTES = kGroup * D * BITS / 8;
+  constexpr int RL = SealRoles<D>::RL;
+  constexpr int WORDS = 16 * BITS / 32;  // code words per 16 codes
+  constexpr int PER = 32 / BITS;         // codes per word
+  const SealRoles<D> ro(tid);
+  const int tp = ro.tp, cb = ro.cb, cp = ro.cp, tb = ro.tb;
 
   // ---- channel scales ----------------------------------------------------
+  float cj = 0.f;
   if (tid < D) {
-    const float c = sqrtf(sm.c2[tid]);
-    sm.cinv[tid] = 1.0f / c;
-    reinterpret_cast<uint16_t*>(rec + CODE_BYTES + 2 * kGroup)[tid] = f2h_rne(c);
-    if (dbg) dbg[kGroup + tid] = c;
+    cj = sqrtf(sm.c2[tid]);
+    sm.cinv[sk(tid)] = 1.0f / cj;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- token scales from the largest |X_r / c| of each token (row role) ---
-  float zr[4][16];
-  float inv[4];
+  float zr[2][16];
+  float inv[2], sc[2];
   {
     float ci[16];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 q = *reinterpret_cast<const float4*>(sm.cinv + 16 * cb + 4 * k);
+      const float4 q = *reinterpret_cast<const float4*>(sm.cinv + 20 * cb + 4 * k);
       ci[4 * k] = q.x;
       ci[4 * k + 1] = q.y;
       ci[4 * k + 2] = q.z;
       ci[4 * k + 3] = q.w;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float* xr = sm.x + (4 * tq + r) * P + 16 * cb;
+    for (int r = 0; r < 2; ++r) {
       float mx = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(xr + 4 * k);
+        const float4 a = *reinterpret_cast<const float4*>(xg(sm, 2 * tp + r, 4 * cb + k));
         zr[r][4 * k] = a.x * ci[4 * k];
         zr[r][4 * k + 1] = a.y * ci[4 * k + 1];
         zr[r][4 * k + 2] = a.z * ci[4 * k + 2];
@@ -250,23 +345,18 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
       for (int c = 0; c < 16; ++c) mx = fmaxf(mx, fabsf(zr[r][c]));
       mx = max_rl<RL>(mx);
       inv[r] = mx > 0.f ? (float)LEVELS / (2.0f * mx) : 0.f;
-      if (cb == 0) {
-        const int t = 4 * tq + r;
-        const float sc = mx * (2.0f / LEVELS);
-        reinterpret_cast<uint16_t*>(rec + CODE_BYTES)[t] = f2h_rne(sc);
-        if (dbg) dbg[t] = sc;
-        sm.inv[t] = inv[r];
-      }
+      sc[r] = mx * (2.0f / LEVELS);
     }
+    if (cb == 0) *reinterpret_cast<float2*>(sm.inv + sk(2 * tp)) = make_float2(inv[0], inv[1]);
   }
+
+  // ---- codes -------------------------------------------------------------
+  // K record: tokens 2tp, 2tp+1, channels [16 cb, 16 cb + 16) (row role).
+  // V record: channels 2cp, 2cp+1, tokens [16 tb, 16 tb + 16) (column role).
+  uint32_t out[2][WORDS];
   if constexpr (TOKEN_MAJOR) {
-    // K record: tokens 4tq .. 4tq+3, channels [16 cb, 16 cb + 16): one
-    // (2-bit) or two (4-bit) little-endian words per token.
-    constexpr int WORDS = 16 * BITS / 32;
-    constexpr int PER = 32 / BITS;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t out[WORDS];
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
       for (int k = 0; k < WORDS; ++k) {
         uint32_t word = 0;
@@ -275,40 +365,29 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
           const float c = fminf(fmaxf(rintf(fmaf(zr[r][k * PER + e], inv[r], MID)), 0.f), (float)LEVELS);
           word |= (uint32_t)c << (BITS * e);
         }
-        out[k] = word;
+        out[r][k] = word;
       }
-      uint8_t* dst = rec + (size_t)(4 * tq + r) * (D * BITS / 8) + cb * (16 * BITS / 8);
-      if constexpr (WORDS == 1)
-        *reinterpret_cast<uint32_t*>(dst) = out[0];
-      else
-        *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
     }
   } else {
-    // V record: channels 4cq .. 4cq+3, tokens [16 tb, 16 tb + 16).
-    __syncthreads();
-    constexpr int WORDS = 16 * BITS / 32;
-    constexpr int PER = 32 / BITS;
-    const float4 ci = *reinterpret_cast<const float4*>(sm.cinv + 4 * cq);
-    float zc[16][4], iv[16];
+    lds_barrier();
+    const float2 ci = *reinterpret_cast<const float2*>(sm.cinv + sk(2 * cp));
+    float zc[16][2], iv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 a = *reinterpret_cast<const float4*>(sm.x + (16 * tb + i) * P + 4 * cq);
+      const float2 a = *reinterpret_cast<const float2*>(xg(sm, 16 * tb + i, cp >> 1) + 2 * (cp & 1));
       zc[i][0] = a.x * ci.x;
       zc[i][1] = a.y * ci.y;
-      zc[i][2] = a.z * ci.z;
-      zc[i][3] = a.w * ci.w;
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 q = *reinterpret_cast<const float4*>(sm.inv + 16 * tb + 4 * k);
+      const float4 q = *reinterpret_cast<const float4*>(sm.inv + 20 * tb + 4 * k);
       iv[4 * k] = q.x;
       iv[4 * k + 1] = q.y;
       iv[4 * k + 2] = q.z;
       iv[4 * k + 3] = q.w;
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t out[WORDS];
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int k = 0; k < WORDS; ++k) {
         uint32_t word = 0;
@@ -318,14 +397,29 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
           const float code = fminf(fmaxf(rintf(fmaf(zc[i][c], iv[i], MID)), 0.f), (float)LEVELS);
           word |= (uint32_t)code << (BITS * e);
         }
-        out[k] = word;
+        out[c][k] = word;
       }
-      uint8_t* dst = rec + (size_t)(4 * cq + c) * (kGroup * BITS / 8) + tb * (16 * BITS / 8);
-      if constexpr (WORDS == 1)
-        *reinterpret_cast<uint32_t*>(dst) = out[0];
-      else
-        *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
     }
+  }
+
+  // ---- stores ------------------------------------------------------------
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    uint8_t* dst = TOKEN_MAJOR ? rec + (size_t)(2 * tp + r) * (D * BITS / 8) + cb * (16 * BITS / 8)
+                               : rec + (size_t)(2 * cp + r) * (kGroup * BITS / 8) + tb * (16 * BITS / 8);
+    if constexpr (WORDS == 1)
+      *reinterpret_cast<uint32_t*>(dst) = out[r][0];
+    else
+      *reinterpret_cast<uint2*>(dst) = make_uint2(out[r][0], out[r][1]);
+  }
+  if (cb == 0) {
+    const uint32_t s2 = (uint32_t)f2h_rne(sc[0]) | ((uint32_t)f2h_rne(sc[1]) << 16);
+    *reinterpret_cast<uint32_t*>(rec + CODE_BYTES + 4 * tp) = s2;
+    if (dbg) *reinterpret_cast<float2*>(dbg + 2 * tp) = make_float2(sc[0], sc[1]);
+  }
+  if (tid < D) {
+    reinterpret_cast<uint16_t*>(rec + CODE_BYTES + 2 * kGroup)[tid] = f2h_rne(cj);
+    if (dbg) dbg[kGroup + tid] = cj;
   }
 }
 
@@ -333,33 +427,46 @@ __device__ __forceinline__ void seal_body(const __half* __restrict__ src, uint8_
 // Kernels
 // ---------------------------------------------------------------------------
 template <int D, int BITS, int KIND>
-__global__ __launch_bounds__(2 * D) void seal_tiles_kernel(const __half* __restrict__ src, uint8_t* __restrict__ dst,
+__global__ __launch_bounds__(kSealThreadsPerD * D) void seal_tiles_kernel(const __half* __restrict__ src, uint8_t* __restrict__ dst,
                                                           int64_t dst_stride, float* __restrict__ dbg, int iters) {
   __shared__ SealSmem<D> sm;
   const int64_t i = blockIdx.x;
-  seal_body<D, BITS, KIND == 0>(src + i * kGroup * D, dst + i * dst_stride, dbg ? dbg + i * (kGroup + D) : nullptr,
-                                iters, sm);
+  uint4 raw[4];
+  load_tile<D>(raw, src + i * kGroup * D, threadIdx.x);
+  seal_rotate<D>(raw, sm, threadIdx.x);
+  seal_iterate<D>(iters, sm, threadIdx.x);
+  seal_finish<D, BITS, KIND == 0>(dst + i * dst_stride, dbg ? dbg + i * (kGroup + D) : nullptr, sm, threadIdx.x);
 }
 
+// Bulk sealing: one workgroup per tile (group g, request-head bh, K|V), tile
+// index g + G (bh + NBH kind); groups a request does not have return at once.
+// One tile per workgroup lets the dispatcher refill a CU as soon as either of
+// its two workgroups finishes.  (A persistent grid that prefetched its next
+// tile during the iterations measured slower: the older workgroup of a CU
+// takes issue priority and finishes its share early, leaving the younger
+// one alone on the CU for the last tiles.)
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(2 * D) void seal_prefill_kernel(SealPrefillArgs a) {
+__global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(SealPrefillArgs a) {
   __shared__ SealSmem<D> sm;
-  const int g = blockIdx.x;
-  const int bl = blockIdx.y / a.hkv, h = blockIdx.y % a.hkv;
-  const int kind = blockIdx.z;
-  const int len = a.lens.len[bl];
-  if (kSink + kGroup * (g + 1) > len) return;
-  const int64_t bh = (int64_t)(a.b0 + bl) * a.hkv + h;
+  const int idx = blockIdx.x;
+  const int g = idx % a.gmax, r = idx / a.gmax;
+  const int bhl = r % a.nbh, kind = r / a.nbh;
+  if (kSink + kGroup * (g + 1) > a.lens.len[bhl / a.hkv]) return;
+  const int64_t bh = (int64_t)a.b0 * a.hkv + bhl;
   const __half* src = (kind ? a.v : a.k) + (bh * a.src_tokens + kSink + (int64_t)kGroup * g) * D;
   uint8_t* rec = a.records + (bh * a.max_groups + g) * a.group_bytes + (kind ? a.rec_k_bytes : 0);
+  uint4 raw[4];
+  load_tile<D>(raw, src, threadIdx.x);
+  seal_rotate<D>(raw, sm, threadIdx.x);
+  seal_iterate<D>(a.iters, sm, threadIdx.x);
   if (kind == 0)
-    seal_body<D, KB, true>(src, rec, nullptr, a.iters, sm);
+    seal_finish<D, KB, true>(rec, nullptr, sm, threadIdx.x);
   else
-    seal_body<D, VB, false>(src, rec, nullptr, a.iters, sm);
+    seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
 }
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(2 * D) void seal_stream_kernel(SealStreamArgs a) {
+__global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealStreamArgs a) {
   __shared__ SealSmem<D> sm;
   const int bh = blockIdx.x;
   const int kind = blockIdx.y;
@@ -370,10 +477,14 @@ __global__ __launch_bounds__(2 * D) void seal_stream_kernel(SealStreamArgs a) {
   if (g >= a.max_groups) return;
   const __half* src = (kind ? a.tail_v : a.tail_k) + (int64_t)bh * kGroup * D;
   uint8_t* rec = a.records + ((int64_t)bh * a.max_groups + g) * a.group_bytes + (kind ? a.rec_k_bytes : 0);
+  uint4 raw[4];
+  load_tile<D>(raw, src, threadIdx.x);
+  seal_rotate<D>(raw, sm, threadIdx.x);
+  seal_iterate<D>(a.iters, sm, threadIdx.x);
   if (kind == 0)
-    seal_body<D, KB, true>(src, rec, nullptr, a.iters, sm);
+    seal_finish<D, KB, true>(rec, nullptr, sm, threadIdx.x);
   else
-    seal_body<D, VB, false>(src, rec, nullptr, a.iters, sm);
+    seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,10 +494,10 @@ template <int D, int BITS>
 static hipError_t launch_tiles_db(int kind, const void* src, void* dst, int64_t stride, float* dbg, int n, int iters,
                                   hipStream_t st) {
   if (kind == 0)
-    hipLaunchKernelGGL((seal_tiles_kernel<D, BITS, 0>), dim3(n), dim3(2 * D), 0, st, (const __half*)src,
+    hipLaunchKernelGGL((seal_tiles_kernel<D, BITS, 0>), dim3(n), dim3(kSealThreadsPerD * D), 0, st, (const __half*)src,
                        (uint8_t*)dst, stride, dbg, iters);
   else
-    hipLaunchKernelGGL((seal_tiles_kernel<D, BITS, 1>), dim3(n), dim3(2 * D), 0, st, (const __half*)src,
+    hipLaunchKernelGGL((seal_tiles_kernel<D, BITS, 1>), dim3(n), dim3(kSealThreadsPerD * D), 0, st, (const __half*)src,
                        (uint8_t*)dst, stride, dbg, iters);
   return hipGetLastError();
 }
@@ -400,12 +511,12 @@ hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* d
 }
 
 template <int D, int KB, int VB>
-static void launch_prefill_t(const SealPrefillArgs& a, int gx, int gy, hipStream_t st) {
-  hipLaunchKernelGGL((seal_prefill_kernel<D, KB, VB>), dim3(gx, gy, 2), dim3(2 * D), 0, st, a);
+static void launch_prefill_t(const SealPrefillArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((seal_prefill_kernel<D, KB, VB>), dim3(a.n_tiles), dim3(kSealThreadsPerD * D), 0, st, a);
 }
 template <int D, int KB, int VB>
 static void launch_stream_t(const SealStreamArgs& a, int gx, hipStream_t st) {
-  hipLaunchKernelGGL((seal_stream_kernel<D, KB, VB>), dim3(gx, 2), dim3(2 * D), 0, st, a);
+  hipLaunchKernelGGL((seal_stream_kernel<D, KB, VB>), dim3(gx, 2), dim3(kSealThreadsPerD * D), 0, st, a);
 }
 
 #define KVARN_DISPATCH_DKV(D, KB, VB, CALL)                       \
@@ -423,10 +534,14 @@ static void launch_stream_t(const SealStreamArgs& a, int gx, hipStream_t st) {
     }                                                             \
   } while (0)
 
-hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& a, int max_groups_in_batch, int nbh,
+hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& args, int max_groups_in_batch, int nbh,
                                hipStream_t st) {
   if (max_groups_in_batch <= 0 || nbh <= 0) return hipSuccess;
-#define CALL(d, k, v) launch_prefill_t<d, k, v>(a, max_groups_in_batch, nbh, st)
+  SealPrefillArgs a = args;
+  a.gmax = max_groups_in_batch;
+  a.nbh = nbh;
+  a.n_tiles = 2 * nbh * max_groups_in_batch;
+#define CALL(d, k, v) launch_prefill_t<d, k, v>(a, st)
   KVARN_DISPATCH_DKV(D, kb, vb, CALL);
 #undef CALL
   return hipGetLastError();
