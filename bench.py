@@ -4,8 +4,9 @@
 Workload (default): the Llama-3.1-8B attention shape -- 32 query / 8 KV
 heads, head dim 128, batch 1, 32768 cached tokens (128-token fp16 sink + 255
 sealed 2-bit groups), 2-bit K and V.  One *step* is one pass of the whole hot
-path over one layer's cache: append the new token's K/V, seal the group if its
-128th token just arrived, then decode attention for the 32 query heads.
+path over one layer's cache: append the new token's K/V and seal the group if
+its 128th token just arrived (one launch, kvarn_append_seal), then decode
+attention for the 32 query heads (split kernel + combine kernel).
 
 Caches of `--copies` layers (distinct memory, 20 MB each) are visited in
 turn, as a model's layers would be, so every step reads its records from HBM
@@ -297,8 +298,7 @@ def main():
     def step(s):
         c = caches[s % ncopy]
         tok = s // ncopy
-        c.append(new_k[tok], new_v[tok])
-        c.seal_group()
+        c.append_seal(new_k[tok], new_v[tok])
         c.decode_attn(q_all[tok], out=outs[s % ncopy])
 
     if args.profile_steps > 0:

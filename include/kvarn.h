@@ -137,6 +137,22 @@ kvarn_status kvarn_append(const kvarn_config *cfg, const kvarn_cache *cache,
 kvarn_status kvarn_seal_group(const kvarn_config *cfg, const kvarn_cache *cache, void *stream);
 
 /*
+ * kvarn_append followed by kvarn_seal_group, in one launch (one workgroup
+ * per KV head and K|V instead of two launches per decode step) [P2 §2.1:
+ * append to the tail; seal a group when its last token arrives].  Same
+ * arguments and results as the two calls: the token goes to its slot, a
+ * tail it completes is sealed into its record, and seq_len[b] advances by
+ * one (not for a full cache).  While the launch runs, bits 23..30 of
+ * seq_len[b] count the request's workgroups that have read the length (the
+ * last one clears them), so nothing else may access seq_len until it
+ * completes (stream order guarantees this for work on the same stream).
+ * Requires num_kv_heads <= 127 (else KVARN_EUNSUPPORTED) and a capacity
+ * 128 + 128*max_groups + 127 below 2^23 tokens (else KVARN_ERANGE).
+ */
+kvarn_status kvarn_append_seal(const kvarn_config *cfg, const kvarn_cache *cache,
+                               const void *k_new, const void *v_new, void *stream);
+
+/*
  * Bulk ingest of a prompt: for each request b, tokens [0, len_host[b]) of
  * k, v (device fp16 [batch][Hkv][src_tokens][D]) fill the sink, every
  * complete group is sealed into its record, the rest goes to the tail, and

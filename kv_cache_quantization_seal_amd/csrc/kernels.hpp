@@ -42,6 +42,28 @@ struct SealStreamArgs {
   int iters;
 };
 
+// Append + seal in one launch.  While it runs, seq_len[b] carries a count of
+// the request's workgroups that have read it in bits kArriveShift..30.
+constexpr int kArriveShift = 23;
+constexpr uint32_t kLenMask = (1u << kArriveShift) - 1;
+
+struct AppendSealArgs {
+  __half* sink_k;
+  __half* sink_v;
+  __half* tail_k;
+  __half* tail_v;
+  const __half* k_new;
+  const __half* v_new;
+  uint8_t* records;
+  int32_t* seq_len;
+  int64_t group_bytes;
+  int rec_k_bytes;
+  int hkv;
+  int max_groups;
+  int cap;  // tokens a request can hold: 128 + 128 max_groups + 127
+  int iters;
+};
+
 struct CacheArgs {
   __half* sink_k;
   __half* sink_v;
@@ -92,6 +114,7 @@ hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* d
 hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& a, int max_groups_in_batch, int nbh,
                                hipStream_t st);
 hipError_t launch_seal_stream(int D, int kb, int vb, const SealStreamArgs& a, int nbh, hipStream_t st);
+hipError_t launch_append_seal(int D, int kb, int vb, const AppendSealArgs& a, int nbh, hipStream_t st);
 hipError_t launch_append(int D, const CacheArgs& c, const void* k, const void* v, hipStream_t st);
 hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const void* v, int64_t src_tokens,
                                const PrefillLens& lens, int b0, int nb, hipStream_t st);

@@ -142,6 +142,43 @@ kvarn_status kvarn_append(const kvarn_config* cfg, const kvarn_cache* cache, con
                     "kvarn_append launch");
 }
 
+kvarn_status kvarn_append_seal(const kvarn_config* cfg, const kvarn_cache* cache, const void* k_new,
+                               const void* v_new, void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (!k_new || !v_new) return fail(KVARN_EINVAL, "k_new and v_new must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVARN_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const int64_t cap = (int64_t)KVARN_SINK + (int64_t)KVARN_GROUP * cache->max_groups + KVARN_GROUP - 1;
+  if (cap > (int64_t)kvarn::kLenMask)
+    return fail(KVARN_ERANGE, "kvarn_append_seal needs a capacity below 2^%d tokens (max_groups %d is too large)",
+                kvarn::kArriveShift, cache->max_groups);
+  if (2 * cfg->num_kv_heads >= (1 << (31 - kvarn::kArriveShift)))
+    return fail(KVARN_EUNSUPPORTED, "kvarn_append_seal supports at most %d KV heads",
+                (1 << (31 - kvarn::kArriveShift)) / 2 - 1);
+  const int64_t nbh = (int64_t)cache->batch * cfg->num_kv_heads;
+  if (nbh > 0x7fffffff) return fail(KVARN_ERANGE, "batch * num_kv_heads too large");
+  const kvarn::CacheArgs c = cache_args(cfg, cache);
+  kvarn::AppendSealArgs a;
+  a.sink_k = c.sink_k;
+  a.sink_v = c.sink_v;
+  a.tail_k = c.tail_k;
+  a.tail_v = c.tail_v;
+  a.k_new = (const __half*)k_new;
+  a.v_new = (const __half*)v_new;
+  a.records = (uint8_t*)cache->records;
+  a.seq_len = cache->seq_len;
+  a.group_bytes = c.group_bytes;
+  a.rec_k_bytes = c.rec_k_bytes;
+  a.hkv = c.hkv;
+  a.max_groups = c.max_groups;
+  a.cap = (int)cap;
+  a.iters = cfg->sinkhorn_iters;
+  return hip_status(kvarn::launch_append_seal(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, (int)nbh,
+                                              (hipStream_t)stream),
+                    "kvarn_append_seal launch");
+}
+
 kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache, void* stream) {
   kvarn_status s = check_cfg(cfg);
   if (s != KVARN_OK) return s;

@@ -487,6 +487,54 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealS
     seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
 }
 
+// Append one token and seal the group it completes, in one launch: workgroup
+// (request-head bh, K|V) writes its row of the new token, and if that row
+// completes the tail it seals the tail into the group's record.  Every
+// workgroup needs the request's old length n, so the length can only advance
+// once all 2 Hkv workgroups of the request have read it: each adds
+// 1 << kArriveShift to seq_len[b] (a device-scope atomic that also returns
+// n in the low bits), and the one that finds the count complete removes the
+// count and adds the token.
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kSealThreadsPerD * D) void append_seal_kernel(AppendSealArgs a) {
+  __shared__ SealSmem<D> sm;
+  __shared__ int s_n;
+  const int bh = blockIdx.x, kind = blockIdx.y;
+  const int b = bh / a.hkv;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const uint32_t nwg = 2u * (uint32_t)a.hkv;
+    uint32_t* len = reinterpret_cast<uint32_t*>(a.seq_len + b);
+    const uint32_t old = atomicAdd(len, 1u << kArriveShift);
+    const int n = (int)(old & kLenMask);
+    if ((old >> kArriveShift) == nwg - 1) atomicAdd(len, (n < a.cap ? 1u : 0u) - (nwg << kArriveShift));
+    s_n = n;
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (n >= a.cap) return;
+  const int slot = n < kSink ? n : (n - kSink) % kGroup;
+  __half* row = (n < kSink ? (kind ? a.sink_v : a.sink_k) : (kind ? a.tail_v : a.tail_k)) +
+                ((int64_t)bh * kGroup + slot) * D;
+  if (tid < D / 8)
+    reinterpret_cast<uint4*>(row)[tid] = reinterpret_cast<const uint4*>((kind ? a.v_new : a.k_new) + (int64_t)bh * D)[tid];
+  const int n1 = n + 1;
+  if (n1 < kSink + kGroup || (n1 - kSink) % kGroup != 0) return;
+  const int g = (n1 - kSink) / kGroup - 1;
+  if (g >= a.max_groups) return;
+  __syncthreads();  // the row written above is part of the tile read below
+  const __half* tile = (kind ? a.tail_v : a.tail_k) + (int64_t)bh * kGroup * D;
+  uint8_t* rec = a.records + ((int64_t)bh * a.max_groups + g) * a.group_bytes + (kind ? a.rec_k_bytes : 0);
+  uint4 raw[4];
+  load_tile<D>(raw, tile, tid);
+  seal_rotate<D>(raw, sm, tid);
+  seal_iterate<D>(a.iters, sm, tid);
+  if (kind == 0)
+    seal_finish<D, KB, true>(rec, nullptr, sm, tid);
+  else
+    seal_finish<D, VB, false>(rec, nullptr, sm, tid);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -542,6 +590,19 @@ hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& arg
   a.nbh = nbh;
   a.n_tiles = 2 * nbh * max_groups_in_batch;
 #define CALL(d, k, v) launch_prefill_t<d, k, v>(a, st)
+  KVARN_DISPATCH_DKV(D, kb, vb, CALL);
+#undef CALL
+  return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+static void launch_append_seal_t(const AppendSealArgs& a, int gx, hipStream_t st) {
+  hipLaunchKernelGGL((append_seal_kernel<D, KB, VB>), dim3(gx, 2), dim3(kSealThreadsPerD * D), 0, st, a);
+}
+
+hipError_t launch_append_seal(int D, int kb, int vb, const AppendSealArgs& a, int nbh, hipStream_t st) {
+  if (nbh <= 0) return hipSuccess;
+#define CALL(d, k, v) launch_append_seal_t<d, k, v>(a, nbh, st)
   KVARN_DISPATCH_DKV(D, kb, vb, CALL);
 #undef CALL
   return hipGetLastError();

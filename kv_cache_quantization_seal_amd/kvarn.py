@@ -21,7 +21,8 @@ SINK = 128
 SINKHORN_ITERS = 16
 EXPORTS = (
     "kvarn_check_config", "kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
-    "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_seal_group", "kvarn_prefill",
+    "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
+    "kvarn_prefill",
     "kvarn_decode_attn", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
     "kvarn_dequant_records",
 )
@@ -66,6 +67,7 @@ def lib():
         L.kvarn_status_string.argtypes = [ctypes.c_int]
         L.kvarn_status_string.restype = ctypes.c_char_p
         L.kvarn_append.argtypes = [cp(Config), cp(CacheView), vp, vp, vp]
+        L.kvarn_append_seal.argtypes = [cp(Config), cp(CacheView), vp, vp, vp]
         L.kvarn_seal_group.argtypes = [cp(Config), cp(CacheView), vp]
         L.kvarn_prefill.argtypes = [cp(Config), cp(CacheView), vp, vp, i64, cp(i32), vp]
         L.kvarn_decode_attn.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp, sz, vp]
@@ -163,6 +165,11 @@ class KVarNCache:
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
         _check(lib().kvarn_append(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k_new), _ptr(v_new),
                                   _stream(stream)))
+
+    def append_seal(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        """append() then seal_group(), in one launch."""
+        _check(lib().kvarn_append_seal(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k_new), _ptr(v_new),
+                                       _stream(stream)))
 
     def seal_group(self, stream=None) -> None:
         _check(lib().kvarn_seal_group(ctypes.byref(self.cfg), ctypes.byref(self.view), _stream(stream)))

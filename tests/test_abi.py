@@ -116,3 +116,17 @@ def test_tile_entry_points_validate():
 def test_status_strings():
     L = K.lib()
     assert L.kvarn_status_string(K.EWORKSPACE) == b"KVARN_EWORKSPACE"
+
+
+def test_append_seal_validates_before_launch():
+    L = K.lib()
+    cfg = K.make_config(128, 32, 8, 2, 2)
+    r = ctypes.byref
+    assert L.kvarn_append_seal(None, r(_view()), FAKE, FAKE, None) == K.EINVAL
+    assert L.kvarn_append_seal(r(cfg), None, FAKE, FAKE, None) == K.EINVAL
+    assert L.kvarn_append_seal(r(cfg), r(_view()), FAKE, None, None) == K.EINVAL
+    assert L.kvarn_append_seal(r(cfg), r(_view()), FAKE + 8, FAKE, None) == K.EINVAL
+    assert L.kvarn_append_seal(r(cfg), r(_view(tail_v=None)), FAKE, FAKE, None) == K.EINVAL
+    # The per-request arrival count shares seq_len with lengths below 2^23.
+    assert L.kvarn_append_seal(r(cfg), r(_view(max_groups=(1 << 23) // 128)), FAKE, FAKE, None) == K.ERANGE
+    assert "2^23" in L.kvarn_last_error().decode()

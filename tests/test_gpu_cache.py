@@ -65,7 +65,8 @@ def test_prefill_ragged(d, kb, vb):
     _check_cache(cache, k, v, lens, kb, vb, d)
 
 
-def test_append_seal_stream_and_decode():
+@pytest.mark.parametrize("fused", [False, True])
+def test_append_seal_stream_and_decode(fused):
     d, hq, hkv, kb, vb = 128, 4, 2, 2, 2
     wl = synth.Workload("s", 80, 2, hq, hkv, d, 200, 50, kb, vb, 260)
     k, v = _streams(wl, 600)
@@ -83,8 +84,11 @@ def test_append_seal_stream_and_decode():
         pos = [lens0[b] + step for b in range(2)]
         knew = torch.stack([kd[b, :, pos[b]] for b in range(2)]).contiguous()
         vnew = torch.stack([vd[b, :, pos[b]] for b in range(2)]).contiguous()
-        cache.append(knew, vnew)
-        cache.seal_group()
+        if fused:
+            cache.append_seal(knew, vnew)
+        else:
+            cache.append(knew, vnew)
+            cache.seal_group()
         for b in range(2):
             for h in range(hkv):
                 states[b][h].append(k[b, h, pos[b]], v[b, h, pos[b]])
@@ -101,17 +105,49 @@ def test_append_seal_stream_and_decode():
     assert worst <= ATTN_ATOL
 
 
-def test_append_refuses_past_capacity():
+@pytest.mark.parametrize("fused", [False, True])
+def test_append_refuses_past_capacity(fused):
     d = 128
     cfg = K.make_config(d, 2, 1, 2, 2)
     cache = K.KVarNCache(cfg, 1, 1)
     cap = cache.capacity   # 128 + 128 + 127
     k = torch.ones(1, 1, d, dtype=torch.float16, device="cuda")
     for _ in range(cap + 5):
-        cache.append(k, k)
-        cache.seal_group()
+        if fused:
+            cache.append_seal(k, k)
+        else:
+            cache.append(k, k)
+            cache.seal_group()
     torch.cuda.synchronize()
     assert int(cache.seq_len.item()) == cap
+
+
+@pytest.mark.parametrize("d,kb,vb,hkv", [(128, 2, 4, 4), (256, 4, 2, 2)])
+def test_append_seal_matches_two_calls(d, kb, vb, hkv):
+    """The fused launch leaves every buffer bit-identical to append followed by
+    seal_group, step after step, for requests at different points of their
+    group cycle (sink filling, tail filling, a group completing, full)."""
+    wl = synth.Workload("f", 81, 4, hkv, hkv, d, 120, 40, kb, vb, 300)
+    k, v = _streams(wl, 700)
+    cfg = K.make_config(d, hkv, hkv, kb, vb)
+    lens0 = [0, 120, 250, 380]
+    a = K.KVarNCache(cfg, 4, 2)   # capacity 128 + 256 + 127 = 511: request 3 fills up
+    b = K.KVarNCache(cfg, 4, 2)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    a.prefill(kd, vd, lens0)
+    b.prefill(kd, vd, lens0)
+    for step in range(150):
+        pos = [min(n + step, 699) for n in lens0]
+        knew = torch.stack([kd[r, :, pos[r]] for r in range(4)]).contiguous()
+        vnew = torch.stack([vd[r, :, pos[r]] for r in range(4)]).contiguous()
+        a.append(knew, vnew)
+        a.seal_group()
+        b.append_seal(knew, vnew)
+        if step % 10 == 9 or step == 149:
+            torch.cuda.synchronize()
+            for name in ("seq_len", "sink_k", "sink_v", "tail_k", "tail_v", "records"):
+                assert torch.equal(getattr(a, name), getattr(b, name)), (step, name)
+    assert [int(x) for x in b.seq_len.cpu()] == [150, 270, 400, 511]
 
 
 @pytest.mark.parametrize("d,bits,kind", [(128, 2, "k"), (128, 4, "v"), (256, 2, "v"), (256, 4, "k")])
