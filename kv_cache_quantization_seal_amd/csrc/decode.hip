@@ -81,7 +81,6 @@ struct alignas(16) WaveLds {
 template <int D, int KB, int VB, int GQ>
 struct alignas(16) RecSmem {
   WaveLds<D, GQ> wv[kWaves];
-  float qx[GQ][D];              // scaled query, rotated in place
   float mm[kWaves][GQ];         // per-wave partial maxima
   float ll[kWaves][GQ];         // per-wave partial sums
   float oo[kWaves][GQ][D];      // per-wave partial outputs (rotated frame)
@@ -96,6 +95,98 @@ struct alignas(16) ExactSmem {
   float ll[kWaves][GQ];
   float oo[kWaves][GQ][D];
 };
+
+// N dwords from global memory (16-byte pieces where N allows).
+template <int N>
+__device__ __forceinline__ void load_dw_global(uint32_t (&dst)[N], const void* src) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 x = reinterpret_cast<const uint4*>(src)[i];
+      dst[4 * i] = x.x;
+      dst[4 * i + 1] = x.y;
+      dst[4 * i + 2] = x.z;
+      dst[4 * i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = reinterpret_cast<const uint32_t*>(src)[i];
+  }
+}
+
+// Rotated, scaled query of one head as the q~ producer lanes need it, by the
+// wave alone (no LDS, no barrier).  Lane j (0..15) of the head's 16-lane row
+// holds channels QB j .. QB j + QB - 1 in `w` (fp16 pairs).  The Hadamard
+// butterflies run over the low channel bits in registers and over the lane
+// bits across the row (DPP: quad_perm for 1 and 2, masked row shifts for 4,
+// row_ror for 8; the upper lane of a pair keeps lower - upper).  Operand
+// byte i of lane j is channel 16 (j/2) + unpack_index<KB>(8 (j%2) + i) (QB 8)
+// or 16 j + unpack_index<KB>(i) (QB 16); for 2-bit K codes at QB 8 half of
+// those channels sit in lane j^1.  The result is q H_D / sqrt(D) times
+// scale * log2(e) (zero for an invalid head).
+template <int D, int QB, int KB>
+__device__ __forceinline__ void rotate_query(const uint32_t (&w)[QB / 2], bool valid, int j, float scale,
+                                             float (&qr)[QB]) {
+  float x[QB];
+#pragma unroll
+  for (int i = 0; i < QB / 2; ++i) {
+    x[2 * i] = valid ? h2f((uint16_t)(w[i] & 0xFFFFu)) : 0.f;
+    x[2 * i + 1] = valid ? h2f((uint16_t)(w[i] >> 16)) : 0.f;
+  }
+#pragma unroll
+  for (int st = 1; st < QB; st <<= 1) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      if (!(i & st)) {
+        const float u = x[i], v = x[i + st];
+        x[i] = u + v;
+        x[i + st] = u - v;
+      }
+    }
+  }
+#pragma unroll
+  for (int st = 1; st < 16; st <<= 1) {
+    const bool hi = j & st;
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      const int v = __float_as_int(x[i]);
+      int o;
+      if (st == 1) {
+        o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+      } else if (st == 2) {
+        o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+      } else if (st == 4) {
+        o = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+        o = __builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false);  // row_shr:4, banks 1, 3
+      } else {
+        o = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true);   // row_ror:8
+      }
+      const float pv = __int_as_float(o);
+      x[i] = hi ? pv - x[i] : x[i] + pv;
+    }
+  }
+  const float f = scale * kLog2e * ((D == 128) ? 0.08838834764831845f : 0.0625f);
+#pragma unroll
+  for (int i = 0; i < QB; ++i) x[i] *= f;
+  if constexpr (QB == 8 && KB == 2) {
+    // Channel offset m within the 16-channel block: lane 2(j/2) holds
+    // m = 0..7, lane 2(j/2)+1 holds m = 8..15.
+    float nb[QB];
+#pragma unroll
+    for (int i = 0; i < QB; ++i) nb[i] = dpp_f<0xB1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      const int m0 = 4 * (i & 3) + (i >> 2);      // j even
+      const int m1 = 4 * (i & 3) + 2 + (i >> 2);  // j odd
+      const float ve = m0 < 8 ? x[m0 & 7] : nb[m0 & 7];
+      const float vo = m1 < 8 ? nb[m1 & 7] : x[m1 & 7];
+      qr[i] = (j & 1) ? vo : ve;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) qr[i] = x[QB == 8 ? 2 * (i & 3) + (i >> 2) : unpack_index<KB>(i)];
+  }
+}
 
 template <int VB>
 __device__ __forceinline__ int tok_of(int nt, int n) {
@@ -255,46 +346,18 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 
   // The query's loads go out first: loads complete in issue order, so waiting
   // for the query must not also wait for the group loads behind it.
-  constexpr int QPT = (GQ * D + 255) / 256;
-  __half qh[QPT];
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = tid + 256 * i;
-    qh[i] = idx < GQ * D ? a.q[((int64_t)b * a.hq + kvh * GQ) * D + idx] : __half(0.f);
-  }
+  const bool qvalid = hq < GQ;
+  uint32_t qw[QB / 2];
+  load_dw_global<QB / 2>(qw, a.q + (((int64_t)b * a.hq + kvh * GQ + (qvalid ? hq : 0)) * D + QB * j));
   __builtin_amdgcn_sched_barrier(0);
   St SA;
   load_k(SA, ga, ga < gb);
   load_v(SA, ga, ga < gb);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Scaled query (log2 domain) of the GQ heads, rotated: qx <- qx H_D.
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = tid + 256 * i;
-    if (idx < GQ * D) sm.qx[idx / D][idx % D] = __half2float(qh[i]) * a.scale * kLog2e;
-  }
-  __syncthreads();
-  for (int s = 1; s < D; s <<= 1) {
-    for (int idx = tid; idx < GQ * D / 2; idx += 256) {
-      const int h = idx / (D / 2), rr = idx % (D / 2);
-      const int lo = ((rr & ~(s - 1)) << 1) | (rr & (s - 1));
-      const float x0 = sm.qx[h][lo], x1 = sm.qx[h][lo + s];
-      sm.qx[h][lo] = x0 + x1;
-      sm.qx[h][lo + s] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  // q~ producer values: operand byte i of lane (hq, j) is channel
-  // 16 cb + unpack_index<KB>(p), its c^K is half ckh(i) of S.ck.
-  const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
-  const bool qvalid = hq < GQ;
+  // q~ producer values (scaled query in the log2 domain, rotated), per wave.
   float qr[QB];
-#pragma unroll
-  for (int i = 0; i < QB; ++i) {
-    const int ch = QB == 8 ? 16 * (j >> 1) + unpack_index<KB>(8 * (j & 1) + i) : 16 * j + unpack_index<KB>(i);
-    qr[i] = qvalid ? sm.qx[hq][ch] * rs : 0.f;
-  }
+  rotate_query<D, QB, KB>(qw, qvalid, j, a.scale, qr);
   auto ckh = [](int i) { return QB == 8 ? 2 * (i & 3) + (i >> 2) : unpack_index<KB>(i); };
 
   float m_run = -INFINITY, l_run = 0.f;  // head G
