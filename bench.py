@@ -155,40 +155,99 @@ def traffic_summary(args):
     print(open(traffic_file(wl.name)).read())
 
 
-def cpu_baseline(wl, k_stream0, v_stream0, q0, n_seal_groups):
-    """The oracle, as it stands, on a bounded sample of the same workload.
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    Seal: ``n_seal_groups`` groups (K and V tiles) of KV head 0.  Decode: one
-    step (all query heads of KV head 0 over its 32k cache, the oracle state
-    built beforehand), scaled to the full step by the number of KV heads.
-    """
-    from oracle import kvarn_oracle as O
+
+def _blas_threads():
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max([d.get("num_threads", 1) for d in info] or [1])
+        return max([d.get("num_threads", 1) for d in info] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    n0 = wl.start_len(0)
+        return 1
+
+
+def _oracle_unit(task):
+    """One independent (request, KV head) unit of the oracle: seal `n_seal`
+    groups of its stream, then (state built untimed) one decode step of its
+    query heads.  Returns (seal seconds, decode seconds)."""
+    name, b, h, n_seal = task
+    from kv_cache_quantization_seal_amd import synth
+    from oracle import kvarn_oracle as O
+    wl = synth.WORKLOADS[name]
+    n0 = wl.start_len(b)
+    k, v = synth.kv_stream(wl, b, h, n0)
+    q = synth.queries(wl, b, 1)[0]
     t0 = time.perf_counter()
-    for g in range(n_seal_groups):
+    for g in range(n_seal):
         lo = 128 + 128 * g
-        O.encode_record(**_enc(O.seal_tile(k_stream0[lo:lo + 128], wl.k_bits), wl.k_bits, "k"))
-        O.encode_record(**_enc(O.seal_tile(v_stream0[lo:lo + 128], wl.v_bits), wl.v_bits, "v"))
+        O.encode_record(**_enc(O.seal_tile(k[lo:lo + 128], wl.k_bits), wl.k_bits, "k"))
+        O.encode_record(**_enc(O.seal_tile(v[lo:lo + 128], wl.v_bits), wl.v_bits, "v"))
     t_seal = time.perf_counter() - t0
-    st = O.state_from_stream(k_stream0[:n0], v_stream0[:n0], wl.k_bits, wl.v_bits)
-    g = wl.num_q_heads // wl.num_kv_heads
+    st = O.state_from_stream(k, v, wl.k_bits, wl.v_bits)
+    gq = wl.num_q_heads // wl.num_kv_heads
     t1 = time.perf_counter()
-    for h in range(g):
-        st.attend(q0[h])
-    t_dec = time.perf_counter() - t1
-    step_s = t_dec * wl.num_kv_heads
+    for hh in range(gq):
+        st.attend(q[h * gq + hh])
+    return t_seal, time.perf_counter() - t1
+
+
+def cpu_baseline(wl, n_seal_groups):
+    """The oracle, as it stands, on a bounded sample of the same workload, in
+    two modes.  Units are the KV heads of request 0 (independent: each seals
+    its own groups and attends its own query heads).
+
+    * One process (NumPy with its BLAS threads): unit 0 alone, its decode step
+      scaled by the number of KV heads, ``n_seal_groups`` seal groups.
+    * A pool of P = min(16, affinity, KV heads) worker processes with one BLAS
+      thread each, every unit at once: the decode step takes the slowest
+      unit's time; seal throughput is all units' groups over the slowest
+      unit's seal time.
+
+    Runs before the GPU is initialized (the pool's workers are spawned).
+    """
+    import multiprocessing as mp
+    t_start = time.perf_counter()
+    blas = _blas_threads()
+    t_seal1, t_dec1 = _oracle_unit((wl.name, 0, 0, n_seal_groups))
+    single = {"value": wl.batch / (t_dec1 * wl.num_kv_heads), "seal_groups_per_s": n_seal_groups / t_seal1,
+              "threads": int(blas)}
+    units = wl.num_kv_heads
+    P = max(1, min(16, len(os.sched_getaffinity(0)), units))
+    per_unit = max(1, n_seal_groups // units)
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env:
+        os.environ[k] = "1"
+    try:
+        with mp.get_context("spawn").Pool(P) as pool:
+            res = pool.map(_oracle_unit, [(wl.name, 0, h, per_unit) for h in range(units)])
+    finally:
+        for k, val in env.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    t_seal_p = max(r[0] for r in res)
+    t_dec_p = max(r[1] for r in res)
+    gq = wl.num_q_heads // wl.num_kv_heads
+    n0 = wl.start_len(0)
     return {
-        "value": wl.batch / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-        "seal_groups_per_s": n_seal_groups / t_seal,
-        "sample": (f"decode: query heads 0..{g - 1} (KV head 0) over {n0} tokens, one step, x{wl.num_kv_heads} "
-                   f"KV heads; seal: {n_seal_groups} groups (K+V tiles) of KV head 0; float64 NumPy"),
-        "seconds": round(t_seal + t_dec, 2),
+        "value": wl.batch / t_dec_p, "unit": "tokens/s", "cores": int(P), "kind": "oracle",
+        "seal_groups_per_s": units * per_unit / t_seal_p,
+        "sample": (f"one decode step of request 0 over {n0} tokens ({units} KV heads x {gq} query heads) and "
+                   f"{units * per_unit} seal groups (K+V tiles), as {units} KV-head units on {P} worker "
+                   f"processes with one BLAS thread each; float64 NumPy oracle"),
+        "single_process": dict(single, sample=(f"KV head 0 only ({gq} query heads, step scaled x{units}), "
+                                               f"{n_seal_groups} seal groups")),
+        "cpu_model": _cpu_model(),
+        "seconds": round(time.perf_counter() - t_start, 2),
     }
 
 
@@ -228,6 +287,14 @@ def main():
     lens0 = [wl.start_len(b) for b in range(B)]
     lmax = max(lens0) + tokens
     max_groups = (lmax - 128) // 128 + 1
+    # The CPU oracle baseline runs first, before the GPU is initialized (its
+    # worker pool is spawned).
+    cpu_line = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a bounded sample...", file=sys.stderr, flush=True)
+        cpu_line = cpu_baseline(wl, args.cpu_seal_groups)
+        print(f"[bench] cpu oracle: {cpu_line['value']:.4f} tokens/s on {cpu_line['cores']} processes, "
+              f"{cpu_line['seconds']} s", file=sys.stderr, flush=True)
     torch.cuda.init()
     dev = torch.device("cuda:0")
     print(f"[bench] workload {wl.name}: B={B} Hq={hq} Hkv={hkv} D={d} ctx={lens0[0]} "
@@ -389,11 +456,7 @@ def main():
                      "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6},
         "seal": seal,
     }
-    if not args.no_cpu:
-        print("[bench] timing the CPU oracle on a bounded sample...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, kh[0, 0], vh[0, 0], qh[0, 0], args.cpu_seal_groups)
-    else:
-        line["cpu_baseline"] = None
+    line["cpu_baseline"] = cpu_line
     print(json.dumps(line))
 
 
