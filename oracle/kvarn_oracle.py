@@ -50,8 +50,14 @@ R8  s and c are stored as fp16 (round to nearest even); codes come from the
     unrounded float64 values; dequantization uses the stored fp16 scales.
 R9  Record = [codes][s: 128 x fp16][c: D x fp16].  K codes token-major (row t
     holds token t's D codes), V codes channel-major (row j holds channel j's
-    128 codes).  In a row, code i sits at bit b*(i mod (32/b)) of the 32-bit
+    128 codes).  A row is a little-endian bit stream: code i occupies bits
+    [b*i, b*i + b) (bit k of the row is bit k mod 8 of byte k div 8).  For
+    b = 2, 4, 8 this is code i at bit b*(i mod 32/b) of the 32-bit
     little-endian word floor(i*b/32).
+R14 Widths: b in {2, 3, 4, 5, 6, 8} for K and V independently.  The pages
+    name whole widths from two to eight bits and K/V pairs built from them
+    (P2 §5 "Changing Only The Format", §6 "Splitting K And V"); seven bits is
+    named by none of them and is left out.
 R10 Sink = positions [0, 128); group g = positions [128+128g, 256+128g), sealed
     when position 255+128g is appended.  A decode step is append -> seal if
     due -> attend.
@@ -76,6 +82,7 @@ GROUP = 128          # tokens per sealed group (P2 §2.1)
 SINK = 128           # permanently exact leading tokens (P2 §2.1)
 TAIL_CAP = 128       # region R: the exact in-progress group (P2 §2.1)
 SINKHORN_ITERS = 16  # P2 §1
+WIDTHS = (2, 3, 4, 5, 6, 8)  # code widths in bits (reading R14)
 
 
 # --------------------------------------------------------------------------
@@ -148,8 +155,8 @@ def rtn(y: np.ndarray, bits: int):
     Returns (codes uint8 [T][D], delta [T], mid).  code = clip(rint(y/delta +
     mid), 0, 2^b-1) with rint = round half to even; a zero row gets 2^(b-1).
     """
-    if bits not in (2, 4):
-        raise ValueError("bits must be 2 or 4")
+    if bits not in WIDTHS:
+        raise ValueError(f"bits must be one of {WIDTHS}")
     levels = (1 << bits) - 1
     mid = levels / 2.0
     m = np.max(np.abs(y), axis=1)
@@ -185,29 +192,25 @@ def seal_tile(x: np.ndarray, bits: int, iters: int = SINKHORN_ITERS) -> dict:
 # Packing and the record layout (P2 §2.1 "payload with its scale metadata"; R9)
 # --------------------------------------------------------------------------
 def pack_row(codes: np.ndarray, bits: int) -> bytes:
-    """Pack one row of codes: code i at bit b*(i mod 32/b) of LE word i*b/32."""
-    per_word = 32 // bits
+    """Pack one row of codes as a little-endian bit stream: code i occupies
+    bits [b*i, b*i + b) (reading R9)."""
     n = len(codes)
-    if (n * bits) % 32:
-        raise ValueError("row length must fill whole 32-bit words")
-    words = []
-    for w in range(n * bits // 32):
-        v = 0
-        for k in range(per_word):
-            code = int(codes[w * per_word + k])
-            if code >> bits:
-                raise ValueError("code out of range")
-            v |= code << (bits * k)
-        words.append(v)
-    return np.array(words, dtype="<u4").tobytes()
+    if (n * bits) % 8:
+        raise ValueError("row length times bits must fill whole bytes")
+    v = 0
+    for i in range(n):
+        code = int(codes[i])
+        if code < 0 or code >> bits:
+            raise ValueError("code out of range")
+        v |= code << (bits * i)
+    return v.to_bytes(n * bits // 8, "little")
 
 
 def unpack_row(buf: bytes, n: int, bits: int) -> np.ndarray:
-    words = np.frombuffer(buf, dtype="<u4")
-    per_word = 32 // bits
+    v = int.from_bytes(bytes(buf), "little")
     out = np.empty(n, dtype=np.uint8)
     for i in range(n):
-        out[i] = (int(words[i // per_word]) >> (bits * (i % per_word))) & ((1 << bits) - 1)
+        out[i] = (v >> (bits * i)) & ((1 << bits) - 1)
     return out
 
 

@@ -11,20 +11,43 @@ from oracle import kvarn_oracle as O
 
 def test_worked_bytes(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "packing_worked_example.json")))
-    assert O.pack_row(np.array(g["two_bit"]["codes"]), 2).hex() == g["two_bit"]["bytes_hex"]
-    assert O.pack_row(np.array(g["four_bit"]["codes"]), 4).hex() == g["four_bit"]["bytes_hex"]
+    for key, bits in (("two_bit", 2), ("three_bit", 3), ("four_bit", 4), ("five_bit", 5), ("six_bit", 6),
+                      ("eight_bit", 8)):
+        codes = np.array(g[key]["codes"])
+        assert O.pack_row(codes, bits).hex() == g[key]["bytes_hex"], key
+        assert np.array_equal(O.unpack_row(bytes.fromhex(g[key]["bytes_hex"]), len(codes), bits), codes), key
     rb = g["record_bytes"]
+    assert O.record_bytes(128, 3) == rb["d128_b3"]
+    assert O.record_bytes(256, 6) == rb["d256_b6"]
     assert O.record_bytes(128, 2) == rb["d128_b2"]
     assert O.record_bytes(128, 4) == rb["d128_b4"]
     assert O.record_bytes(256, 2) == rb["d256_b2"]
     assert O.record_bytes(256, 4) == rb["d256_b4"]
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_pack_round_trip(bits):
     rng = np.random.default_rng(bits)
     codes = rng.integers(0, 1 << bits, 256).astype(np.uint8)
-    assert np.array_equal(O.unpack_row(O.pack_row(codes, bits), 256, bits), codes)
+    packed = O.pack_row(codes, bits)
+    assert len(packed) == 256 * bits // 8
+    assert np.array_equal(O.unpack_row(packed, 256, bits), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_bit_stream_equals_word_layout(bits):
+    """For widths dividing 32 the bit stream is the 32-bit word layout: code i
+    at bit b*(i mod 32/b) of little-endian word floor(i*b/32)."""
+    rng = np.random.default_rng(20 + bits)
+    codes = rng.integers(0, 1 << bits, 128)
+    per = 32 // bits
+    words = [sum(int(codes[w * per + k]) << (bits * k) for k in range(per)) for w in range(128 * bits // 32)]
+    assert O.pack_row(codes, bits) == np.array(words, dtype="<u4").tobytes()
+
+
+def test_pack_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        O.pack_row(np.array([8, 0, 0, 0, 0, 0, 0, 0]), 3)
 
 
 def test_bits_per_element_matches_page(golden_dir):
@@ -44,7 +67,8 @@ def test_bits_per_element_matches_page(golden_dir):
     assert g["sinkhorn_iterations"]["value"] == O.SINKHORN_ITERS
 
 
-@pytest.mark.parametrize("kind,bits", [("k", 2), ("v", 2), ("k", 4), ("v", 4)])
+@pytest.mark.parametrize("kind,bits", [("k", 2), ("v", 2), ("k", 4), ("v", 4), ("k", 3), ("v", 5), ("k", 6),
+                                       ("v", 8)])
 def test_record_round_trip_and_major_order(kind, bits):
     x = synth.gaussian_tile(3, 128, 128)
     out = O.seal_tile(x, bits)

@@ -27,7 +27,7 @@ def _brute(y, bits):
     return out
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_brute_force_tiny_tiles(bits):
     rng = np.random.default_rng(bits)
     levels = (1 << bits) - 1
@@ -42,7 +42,7 @@ def test_brute_force_tiny_tiles(bits):
         assert np.array_equal(codes, _brute(y, bits))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_error_bound_and_extremes(bits):
     rng = np.random.default_rng(10 + bits)
     y = rng.standard_normal((128, 128)) * rng.lognormal(0, 1, (128, 1))
