@@ -14,7 +14,8 @@
  *        Accumulation in Reasoning Tasks" (fig1.dev summary of arXiv
  *        2606.03458): "What it is", "Why it matters".
  *   [P2] "KVarN KV Cache: Implementation and Benchmarks" (anbeeld.com):
- *        §1 "Where KVarN Comes From", §2.1 "Sink, Body, And Tail".
+ *        §1 "Where KVarN Comes From", §2.1 "Sink, Body, And Tail",
+ *        §5 "Changing Only The Format", §6 "Splitting K And V".
  *
  * Conventions shared by every entry point:
  *   - Every buffer is allocated and owned by the caller.  The library never
@@ -31,9 +32,15 @@
  *       record = [codes][s: 128 x fp16][c: D x fp16],
  *       K codes token-major (row t = token t's D codes),
  *       V codes channel-major (row j = channel j's 128 codes);
- *       in a row, code i sits at bit b*(i mod 32/b) of 32-bit little-endian
- *       word floor(i*b/32).  Dequantized value (rotated frame):
- *       s_t * (code_tj - (2^b-1)/2) * c_j; original frame: times H_D/sqrt(D).
+ *       a row is a little-endian bit stream in which code i occupies bits
+ *       [b*i, b*i + b) (for b = 2, 4, 8: bit b*(i mod 32/b) of 32-bit
+ *       little-endian word floor(i*b/32)).  Dequantized value (rotated
+ *       frame): s_t * (code_tj - (2^b-1)/2) * c_j; original frame: times
+ *       H_D/sqrt(D).
+ *   - Code widths b are 2, 3, 4, 5, 6 or 8 bits [P2 §5 "Changing Only The
+ *     Format", §6 "Splitting K And V"].  The (k_bits, v_bits) pairs built
+ *     are every symmetric width, 2/4, 4/2, and the presets 3/2, 5/4 and 6/5;
+ *     other pairs return KVARN_EUNSUPPORTED.
  */
 #ifndef KVARN_H
 #define KVARN_H
@@ -63,8 +70,8 @@ typedef struct {
   int32_t head_dim;       /* D: 128 or 256 */
   int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;   /* Hkv; Hq/Hkv must be 1, 2 or 4 */
-  int32_t k_bits;         /* 2 or 4 */
-  int32_t v_bits;         /* 2 or 4 */
+  int32_t k_bits;         /* 2, 3, 4, 5, 6 or 8 (see the pairs above) */
+  int32_t v_bits;         /* 2, 3, 4, 5, 6 or 8 */
   int32_t group;          /* must be 128 */
   int32_t sink;           /* must be 128 */
   int32_t sinkhorn_iters; /* 0..64; KVarN uses 16 */
@@ -94,7 +101,8 @@ typedef struct {
 /* Checks a config; KVARN_OK or the status an entry point would return. */
 kvarn_status kvarn_check_config(const kvarn_config *cfg);
 
-/* Bytes of one record: 128*D*bits/8 + 2*128 + 2*D; 0 if unsupported. */
+/* Bytes of one record: 128*D*bits/8 + 2*128 + 2*D; 0 if unsupported
+ * (bits must be 2, 3, 4, 5, 6 or 8). */
 size_t kvarn_record_bytes(int32_t head_dim, int32_t bits);
 
 /* Bytes of one (K record, V record) pair; 0 for an invalid config. */

@@ -97,15 +97,16 @@ __global__ __launch_bounds__(2 * D) void dequant_kernel(const uint8_t* __restric
   for (int i = 0; i < 64; ++i) {
     const int j = 64 * rb + i;
     uint32_t code;
-    if (KIND == 0) {
-      const int idx = j;  // token-major: code j of row t
-      const uint32_t word = reinterpret_cast<const uint32_t*>(rec + (size_t)t * (D * BITS / 8))[idx * BITS / 32];
-      code = (word >> (BITS * (idx % (32 / BITS)))) & ((1u << BITS) - 1);
-    } else {
-      const int idx = t;  // channel-major: code t of row j
-      const uint32_t word = reinterpret_cast<const uint32_t*>(rec + (size_t)j * (kGroup * BITS / 8))[idx * BITS / 32];
-      code = (word >> (BITS * (idx % (32 / BITS)))) & ((1u << BITS) - 1);
-    }
+    // A row is a little-endian bit stream: code idx occupies bits
+    // [BITS idx, BITS idx + BITS); rows are 4-byte aligned.
+    const uint8_t* row = KIND == 0 ? rec + (size_t)t * (D * BITS / 8)           // token-major: code j of row t
+                                   : rec + (size_t)j * (kGroup * BITS / 8);     // channel-major: code t of row j
+    const int idx = KIND == 0 ? j : t;
+    const int bit = BITS * idx;
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(row) + bit / 32;
+    uint64_t pair = wp[0];
+    if (bit % 32 + BITS > 32) pair |= (uint64_t)wp[1] << 32;
+    code = (uint32_t)(pair >> (bit % 32)) & ((1u << BITS) - 1);
     x[i] = st * ((float)code - MID) * h2f(c16[j]);
   }
   rotate_row_slice<D, P>(x, xs, t, rb);
@@ -152,13 +153,9 @@ static void launch_dq(int kind, const void* src, int64_t stride, void* dst, int 
 
 hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
                           hipStream_t st) {
-  if (D == 128) {
-    if (bits == 2) launch_dq<128, 2>(kind, src, src_stride, dst, n, st);
-    else launch_dq<128, 4>(kind, src, src_stride, dst, n, st);
-  } else {
-    if (bits == 2) launch_dq<256, 2>(kind, src, src_stride, dst, n, st);
-    else launch_dq<256, 4>(kind, src, src_stride, dst, n, st);
-  }
+#define CALL(d, b) launch_dq<d, b>(kind, src, src_stride, dst, n, st)
+  KVARN_DISPATCH_DB(D, bits, CALL);
+#undef CALL
   return hipGetLastError();
 }
 

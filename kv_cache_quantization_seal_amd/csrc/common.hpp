@@ -110,12 +110,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 //          dword k is code 4b + k;
 //   4-bit: dwords w0,w1 -> w0 & M, (w0 >> 4) & M, w1 & M, (w1 >> 4) & M with
 //          M = 0x0F0F0F0F: byte b of dword k is code 8(k/2) + 2b + (k%2).
+//   other widths: byte p is code p (natural order).
 template <int BITS>
 __host__ __device__ constexpr int unpack_index(int p) {
-  return BITS == 2 ? 4 * (p & 3) + (p >> 2) : 8 * ((p >> 2) >> 1) + 2 * (p & 3) + ((p >> 2) & 1);
+  return BITS == 2 ? 4 * (p & 3) + (p >> 2)
+                   : BITS == 4 ? 8 * ((p >> 2) >> 1) + 2 * (p & 3) + ((p >> 2) & 1) : p;
 }
 
-// Unpack one 16-code block (BITS*2 bytes) into 16 int8 MFMA operand bytes.
+// Unpack one 16-code block (BITS*2 bytes) into 16 int8 MFMA operand bytes
+// (widths 2 and 4).
 template <int BITS>
 __device__ __forceinline__ v4i unpack16(const uint32_t* w) {
   v4i r;
@@ -132,6 +135,44 @@ __device__ __forceinline__ v4i unpack16(const uint32_t* w) {
     r[3] = (int)((w[1] >> 4) & 0x0F0F0F0Fu);
   }
   return r;
+}
+
+// Block s (16 codes) of a lane's chunk of N dwords of one record row, as 16
+// int8 MFMA operand bytes in unpack_index order.  Widths 2 and 4 keep their
+// mask-and-shift order; 8-bit codes are offset by -128 to fit int8 (the
+// caller corrects the mid level for that); 3, 5 and 6 bits are extracted in
+// natural order from the row's little-endian bit stream.
+template <int BITS, int N>
+__device__ __forceinline__ v4i unpack_block(const uint32_t (&c)[N], int s) {
+  if constexpr (BITS == 2) {
+    return unpack16<2>(&c[s]);
+  } else if constexpr (BITS == 4) {
+    return unpack16<4>(&c[2 * s]);
+  } else if constexpr (BITS == 8) {
+    v4i r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = (int)(c[4 * s + k] ^ 0x80808080u);
+    return r;
+  } else {
+    v4i r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bit = 16 * BITS * s + BITS * (4 * k + e);
+        const int wi = bit / 32, sh = bit % 32;
+        uint32_t v;
+        if (sh + BITS <= 32)
+          v = (c[wi] >> sh) & ((1u << BITS) - 1);
+        else
+          v = __builtin_amdgcn_alignbit(c[wi + 1], c[wi], sh) & ((1u << BITS) - 1);
+        d |= v << (8 * e);
+      }
+      r[k] = (int)d;
+    }
+    return r;
+  }
 }
 
 // Magic-number rounding: for |x| < 2^22, x + 1.5*2^23 rounds x to the nearest

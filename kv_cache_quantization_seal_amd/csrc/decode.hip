@@ -184,7 +184,7 @@ __device__ __forceinline__ void rotate_query(const uint32_t (&w)[QB / 2], bool v
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < QB; ++i) qr[i] = x[QB == 8 ? 2 * (i & 3) + (i >> 2) : unpack_index<KB>(i)];
+    for (int i = 0; i < QB; ++i) qr[i] = x[QB == 8 ? (KB == 4 ? 2 * (i & 3) + (i >> 2) : i) : unpack_index<KB>(i)];
   }
 }
 
@@ -199,10 +199,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-// Largest |top limb| so that sum_j A_j (2 code_j - L) fits int32, with
-// A_j = a0*2^14 + a1*2^7 + a2 and |a1|,|a2| <= 64, over k_terms terms.
+// Largest |top limb| 2^m - 1 so that sum_j A_j (2 code_j - L) fits int32,
+// with A_j = a0*2^14 + a1*2^7 + a2 and |a1|,|a2| <= 64, over k_terms terms:
+// k L (a0max 2^14 + 8256) < 2^31.
 __host__ __device__ constexpr float top_limb(int k_terms, int levels) {
-  return (k_terms * levels <= 768) ? 127.0f : (k_terms * levels <= 1920 ? 63.0f : 31.0f);
+  int t = 127;
+  while (t > 1 && (double)k_terms * levels * ((double)t * 16384.0 + 8256.0) >= 2147483648.0) t >>= 1;
+  return (float)t;
 }
 
 __device__ __forceinline__ void store_partial_ml(const DecodeArgs& a, int b, int hq_idx, int split, float m, float l) {
@@ -232,10 +235,14 @@ struct Stage {
   uint32_t cv[Gm::NCT / 2];
 };
 
+// N dwords at byte offset `off` of a buffer: 16-byte loads when N is a
+// multiple of 4 (those offsets are 16-byte aligned), else 8- or 4-byte ones.
 template <int N>
 __device__ __forceinline__ void load_dw(uint32_t (&dst)[N], __amdgpu_buffer_rsrc_t r, int off) {
-  static_assert(N % 2 == 0 || N == 1, "");
-  if constexpr (N == 1) {
+  if constexpr (N % 4 != 0 && N > 2) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+  } else if constexpr (N == 1) {
     dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   } else if constexpr (N == 2) {
     const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
@@ -266,6 +273,13 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   constexpr int LK = (1 << KB) - 1, LV = (1 << VB) - 1;
   constexpr float QMAX = top_limb(D, LK);
   constexpr float WMAX = top_limb(kGroup, LV);
+  // 8-bit codes enter the MFMAs offset by -128: sum q (2 code - L) =
+  // 2 sum q (code - 128) - (L - 256) sum q.
+  constexpr int LKE = KB == 8 ? LK - 256 : LK, LVE = VB == 8 ? LV - 256 : LV;
+  // Token order of a lane's eight tokens (see tok_of) and the half index of
+  // token nt in the lane's s^K / s^V dwords.
+  auto tstep = [](int nt) { return VB == 2 ? 4 * (nt & 3) + (nt >> 2) : VB == 4 ? 2 * (nt & 3) + (nt >> 2) : nt; };
+  auto shalf = [](int nt) { return (VB == 2 || VB == 4) ? 2 * (nt & 3) + (nt >> 2) : nt; };
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
   const int tid = threadIdx.x;
@@ -284,19 +298,19 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   const int gb = min(gw0 + a.groups_per_wave, n_groups);
 
   // Per-lane byte offsets within a group (loop-invariant).
-  // Tokens tok(0..7, n) are tok0 + 2(nt&3) + (nt>>2) with
-  // tok0 = 16(n/2) + 8(n&1) (4-bit V), or tok0 + 4(nt&3) + (nt>>2) with
-  // tok0 = 16(n/2) + 2(n&1) (2-bit V): a lane base plus a constant.
-  const int tok0 = VB == 4 ? 16 * (n >> 1) + 8 * (n & 1) : 16 * (n >> 1) + 2 * (n & 1);
+  // Tokens tok(0..7, n) are tok0 + tstep(nt): tok0 = 16(n/2) + 2(n&1) and
+  // steps 4(nt&3) + (nt>>2) (2-bit V), tok0 = 8n and steps 2(nt&3) + (nt>>2)
+  // (4-bit V) or nt (other widths): a lane base plus a constant.
+  const int tok0 = VB == 2 ? 16 * (n >> 1) + 2 * (n & 1) : 8 * n;
   const int kbase = tok0 * Gm::KROW + G * Gm::LBK;
-  auto kofs = [&](int nt) { return kbase + (VB == 4 ? 2 * (nt & 3) + (nt >> 2) : 4 * (nt & 3) + (nt >> 2)) * Gm::KROW; };
+  auto kofs = [&](int nt) { return kbase + tstep(nt) * Gm::KROW; };
   const int skofs = Gm::KCODE + 2 * tok0;
   const int svofs = Gm::KREC + Gm::VCODE + 2 * tok0;
   // q~ producer lane: head hq = l/16, operand bytes [QB*j, QB*j + QB), j = l%16.
   const int hq = l >> 4, j = l & 15;
   int ckofs;
   if constexpr (QB == 8)
-    ckofs = Gm::KCODE + 2 * kGroup + 2 * (16 * (j >> 1) + (KB == 4 ? 8 * (j & 1) : 2 * (j & 1)));
+    ckofs = Gm::KCODE + 2 * kGroup + 2 * (16 * (j >> 1) + (KB == 2 ? 2 * (j & 1) : 8 * (j & 1)));
   else
     ckofs = Gm::KCODE + 2 * kGroup + 2 * (16 * j);
   const int cvofs = Gm::KREC + Gm::VCODE + 2 * kGroup + 2 * NCT * n;
@@ -322,7 +336,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
     } else {
       load_dw(S.ck, r, ckofs);
     }
-    if constexpr (VB == 4) {
+    if constexpr (VB != 2) {
       load_dw(S.sk, r, skofs);
     } else {
 #pragma unroll
@@ -333,7 +347,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   };
   auto load_v = [&](St& S, int g, bool on) {
     const __amdgpu_buffer_rsrc_t r = rsrc_of(g, on);
-    if constexpr (VB == 4) {
+    if constexpr (VB != 2) {
       load_dw(S.sv, r, svofs);
     } else {
 #pragma unroll
@@ -358,7 +372,9 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   // q~ producer values (scaled query in the log2 domain, rotated), per wave.
   float qr[QB];
   rotate_query<D, QB, KB>(qw, qvalid, j, a.scale, qr);
-  auto ckh = [](int i) { return QB == 8 ? 2 * (i & 3) + (i >> 2) : unpack_index<KB>(i); };
+  auto ckh = [](int i) {
+    return QB == 8 ? ((KB == 2 || KB == 4) ? 2 * (i & 3) + (i >> 2) : i) : unpack_index<KB>(i);
+  };
 
   float m_run = -INFINITY, l_run = 0.f;  // head G
   float o_acc[NCT];                      // head G, channel NCT*n + ct
@@ -422,7 +438,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 #pragma unroll
     for (int s = 0; s < KS; ++s) sacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], ones, sacc, 0, 0, 0);
     const uint32_t negls =
-        0u - (uint32_t)LK * (((uint32_t)sacc[0] << 14) + ((uint32_t)sacc[1] << 7) + (uint32_t)sacc[2]);
+        0u - (uint32_t)LKE * (((uint32_t)sacc[0] << 14) + ((uint32_t)sacc[1] << 7) + (uint32_t)sacc[2]);
     const float kscale = E * (1.0f / (QMAX * 32768.0f));
     float logit[NTT];
     float lmax = -INFINITY;
@@ -431,10 +447,10 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack16<KB>(&S.k[nt][s * (KB / 2)]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack_block<KB>(S.k[nt], s), acc, 0, 0, 0);
       const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
       const int yv = (int)((x << 1) + negls);
-      logit[nt] = hvalid ? (float)yv * (half_of(S.sk, 2 * (nt & 3) + (nt >> 2)) * kscale) : -INFINITY;
+      logit[nt] = hvalid ? (float)yv * (half_of(S.sk, shalf(nt)) * kscale) : -INFINITY;
       lmax = fmaxf(lmax, logit[nt]);
     }
     load_k(S, gn, on);
@@ -450,7 +466,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
     for (int nt = 0; nt < NTT; ++nt) {
       const float p = hvalid ? __builtin_amdgcn_exp2f(logit[nt] - m_new) : 0.f;
       psum += p;
-      wv_[nt] = p * half_of(S.sv, 2 * (nt & 3) + (nt >> 2));
+      wv_[nt] = p * half_of(S.sv, shalf(nt));
       wm = fmaxf(wm, wv_[nt]);
     }
     l_run = fmaf(l_run, alpha, psum);
@@ -494,14 +510,14 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 #pragma unroll
     for (int s = 0; s < 2; ++s) tacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], ones, tacc, 0, 0, 0);
     const uint32_t neglt =
-        0u - (uint32_t)LV * (((uint32_t)tacc[0] << 14) + ((uint32_t)tacc[1] << 7) + (uint32_t)tacc[2]);
+        0u - (uint32_t)LVE * (((uint32_t)tacc[0] << 14) + ((uint32_t)tacc[1] << 7) + (uint32_t)tacc[2]);
     const float vscale = W * (1.0f / (WMAX * 32768.0f));
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], unpack16<VB>(&S.v[ct][s * (VB / 2)]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[s], unpack_block<VB>(S.v[ct], s), acc, 0, 0, 0);
       const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
       const int yv = (int)((x << 1) + neglt);
       o_acc[ct] = fmaf((float)yv * vscale, half_of(S.cv, ct), o_acc[ct]);
@@ -904,24 +920,16 @@ static int resident_g(int gq, int dev) {
 
 int decode_resident_wgs(int D, int kb, int vb, int gq) {
   // Cached per device and kernel instance: [device][D][kb][vb][gq].
-  static std::atomic<int> cache[16][2][2][2][3];
+  static std::atomic<int> cache[16][2][6][6][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxResidentWgs;
-  const int di = D == 128 ? 0 : 1, ki = kb == 2 ? 0 : 1, vi = vb == 2 ? 0 : 1, gi = gq == 1 ? 0 : gq == 2 ? 1 : 2;
+  const int di = D == 128 ? 0 : 1, ki = width_index(kb), vi = width_index(vb), gi = gq == 1 ? 0 : gq == 2 ? 1 : 2;
   std::atomic<int>* slot = dev < 16 ? &cache[dev][di][ki][vi][gi] : nullptr;
   int r = slot ? slot->load(std::memory_order_relaxed) : 0;
   if (r > 0) return r;
-  if (D == 128) {
-    if (kb == 2 && vb == 2) r = resident_g<128, 2, 2>(gq, dev);
-    else if (kb == 2) r = resident_g<128, 2, 4>(gq, dev);
-    else if (vb == 2) r = resident_g<128, 4, 2>(gq, dev);
-    else r = resident_g<128, 4, 4>(gq, dev);
-  } else {
-    if (kb == 2 && vb == 2) r = resident_g<256, 2, 2>(gq, dev);
-    else if (kb == 2) r = resident_g<256, 2, 4>(gq, dev);
-    else if (vb == 2) r = resident_g<256, 4, 2>(gq, dev);
-    else r = resident_g<256, 4, 4>(gq, dev);
-  }
+#define CALL(d, k, v) r = resident_g<d, k, v>(gq, dev)
+  KVARN_DISPATCH_DKV(D, kb, vb, CALL);
+#undef CALL
   r = r > 0 ? std::min(r, kMaxResidentWgs) : kMaxResidentWgs;
   if (slot) slot->store(r, std::memory_order_relaxed);
   return r;
@@ -943,17 +951,9 @@ static void launch_g(int gq, const DecodeArgs& a, int phases, hipStream_t st) {
 }
 
 hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int phases, hipStream_t st) {
-  if (D == 128) {
-    if (kb == 2 && vb == 2) launch_g<128, 2, 2>(gq, a, phases, st);
-    else if (kb == 2 && vb == 4) launch_g<128, 2, 4>(gq, a, phases, st);
-    else if (kb == 4 && vb == 2) launch_g<128, 4, 2>(gq, a, phases, st);
-    else launch_g<128, 4, 4>(gq, a, phases, st);
-  } else {
-    if (kb == 2 && vb == 2) launch_g<256, 2, 2>(gq, a, phases, st);
-    else if (kb == 2 && vb == 4) launch_g<256, 2, 4>(gq, a, phases, st);
-    else if (kb == 4 && vb == 2) launch_g<256, 4, 2>(gq, a, phases, st);
-    else launch_g<256, 4, 4>(gq, a, phases, st);
-  }
+#define CALL(d, k, v) launch_g<d, k, v>(gq, a, phases, st)
+  KVARN_DISPATCH_DKV(D, kb, vb, CALL);
+#undef CALL
   return hipGetLastError();
 }
 

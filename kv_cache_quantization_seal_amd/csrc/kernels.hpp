@@ -9,6 +9,50 @@ namespace kvarn {
 
 constexpr int kMaxPrefillBatch = 256;  // requests per prefill launch
 
+// Code widths (bits) and the (K, V) width pairs the kernels are built for:
+// every symmetric width, the pairs of widths 2 and 4, and the asymmetric
+// presets 3-2, 5-4 and 6-5.
+constexpr bool width_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
+constexpr bool pair_ok(int kb, int vb) {
+  return (kb == vb && width_ok(kb)) || (kb == 2 && vb == 4) || (kb == 4 && vb == 2) || (kb == 3 && vb == 2) ||
+         (kb == 5 && vb == 4) || (kb == 6 && vb == 5);
+}
+// Index of a width in 2, 3, 4, 5, 6, 8.
+constexpr int width_index(int b) { return b == 8 ? 5 : b - 2; }
+
+// CALL(d, kb, vb) for the instance matching (D, KB, VB); nothing for a pair
+// that pair_ok rejects (the host checks first).
+#define KVARN_PAIRS_FOR_D(d, KB, VB, CALL)      \
+  if (KB == 2 && VB == 2) CALL(d, 2, 2);        \
+  else if (KB == 2 && VB == 4) CALL(d, 2, 4);   \
+  else if (KB == 4 && VB == 2) CALL(d, 4, 2);   \
+  else if (KB == 4 && VB == 4) CALL(d, 4, 4);   \
+  else if (KB == 3 && VB == 3) CALL(d, 3, 3);   \
+  else if (KB == 5 && VB == 5) CALL(d, 5, 5);   \
+  else if (KB == 6 && VB == 6) CALL(d, 6, 6);   \
+  else if (KB == 8 && VB == 8) CALL(d, 8, 8);   \
+  else if (KB == 3 && VB == 2) CALL(d, 3, 2);   \
+  else if (KB == 5 && VB == 4) CALL(d, 5, 4);   \
+  else if (KB == 6 && VB == 5) CALL(d, 6, 5);
+#define KVARN_DISPATCH_DKV(D, KB, VB, CALL)     \
+  do {                                          \
+    if (D == 128) {                             \
+      KVARN_PAIRS_FOR_D(128, KB, VB, CALL)      \
+    } else {                                    \
+      KVARN_PAIRS_FOR_D(256, KB, VB, CALL)      \
+    }                                           \
+  } while (0)
+#define KVARN_DISPATCH_DB(D, B, CALL)                                                 \
+  do {                                                                                \
+    if (D == 128) {                                                                   \
+      if (B == 2) CALL(128, 2); else if (B == 3) CALL(128, 3); else if (B == 4) CALL(128, 4); \
+      else if (B == 5) CALL(128, 5); else if (B == 6) CALL(128, 6); else if (B == 8) CALL(128, 8); \
+    } else {                                                                          \
+      if (B == 2) CALL(256, 2); else if (B == 3) CALL(256, 3); else if (B == 4) CALL(256, 4); \
+      else if (B == 5) CALL(256, 5); else if (B == 6) CALL(256, 6); else if (B == 8) CALL(256, 8); \
+    }                                                                                 \
+  } while (0)
+
 struct PrefillLens {
   int32_t len[kMaxPrefillBatch];
 };

@@ -29,7 +29,7 @@ kvarn_status ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool bits_ok(int b) { return b == 2 || b == 4; }
+bool bits_ok(int b) { return kvarn::width_ok(b); }
 bool dim_ok(int d) { return d == 128 || d == 256; }
 
 kvarn_status check_cfg(const kvarn_config* c) {
@@ -38,7 +38,12 @@ kvarn_status check_cfg(const kvarn_config* c) {
     return fail(KVARN_EUNSUPPORTED, "group and sink must both be 128 (got %d, %d)", c->group, c->sink);
   if (!dim_ok(c->head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", c->head_dim);
   if (!bits_ok(c->k_bits) || !bits_ok(c->v_bits))
-    return fail(KVARN_EUNSUPPORTED, "k_bits and v_bits must be 2 or 4 (got %d, %d)", c->k_bits, c->v_bits);
+    return fail(KVARN_EUNSUPPORTED, "k_bits and v_bits must be 2, 3, 4, 5, 6 or 8 (got %d, %d)", c->k_bits,
+                c->v_bits);
+  if (!kvarn::pair_ok(c->k_bits, c->v_bits))
+    return fail(KVARN_EUNSUPPORTED,
+                "K/V widths %d/%d are not built (symmetric widths, 2/4, 4/2, 3/2, 5/4 and 6/5 are)", c->k_bits,
+                c->v_bits);
   if (c->num_q_heads <= 0 || c->num_kv_heads <= 0)
     return fail(KVARN_EINVAL, "head counts must be positive (got %d, %d)", c->num_q_heads, c->num_kv_heads);
   if (c->num_q_heads % c->num_kv_heads)
@@ -313,7 +318,7 @@ kvarn_status kvarn_decode_attn_combine(const kvarn_config* cfg, const kvarn_cach
 kvarn_status kvarn_seal_tiles(int32_t head_dim, int32_t bits, int32_t kind, int32_t sinkhorn_iters, const void* src,
                               void* dst, int64_t dst_stride, float* dbg, int32_t n, void* stream) {
   if (!dim_ok(head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", head_dim);
-  if (!bits_ok(bits)) return fail(KVARN_EUNSUPPORTED, "bits must be 2 or 4 (got %d)", bits);
+  if (!bits_ok(bits)) return fail(KVARN_EUNSUPPORTED, "bits must be 2, 3, 4, 5, 6 or 8 (got %d)", bits);
   if (kind != 0 && kind != 1) return fail(KVARN_EINVAL, "kind must be 0 (K) or 1 (V) (got %d)", kind);
   if (sinkhorn_iters < 0 || sinkhorn_iters > 64) return fail(KVARN_EINVAL, "sinkhorn_iters must be in [0, 64]");
   if (n < 0) return fail(KVARN_EINVAL, "n must be >= 0");
@@ -331,7 +336,7 @@ kvarn_status kvarn_seal_tiles(int32_t head_dim, int32_t bits, int32_t kind, int3
 kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind, const void* src, int64_t src_stride,
                                    void* dst, int32_t n, void* stream) {
   if (!dim_ok(head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", head_dim);
-  if (!bits_ok(bits)) return fail(KVARN_EUNSUPPORTED, "bits must be 2 or 4 (got %d)", bits);
+  if (!bits_ok(bits)) return fail(KVARN_EUNSUPPORTED, "bits must be 2, 3, 4, 5, 6 or 8 (got %d)", bits);
   if (kind != 0 && kind != 1) return fail(KVARN_EINVAL, "kind must be 0 (K) or 1 (V) (got %d)", kind);
   if (n < 0) return fail(KVARN_EINVAL, "n must be >= 0");
   if (n == 0) return ok();

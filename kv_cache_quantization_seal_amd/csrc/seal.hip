@@ -107,48 +107,56 @@ __device__ __forceinline__ void load_tile(uint4 (&raw)[4], const __half* __restr
 
 // One Hadamard stage across the lanes whose block indices differ in bit M of
 // a 4-lane quad (M = 1, 2) or of an 8-lane group (M = 4): the lane with the
-// bit clear keeps x + x', the other x - x' negated, i.e. x' - ... computed as
-// x + s x' with s = -1; the negations are undone by the caller.
+// bit clear keeps x + x', the other x - x' negated, i.e. computed as x + s x'
+// with s = -1; the negations are undone by the caller.  Values are float64
+// (two 32-bit halves move through DPP).
 template <int M>
-__device__ __forceinline__ void block_stage(float (&x)[32], bool upper) {
-  const float s = upper ? -1.0f : 1.0f;
+__device__ __forceinline__ int dpp_pair(int v) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else {
+    // Lanes 0-3 of each eight read lanes 4-7 (row_shl:4, banks 0 and 2),
+    // lanes 4-7 read lanes 0-3 (row_shr:4, banks 1 and 3).
+    const int o = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);
+    return __builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false);
+  }
+}
+template <int M>
+__device__ __forceinline__ void block_stage(double (&x)[32], bool upper) {
+  const double s = upper ? -1.0 : 1.0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const int v = __float_as_int(x[i]);
-    int o;
-    if constexpr (M == 1) {
-      o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-    } else if constexpr (M == 2) {
-      o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
-    } else {
-      // Lanes 0-3 of each eight read lanes 4-7 (row_shl:4, banks 0 and 2),
-      // lanes 4-7 read lanes 0-3 (row_shr:4, banks 1 and 3).
-      o = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);
-      o = __builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false);
-    }
-    x[i] = fmaf(s, __int_as_float(o), x[i]);
+    const int lo = dpp_pair<M>(__double2loint(x[i]));
+    const int hi = dpp_pair<M>(__double2hiint(x[i]));
+    x[i] = fma(s, __hiloint2double(hi, lo), x[i]);
   }
 }
 
 // Rotation X_r = X H_D / sqrt(D) of the tile in `raw` into the LDS tile, then
-// the factor vectors reset.  Butterflies over the five low channel-index bits
-// run in registers, those over the block bits across neighbouring lanes.  A
-// lane whose block index has an odd number of set bits ends with its values
-// negated by those lane stages (each stage negates the lanes with its bit
-// set, and the negations commute with the later stages), which the final
-// scale undoes.  Ends with a barrier.
+// the factor vectors reset.  The sums run in float64, where they are exact
+// (a sum of at most 256 fp16 values needs at most 48 significant bits), and
+// are rounded to fp32 once: in fp32, channels whose rotated value nearly
+// cancels would keep rounding noise of the size of the value itself.
+// Butterflies over the five low channel-index bits run in registers, those
+// over the block bits across neighbouring lanes.  A lane whose block index
+// has an odd number of set bits ends with its values negated by those lane
+// stages (each stage negates the lanes with its bit set, and the negations
+// commute with the later stages), which the final scale undoes.  Ends with a
+// barrier.
 template <int D>
 __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& sm, int tid) {
   constexpr int NB = D / 32;
   const int tl = tid / NB, bl = tid % NB;
-  float x[32];
+  double x[32];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t ws[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[8 * k + 2 * e] = h2f((uint16_t)(ws[e] & 0xFFFFu));
-      x[8 * k + 2 * e + 1] = h2f((uint16_t)(ws[e] >> 16));
+      x[8 * k + 2 * e] = (double)h2f((uint16_t)(ws[e] & 0xFFFFu));
+      x[8 * k + 2 * e + 1] = (double)h2f((uint16_t)(ws[e] >> 16));
     }
   }
 #pragma unroll
@@ -156,7 +164,7 @@ __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& 
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (!(i & st)) {
-        const float a0 = x[i], a1 = x[i + st];
+        const double a0 = x[i], a1 = x[i + st];
         x[i] = a0 + a1;
         x[i + st] = a0 - a1;
       }
@@ -165,11 +173,12 @@ __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& 
   block_stage<1>(x, bl & 1);
   block_stage<2>(x, bl & 2);
   if constexpr (NB == 8) block_stage<4>(x, bl & 4);
-  const float rs = ((D == 128) ? 0.08838834764831845f : 0.0625f) * ((__popc(bl) & 1) ? -1.0f : 1.0f);
+  const double rs = ((D == 128) ? 0.088388347648318440550 : 0.0625) * ((__popc(bl) & 1) ? -1.0 : 1.0);
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     *reinterpret_cast<float4*>(xg(sm, tl, 8 * bl + k)) =
-        make_float4(x[4 * k] * rs, x[4 * k + 1] * rs, x[4 * k + 2] * rs, x[4 * k + 3] * rs);
+        make_float4((float)(x[4 * k] * rs), (float)(x[4 * k + 1] * rs), (float)(x[4 * k + 2] * rs),
+                    (float)(x[4 * k + 3] * rs));
   if (tid < D) {
     sm.u[sk(tid)] = 1.0f;
     sm.c2[tid] = 1.0f;
@@ -291,6 +300,35 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
   }
 }
 
+// Sixteen codes of one record row as a little-endian bit stream: code e
+// occupies bits [BITS e, BITS e + BITS) of the words (the whole-row layout
+// restricted to one 16-code block, which starts on a byte boundary).
+template <int BITS>
+__device__ __forceinline__ void pack16(const uint32_t (&code)[16], uint32_t (&w)[(16 * BITS + 31) / 32]) {
+#pragma unroll
+  for (int k = 0; k < (16 * BITS + 31) / 32; ++k) w[k] = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int bit = BITS * e;
+    w[bit / 32] |= code[e] << (bit % 32);
+    if (bit % 32 + BITS > 32) w[bit / 32 + 1] |= code[e] >> (32 - bit % 32);
+  }
+}
+
+// Store the 2*BITS bytes of a packed 16-code block at dst (dst is 2*BITS
+// bytes into a row: 4-byte aligned when BITS is even, 2-byte aligned else).
+template <int BITS>
+__device__ __forceinline__ void store16(uint8_t* dst, const uint32_t (&w)[(16 * BITS + 31) / 32]) {
+  if constexpr (BITS % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k) reinterpret_cast<uint32_t*>(dst)[k] = w[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+      reinterpret_cast<uint16_t*>(dst)[k] = (uint16_t)((k & 1) ? (w[k / 2] >> 16) : (w[k / 2] & 0xFFFFu));
+  }
+}
+
 // Channel and token scales, round to nearest and packing of the tile that
 // seal_iterate left (X_r in LDS, c_j^2 in sm.c2) into record `rec`.  Every
 // global store comes last, after all of the phase's arithmetic: a store's
@@ -304,8 +342,7 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
   constexpr float MID = 0.5f * LEVELS;
   constexpr int CODE_BYTES = kGroup * D * BITS / 8;
   constexpr int RL = SealRoles<D>::RL;
-  constexpr int WORDS = 16 * BITS / 32;  // code words per 16 codes
-  constexpr int PER = 32 / BITS;         // codes per word
+  constexpr int NW = (16 * BITS + 31) / 32;  // 32-bit words holding 16 codes
   const SealRoles<D> ro(tid);
   const int tp = ro.tp, cb = ro.cb, cp = ro.cp, tb = ro.tb;
 
@@ -353,20 +390,15 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
   // ---- codes -------------------------------------------------------------
   // K record: tokens 2tp, 2tp+1, channels [16 cb, 16 cb + 16) (row role).
   // V record: channels 2cp, 2cp+1, tokens [16 tb, 16 tb + 16) (column role).
-  uint32_t out[2][WORDS];
+  uint32_t out[2][NW];
   if constexpr (TOKEN_MAJOR) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
+      uint32_t code[16];
 #pragma unroll
-      for (int k = 0; k < WORDS; ++k) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          const float c = fminf(fmaxf(rintf(fmaf(zr[r][k * PER + e], inv[r], MID)), 0.f), (float)LEVELS);
-          word |= (uint32_t)c << (BITS * e);
-        }
-        out[r][k] = word;
-      }
+      for (int e = 0; e < 16; ++e)
+        code[e] = (uint32_t)fminf(fmaxf(rintf(fmaf(zr[r][e], inv[r], MID)), 0.f), (float)LEVELS);
+      pack16<BITS>(code, out[r]);
     }
   } else {
     lds_barrier();
@@ -388,17 +420,11 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      uint32_t code[16];
 #pragma unroll
-      for (int k = 0; k < WORDS; ++k) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          const int i = k * PER + e;
-          const float code = fminf(fmaxf(rintf(fmaf(zc[i][c], iv[i], MID)), 0.f), (float)LEVELS);
-          word |= (uint32_t)code << (BITS * e);
-        }
-        out[c][k] = word;
-      }
+      for (int i = 0; i < 16; ++i)
+        code[i] = (uint32_t)fminf(fmaxf(rintf(fmaf(zc[i][c], iv[i], MID)), 0.f), (float)LEVELS);
+      pack16<BITS>(code, out[c]);
     }
   }
 
@@ -407,10 +433,7 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
   for (int r = 0; r < 2; ++r) {
     uint8_t* dst = TOKEN_MAJOR ? rec + (size_t)(2 * tp + r) * (D * BITS / 8) + cb * (16 * BITS / 8)
                                : rec + (size_t)(2 * cp + r) * (kGroup * BITS / 8) + tb * (16 * BITS / 8);
-    if constexpr (WORDS == 1)
-      *reinterpret_cast<uint32_t*>(dst) = out[r][0];
-    else
-      *reinterpret_cast<uint2*>(dst) = make_uint2(out[r][0], out[r][1]);
+    store16<BITS>(dst, out[r]);
   }
   if (cb == 0) {
     const uint32_t s2 = (uint32_t)f2h_rne(sc[0]) | ((uint32_t)f2h_rne(sc[1]) << 16);
@@ -552,10 +575,11 @@ static hipError_t launch_tiles_db(int kind, const void* src, void* dst, int64_t 
 
 hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* dst, int64_t stride, float* dbg, int n,
                              int iters, hipStream_t st) {
-  if (D == 128) return bits == 2 ? launch_tiles_db<128, 2>(kind, src, dst, stride, dbg, n, iters, st)
-                                 : launch_tiles_db<128, 4>(kind, src, dst, stride, dbg, n, iters, st);
-  return bits == 2 ? launch_tiles_db<256, 2>(kind, src, dst, stride, dbg, n, iters, st)
-                   : launch_tiles_db<256, 4>(kind, src, dst, stride, dbg, n, iters, st);
+  hipError_t e = hipErrorInvalidValue;
+#define CALL(d, b) e = launch_tiles_db<d, b>(kind, src, dst, stride, dbg, n, iters, st)
+  KVARN_DISPATCH_DB(D, bits, CALL);
+#undef CALL
+  return e;
 }
 
 template <int D, int KB, int VB>
@@ -567,20 +591,6 @@ static void launch_stream_t(const SealStreamArgs& a, int gx, hipStream_t st) {
   hipLaunchKernelGGL((seal_stream_kernel<D, KB, VB>), dim3(gx, 2), dim3(kSealThreadsPerD * D), 0, st, a);
 }
 
-#define KVARN_DISPATCH_DKV(D, KB, VB, CALL)                       \
-  do {                                                            \
-    if (D == 128) {                                               \
-      if (KB == 2 && VB == 2) CALL(128, 2, 2);                    \
-      else if (KB == 2 && VB == 4) CALL(128, 2, 4);               \
-      else if (KB == 4 && VB == 2) CALL(128, 4, 2);               \
-      else CALL(128, 4, 4);                                       \
-    } else {                                                      \
-      if (KB == 2 && VB == 2) CALL(256, 2, 2);                    \
-      else if (KB == 2 && VB == 4) CALL(256, 2, 4);               \
-      else if (KB == 4 && VB == 2) CALL(256, 4, 2);               \
-      else CALL(256, 4, 4);                                       \
-    }                                                             \
-  } while (0)
 
 hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& args, int max_groups_in_batch, int nbh,
                                hipStream_t st) {

@@ -54,7 +54,7 @@ R9  Record = [codes][s: 128 x fp16][c: D x fp16].  K codes token-major (row t
     [b*i, b*i + b) (bit k of the row is bit k mod 8 of byte k div 8).  For
     b = 2, 4, 8 this is code i at bit b*(i mod 32/b) of the 32-bit
     little-endian word floor(i*b/32).
-R14 Widths: b in {2, 3, 4, 5, 6, 8} for K and V independently.  The pages
+R15 Widths: b in {2, 3, 4, 5, 6, 8} for K and V independently.  The pages
     name whole widths from two to eight bits and K/V pairs built from them
     (P2 §5 "Changing Only The Format", §6 "Splitting K And V"); seven bits is
     named by none of them and is left out.
@@ -82,7 +82,7 @@ GROUP = 128          # tokens per sealed group (P2 §2.1)
 SINK = 128           # permanently exact leading tokens (P2 §2.1)
 TAIL_CAP = 128       # region R: the exact in-progress group (P2 §2.1)
 SINKHORN_ITERS = 16  # P2 §1
-WIDTHS = (2, 3, 4, 5, 6, 8)  # code widths in bits (reading R14)
+WIDTHS = (2, 3, 4, 5, 6, 8)  # code widths in bits (reading R15)
 
 
 # --------------------------------------------------------------------------

@@ -33,7 +33,9 @@ def test_record_bytes_match_oracle(d, bits):
 
 
 def test_record_bytes_unsupported():
-    assert K.record_bytes(96, 2) == 0 and K.record_bytes(128, 3) == 0
+    assert K.record_bytes(96, 2) == 0 and K.record_bytes(128, 7) == 0 and K.record_bytes(128, 1) == 0
+    for bits in (3, 5, 6, 8):
+        assert K.record_bytes(128, bits) == O.record_bytes(128, bits)
 
 
 def test_group_and_workspace_bytes():
@@ -45,7 +47,8 @@ def test_group_and_workspace_bytes():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("head_dim", 64, K.EUNSUPPORTED), ("k_bits", 3, K.EUNSUPPORTED), ("v_bits", 8, K.EUNSUPPORTED),
+    ("head_dim", 64, K.EUNSUPPORTED), ("k_bits", 7, K.EUNSUPPORTED), ("v_bits", 1, K.EUNSUPPORTED),
+    ("k_bits", 8, K.EUNSUPPORTED),  # K8 with V2 is not a built pair
     ("group", 64, K.EUNSUPPORTED), ("sink", 0, K.EUNSUPPORTED), ("num_q_heads", 12, K.EINVAL),
     ("num_q_heads", 64, K.EUNSUPPORTED), ("num_kv_heads", 0, K.EINVAL), ("sinkhorn_iters", -1, K.EINVAL),
 ])
@@ -103,7 +106,7 @@ def test_prefill_range_checks():
 def test_tile_entry_points_validate():
     L = K.lib()
     assert L.kvarn_seal_tiles(64, 2, 0, 16, FAKE, FAKE, 4608, None, 1, None) == K.EUNSUPPORTED
-    assert L.kvarn_seal_tiles(128, 3, 0, 16, FAKE, FAKE, 4608, None, 1, None) == K.EUNSUPPORTED
+    assert L.kvarn_seal_tiles(128, 7, 0, 16, FAKE, FAKE, 4608, None, 1, None) == K.EUNSUPPORTED
     assert L.kvarn_seal_tiles(128, 2, 2, 16, FAKE, FAKE, 4608, None, 1, None) == K.EINVAL
     assert L.kvarn_seal_tiles(128, 2, 0, 16, FAKE, FAKE, 4600, None, 1, None) == K.EINVAL
     assert L.kvarn_seal_tiles(128, 2, 0, 99, FAKE, FAKE, 4608, None, 1, None) == K.EINVAL
@@ -130,3 +133,10 @@ def test_append_seal_validates_before_launch():
     # The per-request arrival count shares seq_len with lengths below 2^23.
     assert L.kvarn_append_seal(r(cfg), r(_view(max_groups=(1 << 23) // 128)), FAKE, FAKE, None) == K.ERANGE
     assert "2^23" in L.kvarn_last_error().decode()
+
+
+@pytest.mark.parametrize("kb,vb,ok", [(3, 3, True), (5, 4, True), (6, 5, True), (3, 2, True), (8, 8, True),
+                                      (2, 8, False), (4, 5, False), (5, 6, False), (7, 7, False)])
+def test_width_pairs(kb, vb, ok):
+    cfg = K.make_config(128, 8, 2, kb, vb)
+    assert (K.check_config(cfg) == K.OK) == ok

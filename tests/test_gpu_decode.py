@@ -2,8 +2,8 @@
 
 Decode is checked on caches the oracle built (sink, tail and records encoded
 by the oracle, so independent of the GPU seal), over ragged lengths, GQA
-ratios 1/2/4, head dims 128/256 and 2/4-bit K and V.  Tolerance: 2e-3 max-abs
-on the fp32 output.
+ratios 1/2/4, head dims 128/256 and every built K/V width pair (2 to 8 bits).
+Tolerance: 2e-3 max-abs on the fp32 output.
 """
 import numpy as np
 import pytest
@@ -75,6 +75,10 @@ def test_ragged_lengths_gqa4(lens):
 @pytest.mark.parametrize("d,hq,hkv,kb,vb", [
     (128, 4, 4, 2, 2), (128, 4, 2, 4, 4), (128, 8, 2, 2, 4), (128, 8, 2, 4, 2),
     (256, 4, 2, 4, 2), (256, 4, 1, 2, 2), (256, 2, 2, 4, 4),
+    # widths 3, 5, 6, 8 and the asymmetric presets 3-2, 5-4, 6-5
+    (128, 8, 2, 3, 3), (128, 4, 2, 5, 5), (128, 4, 4, 6, 6), (128, 8, 2, 8, 8),
+    (128, 8, 2, 3, 2), (128, 4, 1, 5, 4), (128, 8, 2, 6, 5),
+    (256, 4, 2, 3, 3), (256, 2, 2, 5, 4), (256, 4, 1, 6, 5), (256, 4, 2, 8, 8),
 ])
 def test_shapes_and_widths(d, hq, hkv, kb, vb):
     err = _run(d, hq, hkv, kb, vb, [700, 389], seed=d + kb * 10 + vb)

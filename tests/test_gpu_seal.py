@@ -28,7 +28,7 @@ def _tiles(d, n, seed):
 
 
 @pytest.mark.parametrize("d", [128, 256])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("kind", ["k", "v"])
 def test_seal_tiles_parity(d, bits, kind):
     x = _tiles(d, 9, seed=d + bits + (kind == "v"))
