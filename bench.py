@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--workload", default="llama31_8b_32k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seal-groups", type=int, default=48)
+    ap.add_argument("--other-workloads", default="qwen3_4b_16k_b16,phi4_14b_32k_b8,longctx_d256_64k_b4",
+                    help="comma-separated workloads measured after the headline one and reported under "
+                         "'workloads' (empty: none)")
+    ap.add_argument("--other-steps", type=int, default=256, help="decode steps timed per other workload")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run this many eager steps only (for rocprofv3) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -255,6 +259,96 @@ def _enc(out, bits, kind):
     return dict(codes=out["codes"], s16=out["s16"], c16=out["c16"], bits=bits, kind=kind)
 
 
+def measure_workload(torch, K, synth, dev, name, steps, hbm_target_bytes=768 * 2**20):
+    """Decode step (append + seal-if-due + decode attention) and bulk seal of
+    one more workload, measured like the headline one: K/V drawn on the device
+    with the synthetic recipe, enough layer caches (at least 2) to exceed
+    `hbm_target_bytes` so steps read HBM rather than the Infinity Cache, a HIP
+    graph of `steps` steps rotating over them, then HIP-event timing of the
+    split kernel alone."""
+    wl = synth.WORKLOADS[name]
+    B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens0 = [wl.start_len(b) for b in range(B)]
+    k_rec, v_rec = K.record_bytes(d, wl.k_bits), K.record_bytes(d, wl.v_bits)
+    bytes_launch = algorithmic_decode_bytes(wl, lens0, k_rec, v_rec)
+    ncopy = max(2, -(-hbm_target_bytes // bytes_launch))
+    tokens = max(1, -(-steps // ncopy))
+    lmax = max(lens0) + tokens
+    max_groups = (lmax - 128) // 128 + 1
+    kd, vd = synth.kv_streams_device(wl, lmax, dev)
+    idx = torch.tensor([[n + t for n in lens0] for t in range(tokens)], device=dev)   # [T][B]
+    ar = torch.arange(B, device=dev)
+    new_k = torch.stack([kd[ar, :, idx[t]] for t in range(tokens)]).contiguous()      # [T][B][Hkv][D]
+    new_v = torch.stack([vd[ar, :, idx[t]] for t in range(tokens)]).contiguous()
+    q_all = torch.from_numpy(np.stack([synth.queries(wl, b, tokens) for b in range(B)], axis=1)).to(dev)
+    cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
+    caches = [K.KVarNCache(cfg, B, max_groups, device=dev) for _ in range(ncopy)]
+    for c in caches:
+        c.prefill(kd, vd, lens0)
+    torch.cuda.synchronize()
+    # bulk seal, timed on cache 0
+    n_groups_seal = sum(hkv * ((n - 128) // 128) for n in lens0 if n > 128)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    caches[0].prefill(kd, vd, lens0)
+    e1.record()
+    torch.cuda.synchronize()
+    t_prefill = e0.elapsed_time(e1) / 1e3
+    del kd, vd
+    seq0 = caches[0].seq_len.clone()
+    outs = [torch.empty(B, hq, d, dtype=torch.float32, device=dev) for _ in range(ncopy)]
+
+    def reset():
+        for c in caches:
+            c.seq_len.copy_(seq0)
+
+    stream = torch.cuda.Stream()
+
+    def timed_graph(fn, n):
+        reset()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(n):
+                fn(r)
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        reset()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    def step(s):
+        c = caches[s % ncopy]
+        t = s // ncopy
+        c.append_seal(new_k[t], new_v[t])
+        c.decode_attn(q_all[t], out=outs[s % ncopy])
+
+    t_step = timed_graph(step, tokens * ncopy)
+    t_split = timed_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]), 4 * ncopy)
+    achieved = bytes_launch / t_split
+    seal_bytes_per_group = 2 * 128 * d * 2 + k_rec + v_rec
+    out = {
+        "tokens_per_s": B / t_step, "ms_per_step": t_step * 1e3,
+        "config": {"batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "context": lens0[0],
+                   "context_stagger": wl.stagger, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
+                   "layer_caches": ncopy, "steps": tokens * ncopy},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "kernel": "decode_split_kernel",
+                     "bytes_per_launch": bytes_launch, "us_per_launch": t_split * 1e6},
+        "seal": {"groups_per_s": n_groups_seal / t_prefill,
+                 "hbm_frac": n_groups_seal * seal_bytes_per_group / t_prefill / HBM_PEAK},
+    }
+    del caches, outs, new_k, new_v, q_all
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -434,6 +528,15 @@ def main():
           f"({achieved / HBM_PEAK * 100:.1f}% of HBM); combine {t_combine * 1e6:.2f} us; "
           f"step {t_total / args.steps * 1e6:.2f} us", file=sys.stderr, flush=True)
 
+    others = {}
+    for name in [x for x in args.other_workloads.split(",") if x and x != wl.name]:
+        others[name] = measure_workload(torch, K, synth, dev, name, args.other_steps)
+        o = others[name]
+        print(f"[bench] {name}: {o['tokens_per_s']:.0f} tokens/s, step {o['ms_per_step'] * 1e3:.1f} us, split "
+              f"{o['roofline']['us_per_launch']:.1f} us = {o['roofline']['achieved']:.0f} GB/s "
+              f"({o['roofline']['frac'] * 100:.1f}% of HBM); seal {o['seal']['groups_per_s'] / 1e6:.2f} M groups/s",
+              file=sys.stderr, flush=True)
+
     line = {
         "metric": "quantized decode-attn tokens/s + % HBM peak; seal_group groups/s (1 MI355X)",
         "value": value,
@@ -455,6 +558,7 @@ def main():
                      "kernel": "decode_split_kernel", "bytes_per_launch": bytes_launch,
                      "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6},
         "seal": seal,
+        "workloads": others,
     }
     line["cpu_baseline"] = cpu_line
     print(json.dumps(line))
