@@ -733,18 +733,26 @@ union DecodeSmemU {
   ExactSmem<D, GQ> ex;
 };
 
+// 1-D grid: the exact workgroups of every pair first (n_exact_splits per
+// pair), then the record workgroups, pair-major.  Only the record workgroups
+// are sized to be resident together; the short exact ones are dispatched
+// first and the record workgroups that do not fit start as they retire.
 template <int D, int KB, int VB, int GQ>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecodeSmemU<D, KB, VB, GQ> sm;
-  // The exact splits (workgroups 0 and 1) go first in dispatch order; their
-  // partials follow the record splits' in the workspace.
   const int nex = a.nsplit - a.n_rec_splits;
-  const int bx = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int n = a.c.seq_len[b];
-  if (bx >= nex)
-    record_split<D, KB, VB, GQ>(sm.rec, a, b, kvh, bx - nex, n);
-  else
-    exact_split<D, GQ>(sm.ex, a, b, kvh, bx, a.n_rec_splits + bx, n);
+  const int npair = a.c.batch * a.c.hkv;
+  const int bx = blockIdx.x;
+  if (bx < nex * npair) {
+    const int pair = bx / nex, es = bx - pair * nex;
+    const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
+    exact_split<D, GQ>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b]);
+  } else {
+    const int r = bx - nex * npair;
+    const int pair = r / a.n_rec_splits, split = r - pair * a.n_rec_splits;
+    const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
+    record_split<D, KB, VB, GQ>(sm.rec, a, b, kvh, split, a.c.seq_len[b]);
+  }
 }
 
 // One workgroup (256 threads) per (query head, request): log-sum-exp merge of
@@ -879,9 +887,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs) {
   DecodePlan p;
   // Each record workgroup is four independent waves walking consecutive runs
-  // of groups_per_wave groups of one (request, KV head).  The whole grid
-  // (record and exact workgroups) should be resident at once, so the smallest
-  // run length whose grid fits `resident_wgs` maximises parallelism.
+  // of groups_per_wave groups of one (request, KV head).  The record
+  // workgroups should be resident at once, so the smallest run length whose
+  // record grid fits `resident_wgs` maximises parallelism; the exact
+  // workgroups (short, dispatched first) are not counted.
   const int64_t pairs = (int64_t)batch * hkv;
   const int64_t target = resident_wgs;
   p.n_exact_splits = 2;  // exact tokens [0,128) and [128,256)
@@ -889,7 +898,7 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int re
   if (max_groups > 0) {
     while (4 * gpw < max_groups) {
       const int64_t splits = (max_groups + 4 * gpw - 1) / (4 * gpw);
-      if (pairs * (splits + p.n_exact_splits) <= target) break;
+      if (pairs * splits <= target) break;
       ++gpw;
     }
   }
@@ -938,7 +947,7 @@ int decode_resident_wgs(int D, int kb, int vb, int gq) {
 template <int D, int KB, int VB, int GQ>
 static void launch_t(const DecodeArgs& a, int phases, hipStream_t st) {
   if (phases & 1)
-    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, GQ>), dim3(a.nsplit, a.c.hkv, a.c.batch), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, GQ>), dim3(a.nsplit * a.c.hkv * a.c.batch), dim3(256), 0, st,
                        a);
   if (phases & 2) hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.hq, a.c.batch), dim3(256), 0, st, a);
 }
