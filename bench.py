@@ -441,6 +441,29 @@ def main():
     print(f"[bench] seal: {seal['groups_per_s'] / 1e6:.2f} M groups/s ({seal['hbm_frac'] * 100:.1f}% of HBM)",
           file=sys.stderr, flush=True)
 
+    # ---- record -> fp16 conversion of every record slot of layer 0, timed ----
+    gb = k_rec + v_rec
+    slots = cache0.records.view(torch.uint8).reshape(-1, gb)
+    dq_out = torch.empty(slots.shape[0], 128, d, dtype=torch.float16, device=dev)
+    for kind, lo, bits in (("k", 0, wl.k_bits), ("v", k_rec, wl.v_bits)):
+        K.dequant_records(slots[:, lo:], d, bits, kind, out=dq_out)
+    torch.cuda.synchronize()
+    dq_reps = 5
+    e0.record()
+    for _ in range(dq_reps):
+        for kind, lo, bits in (("k", 0, wl.k_bits), ("v", k_rec, wl.v_bits)):
+            K.dequant_records(slots[:, lo:], d, bits, kind, out=dq_out)
+    e1.record()
+    torch.cuda.synchronize()
+    t_dq = e0.elapsed_time(e1) / 1e3 / dq_reps
+    dq_bytes = slots.shape[0] * (k_rec + v_rec + 2 * 128 * d * 2)   # records in, fp16 tiles out
+    dequant = {"records_per_s": 2 * slots.shape[0] / t_dq, "us_per_call": t_dq * 1e6 / 2,
+               "hbm_GBps": dq_bytes / t_dq / 1e9, "hbm_frac": dq_bytes / t_dq / HBM_PEAK,
+               "note": f"kvarn_dequant_records over all {slots.shape[0]} record slots, K then V"}
+    del dq_out
+    print(f"[bench] record -> fp16: {dequant['hbm_GBps']:.0f} GB/s ({dequant['hbm_frac'] * 100:.1f}% of HBM)",
+          file=sys.stderr, flush=True)
+
     # ---- layer caches ----------------------------------------------------
     caches = [cache0]
     for c in range(1, ncopy):
@@ -558,6 +581,7 @@ def main():
                      "kernel": "decode_split_kernel", "bytes_per_launch": bytes_launch,
                      "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6},
         "seal": seal,
+        "dequant": dequant,
         "workloads": others,
     }
     line["cpu_baseline"] = cpu_line

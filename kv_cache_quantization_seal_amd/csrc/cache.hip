@@ -75,45 +75,77 @@ __global__ __launch_bounds__(256) void prefill_copy_kernel(CacheArgs c, const ui
   if (h == 0 && threadIdx.x == 0) c.seq_len[b] = len;
 }
 
-// Record -> fp16 original-frame rows.  Thread (t, rb) rebuilds channels
-// [64 rb, 64 rb + 64) of token t: s_t (code - mid) c_j, then H_D / sqrt(D).
+// Record -> fp16 original-frame rows.  The record is staged in LDS with
+// 16-byte loads; thread (token t, 32-channel block bl), NB = D/32 threads per
+// token, rebuilds s_t (code - mid) c_j for its 32 channels, rotates by
+// H_D / sqrt(D) (butterflies over the five low channel bits in registers,
+// over the block bits across neighbouring lanes), and writes its 64 bytes.
+// A row of codes is a little-endian bit stream: code i occupies bits
+// [BITS i, BITS i + BITS).
+template <int M>
+__device__ __forceinline__ float dq_pair(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true));
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true));
+  else {
+    const int o = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);  // lanes 0-3 <- 4-7
+    return __int_as_float(__builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false));  // 4-7 <- 0-3
+  }
+}
+
 template <int D, int BITS, int KIND>
-__global__ __launch_bounds__(2 * D) void dequant_kernel(const uint8_t* __restrict__ src, int64_t src_stride,
+__global__ __launch_bounds__(4 * D) void dequant_kernel(const uint8_t* __restrict__ src, int64_t src_stride,
                                                         __half* __restrict__ dst) {
-  constexpr int NB = D / 64;
-  constexpr int P = D + 4;
+  constexpr int NB = D / 32;
   constexpr int CODE_BYTES = kGroup * D * BITS / 8;
+  constexpr int REC = CODE_BYTES + 2 * kGroup + 2 * D;  // a multiple of 16
   constexpr float MID = 0.5f * ((1 << BITS) - 1);
-  __shared__ float xs[NB > 1 ? kGroup * P : 1];
+  constexpr int ROWBITS = (KIND == 0 ? D : kGroup) * BITS;
+  __shared__ uint32_t rs_[REC / 4];
   const uint8_t* rec = src + blockIdx.x * src_stride;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rb = w % NB;
-  const int t = 64 * (w / NB) + lane;
-  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(rec + CODE_BYTES);
+  for (int i = threadIdx.x; i < REC / 16; i += blockDim.x)
+    reinterpret_cast<uint4*>(rs_)[i] = reinterpret_cast<const uint4*>(rec)[i];
+  __syncthreads();
+  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(rs_) + CODE_BYTES / 2;
   const uint16_t* c16 = s16 + kGroup;
+  const int t = threadIdx.x / NB, bl = threadIdx.x % NB;
   const float st = h2f(s16[t]);
-  float x[64];
+  float x[32];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const int j = 64 * rb + i;
-    uint32_t code;
-    // A row is a little-endian bit stream: code idx occupies bits
-    // [BITS idx, BITS idx + BITS); rows are 4-byte aligned.
-    const uint8_t* row = KIND == 0 ? rec + (size_t)t * (D * BITS / 8)           // token-major: code j of row t
-                                   : rec + (size_t)j * (kGroup * BITS / 8);     // channel-major: code t of row j
-    const int idx = KIND == 0 ? j : t;
-    const int bit = BITS * idx;
-    const uint32_t* wp = reinterpret_cast<const uint32_t*>(row) + bit / 32;
-    uint64_t pair = wp[0];
-    if (bit % 32 + BITS > 32) pair |= (uint64_t)wp[1] << 32;
-    code = (uint32_t)(pair >> (bit % 32)) & ((1u << BITS) - 1);
+  for (int i = 0; i < 32; ++i) {
+    const int j = 32 * bl + i;
+    const int bit = (KIND == 0 ? t : j) * ROWBITS + BITS * (KIND == 0 ? j : t);
+    uint64_t pair = rs_[bit / 32];
+    if (bit % 32 + BITS > 32) pair |= (uint64_t)rs_[bit / 32 + 1] << 32;
+    const uint32_t code = (uint32_t)(pair >> (bit % 32)) & ((1u << BITS) - 1);
     x[i] = st * ((float)code - MID) * h2f(c16[j]);
   }
-  rotate_row_slice<D, P>(x, xs, t, rb);
-  const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
-  uint4* out = reinterpret_cast<uint4*>(dst + ((int64_t)blockIdx.x * kGroup + t) * D + 64 * rb);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int s = 1; s < 32; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & s)) {
+        const float a0 = x[i], a1 = x[i + s];
+        x[i] = a0 + a1;
+        x[i + s] = a0 - a1;
+      }
+    }
+  }
+  // Block bits: the lane with the bit set keeps x - x' negated (x + s x',
+  // s = -1); the negations commute with later stages and the final sign
+  // undoes them.
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fmaf((bl & 1) ? -1.0f : 1.0f, dq_pair<1>(x[i]), x[i]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fmaf((bl & 2) ? -1.0f : 1.0f, dq_pair<2>(x[i]), x[i]);
+  if constexpr (NB == 8) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = fmaf((bl & 4) ? -1.0f : 1.0f, dq_pair<4>(x[i]), x[i]);
+  }
+  const float rs = ((D == 128) ? 0.08838834764831845f : 0.0625f) * ((__popc(bl) & 1) ? -1.0f : 1.0f);
+  uint4* out = reinterpret_cast<uint4*>(dst + ((int64_t)blockIdx.x * kGroup + t) * D + 32 * bl);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
     uint32_t wd[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -144,10 +176,10 @@ hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const v
 template <int D, int BITS>
 static void launch_dq(int kind, const void* src, int64_t stride, void* dst, int n, hipStream_t st) {
   if (kind == 0)
-    hipLaunchKernelGGL((dequant_kernel<D, BITS, 0>), dim3(n), dim3(2 * D), 0, st, (const uint8_t*)src, stride,
+    hipLaunchKernelGGL((dequant_kernel<D, BITS, 0>), dim3(n), dim3(4 * D), 0, st, (const uint8_t*)src, stride,
                        (__half*)dst);
   else
-    hipLaunchKernelGGL((dequant_kernel<D, BITS, 1>), dim3(n), dim3(2 * D), 0, st, (const uint8_t*)src, stride,
+    hipLaunchKernelGGL((dequant_kernel<D, BITS, 1>), dim3(n), dim3(4 * D), 0, st, (const uint8_t*)src, stride,
                        (__half*)dst);
 }
 

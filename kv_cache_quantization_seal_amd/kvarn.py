@@ -217,10 +217,15 @@ def seal_tiles(src: torch.Tensor, bits: int, kind: str, out: Optional[torch.Tens
 
 def dequant_records(recs: torch.Tensor, head_dim: int, bits: int, kind: str, out: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
-    """Records uint8 [n][>= record_bytes] -> fp16 [n][128][D], original frame."""
+    """Records uint8 [n][>= record_bytes] -> fp16 [n][128][D], original frame.
+
+    Rows may be strided (a view into a cache's record slots): each row must be
+    contiguous and the row stride a multiple of 16 bytes."""
     n = recs.shape[0]
     if out is None:
         out = torch.empty(n, GROUP, head_dim, dtype=torch.float16, device=recs.device)
-    _check(lib().kvarn_dequant_records(head_dim, bits, 0 if kind == "k" else 1, _ptr(recs), recs.stride(0),
-                                       _ptr(out), n, _stream(stream)))
+    if recs.dim() != 2 or recs.dtype != torch.uint8 or recs.stride(1) != 1:
+        raise ValueError("recs must be a uint8 [n][bytes] tensor with contiguous rows")
+    _check(lib().kvarn_dequant_records(head_dim, bits, 0 if kind == "k" else 1, ctypes.c_void_p(recs.data_ptr()),
+                                       recs.stride(0), _ptr(out), n, _stream(stream)))
     return out
