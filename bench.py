@@ -551,6 +551,32 @@ def main():
           f"({achieved / HBM_PEAK * 100:.1f}% of HBM); combine {t_combine * 1e6:.2f} us; "
           f"step {t_total / args.steps * 1e6:.2f} us", file=sys.stderr, flush=True)
 
+    # ---- the same split kernel over paged records: every layer cache's
+    # records moved to a shuffled block table over a pool with spare blocks.
+    nblk = B * max_groups + 64
+    perm = torch.from_numpy(np.random.default_rng(11).permutation(nblk)[:B * max_groups].astype(np.int32)).to(dev)
+    reset()
+    paged = []
+    for c in caches:
+        pc = K.KVarNCache(cfg, B, max_groups, device=dev, num_blocks=nblk)
+        pc.block_table.copy_(perm.view(B, max_groups))
+        src = c.records.view(B, hkv, max_groups, gb).permute(0, 2, 1, 3).reshape(B * max_groups, hkv, gb)
+        pc.records.view(nblk, hkv, gb)[perm.long()] = src
+        for name in ("sink_k", "sink_v", "tail_k", "tail_v", "seq_len"):
+            getattr(pc, name).copy_(getattr(c, name))
+        paged.append(pc)
+    torch.cuda.synchronize()
+    pdiff = (paged[0].decode_attn(q_all[0]) - caches[0].decode_attn(q_all[0])).abs().max().item()
+    if not pdiff <= 1e-5:
+        raise RuntimeError(f"paged decode differs from the contiguous one by {pdiff}")
+    t_paged = time_graph(lambda r: paged[r % ncopy].decode_partial(q_all[0]))
+    paged_line = {"us_per_launch": t_paged * 1e6, "GBps": bytes_launch / t_paged / 1e9,
+                  "frac": bytes_launch / t_paged / HBM_PEAK,
+                  "note": f"decode split kernel, records behind a shuffled block table over {nblk} blocks"}
+    del paged
+    print(f"[bench] paged records: split kernel {t_paged * 1e6:.2f} us/launch "
+          f"({paged_line['frac'] * 100:.1f}% of HBM)", file=sys.stderr, flush=True)
+
     others = {}
     for name in [x for x in args.other_workloads.split(",") if x and x != wl.name]:
         others[name] = measure_workload(torch, K, synth, dev, name, args.other_steps)
@@ -582,6 +608,7 @@ def main():
                      "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6},
         "seal": seal,
         "dequant": dequant,
+        "paged": paged_line,
         "workloads": others,
     }
     line["cpu_baseline"] = cpu_line

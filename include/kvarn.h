@@ -79,21 +79,35 @@ typedef struct {
 
 /*
  * Cache view (pointers only).  Element (b, h, i, d) of an fp16 block is at
- * index ((b*Hkv + h)*128 + i)*D + d.  Record g of (b, h) starts at byte
- * ((b*Hkv + h)*max_groups + g) * kvarn_group_bytes(cfg): the K record first,
- * then the V record.  seq_len[b] = tokens cached for request b.  Positions
- * [0,128) live in the sink, group g covers positions [128+128g, 256+128g),
- * and the tail holds positions [128+128*G, n) with G = max(0,(n-128)/128)
- * sealed groups [P2 §2.1].  The cache holds at most
+ * index ((b*Hkv + h)*128 + i)*D + d.  seq_len[b] = tokens cached for
+ * request b.  Positions [0,128) live in the sink, group g covers positions
+ * [128+128g, 256+128g), and the tail holds positions [128+128*G, n) with
+ * G = max(0,(n-128)/128) sealed groups [P2 §2.1].  The cache holds at most
  * 128 + 128*max_groups + 127 tokens per request.
+ *
+ * Records.  Each (request b, KV head h, group g) owns one pair of
+ * kvarn_group_bytes(cfg) bytes: the K record first, then the V record.
+ *   - Contiguous (block_table NULL): pair (b*Hkv + h)*max_groups + g of
+ *     `records`, which holds batch*Hkv*max_groups pairs.
+ *   - Paged (block_table non-NULL): `records` is a pool of num_blocks blocks,
+ *     a block being the Hkv pairs of one 128-token group, and group g of
+ *     request b lives in block block_table[b*max_groups + g] (device int32
+ *     [batch][max_groups]): pair block*Hkv + h.  This is the block table of
+ *     a paged KV cache with 128-token blocks, which lets requests share one
+ *     pool and grow without copying.  An entry outside [0, num_blocks) gives
+ *     the group no storage: sealing skips it and decoding treats it as
+ *     absent (an empty group), so a bad entry never addresses memory outside
+ *     the pool.  Entries for groups not yet sealed are not read by decoding.
  */
 typedef struct {
   void *sink_k, *sink_v; /* device fp16 [batch][Hkv][128][D] */
   void *tail_k, *tail_v; /* device fp16 [batch][Hkv][128][D] */
-  void *records;         /* device, batch*Hkv*max_groups*kvarn_group_bytes(cfg) bytes */
+  void *records;         /* device record pairs (see above) */
   int32_t *seq_len;      /* device int32 [batch] */
   int32_t batch;
-  int32_t max_groups;
+  int32_t max_groups;            /* groups per request (table row length when paged) */
+  const int32_t *block_table;    /* NULL (contiguous) or device int32 [batch][max_groups] */
+  int32_t num_blocks;            /* blocks in the pool when paged; ignored otherwise */
 } kvarn_cache;
 
 /* Pure host helpers (no GPU needed). ---------------------------------- */

@@ -233,6 +233,7 @@ struct Stage {
   uint32_t sk[4], sv[4];
   uint32_t ck[Gm::QB / 2];
   uint32_t cv[Gm::NCT / 2];
+  bool live;  // the K part came from a stored group (else it reads as zeros)
 };
 
 // N dwords at byte offset `off` of a buffer: 16-byte loads when N is a
@@ -264,7 +265,7 @@ __device__ __forceinline__ float half_of(const uint32_t* w, int i) {
   return h2f((uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu)));
 }
 
-template <int D, int KB, int VB, int GQ>
+template <int D, int KB, int VB, int GQ, bool PAGED>
 __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, int b, int kvh, int split,
                              int nseq) {
   using Gm = RecGeom<D, KB, VB>;
@@ -291,7 +292,6 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   const bool arow_valid = hm < GQ && im < 3;
   WaveLds<D, GQ>& wv = sm.wv[w];
 
-  const uint8_t* recs = a.c.records + (((int64_t)b * a.c.hkv + kvh) * a.c.max_groups) * a.c.group_bytes;
   const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
   const int gw0 = split * a.groups_per_split + w * a.groups_per_wave;
   const int ga = min(gw0, n_groups);
@@ -317,19 +317,32 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   const int vbase = Gm::KREC + NCT * n * Gm::VROW + G * Gm::LBV;
   auto vofs = [&](int ct) { return vbase + ct * Gm::VROW; };
 
-  // Wave-uniform buffer range of group g; an unused range is empty, so its
+  // Byte offset of group g's record pair, or -1 for a group past the wave's
+  // range or with no storage.  Wave-uniform: a paged cache's block table is
+  // read with a scalar load (its own counter, so waiting for it never waits
+  // for the record loads in flight).
+  const int64_t pair_base = (((int64_t)b * a.c.hkv + kvh) * a.c.max_groups) * a.c.group_bytes;
+  auto group_off = [&](int g, bool on) -> int64_t {
+    if (!on) return -1;
+    if constexpr (!PAGED) return pair_base + (int64_t)g * a.c.group_bytes;
+    typedef const __attribute__((address_space(4))) int32_t ConstI32;
+    const int blk = *(ConstI32*)(a.c.map.table + (int64_t)b * a.c.max_groups + g);
+    return (blk >= 0 && blk < a.c.map.num_blocks) ? ((int64_t)blk * a.c.hkv + kvh) * a.c.group_bytes : -1;
+  };
+  // Wave-uniform buffer range of a group; an unused range is empty, so its
   // loads return zero without touching memory and every path issues the
   // same loads.
-  auto rsrc_of = [&](int g, bool on) {
-    const uint64_t addr = reinterpret_cast<uint64_t>(recs + (int64_t)(on ? g : 0) * a.c.group_bytes);
+  auto rsrc_at = [&](int64_t off) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(a.c.records + (off >= 0 ? off : 0));
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
-    const int bytes = __builtin_amdgcn_readfirstlane(on ? Gm::GB : 0);
+    const int bytes = __builtin_amdgcn_readfirstlane(off >= 0 ? Gm::GB : 0);
     return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), bytes);
   };
   // K part (c^K first: it is needed first), V part (s^V first).
-  auto load_k = [&](St& S, int g, bool on) {
-    const __amdgpu_buffer_rsrc_t r = rsrc_of(g, on);
+  auto load_k = [&](St& S, int64_t off) {
+    S.live = off >= 0;
+    const __amdgpu_buffer_rsrc_t r = rsrc_at(off);
     if constexpr (QB == 8 && KB == 2) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) S.ck[k] = __builtin_amdgcn_raw_buffer_load_b32(r, ckofs + 8 * k, 0, 0);
@@ -345,8 +358,8 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 #pragma unroll
     for (int nt = 0; nt < NTT; ++nt) load_dw(S.k[nt], r, kofs(nt));
   };
-  auto load_v = [&](St& S, int g, bool on) {
-    const __amdgpu_buffer_rsrc_t r = rsrc_of(g, on);
+  auto load_v = [&](St& S, int64_t off) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_at(off);
     if constexpr (VB != 2) {
       load_dw(S.sv, r, svofs);
     } else {
@@ -365,8 +378,9 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   load_dw_global<QB / 2>(qw, a.q + (((int64_t)b * a.hq + kvh * GQ + (qvalid ? hq : 0)) * D + QB * j));
   __builtin_amdgcn_sched_barrier(0);
   St SA;
-  load_k(SA, ga, ga < gb);
-  load_v(SA, ga, ga < gb);
+  const int64_t off0 = group_off(ga, ga < gb);
+  load_k(SA, off0);
+  load_v(SA, off0);
   __builtin_amdgcn_sched_barrier(0);
 
   // q~ producer values (scaled query in the log2 domain, rotated), per wave.
@@ -385,7 +399,8 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   // as soon as it has been consumed (K part after QK, V part after PV), so
   // the next group's loads overlap most of this group's work.
   auto process = [&](St& S, int gn) {
-    const bool on = gn < gb;
+    const int64_t offn = group_off(gn, gn < gb);  // issued early: used after QK
+    const bool live = !PAGED || S.live;  // this group is stored (a paged table may leave it out)
     // q~ limbs of head hq with E = max |q~| over the head's channels (one
     // DPP row per head).
     float y[QB];
@@ -450,10 +465,10 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[s], unpack_block<KB>(S.k[nt], s), acc, 0, 0, 0);
       const uint32_t x = ((uint32_t)acc[0] << 14) + ((uint32_t)acc[1] << 7) + (uint32_t)acc[2];
       const int yv = (int)((x << 1) + negls);
-      logit[nt] = hvalid ? (float)yv * (half_of(S.sk, shalf(nt)) * kscale) : -INFINITY;
+      logit[nt] = (hvalid && live) ? (float)yv * (half_of(S.sk, shalf(nt)) * kscale) : -INFINITY;
       lmax = fmaxf(lmax, logit[nt]);
     }
-    load_k(S, gn, on);
+    load_k(S, offn);
 
     // Softmax update; w = p * s^V with its exact per-head maximum W.
     const float gmax = row16_max(lmax);
@@ -464,7 +479,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
     float psum = 0.f, wm = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NTT; ++nt) {
-      const float p = hvalid ? __builtin_amdgcn_exp2f(logit[nt] - m_new) : 0.f;
+      const float p = (hvalid && live) ? __builtin_amdgcn_exp2f(logit[nt] - m_new) : 0.f;
       psum += p;
       wv_[nt] = p * half_of(S.sv, shalf(nt));
       wm = fmaxf(wm, wv_[nt]);
@@ -522,7 +537,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
       const int yv = (int)((x << 1) + neglt);
       o_acc[ct] = fmaf((float)yv * vscale, half_of(S.cv, ct), o_acc[ct]);
     }
-    load_v(S, gn, on);
+    load_v(S, offn);
     wave_sync();  // this group's limbs have been read before the next group writes
   };
 
@@ -737,7 +752,7 @@ union DecodeSmemU {
 // pair), then the record workgroups, pair-major.  Only the record workgroups
 // are sized to be resident together; the short exact ones are dispatched
 // first and the record workgroups that do not fit start as they retire.
-template <int D, int KB, int VB, int GQ>
+template <int D, int KB, int VB, int GQ, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecodeSmemU<D, KB, VB, GQ> sm;
   const int nex = a.nsplit - a.n_rec_splits;
@@ -751,7 +766,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int r = bx - nex * npair;
     const int pair = r / a.n_rec_splits, split = r - pair * a.n_rec_splits;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
-    record_split<D, KB, VB, GQ>(sm.rec, a, b, kvh, split, a.c.seq_len[b]);
+    record_split<D, KB, VB, GQ, PAGED>(sm.rec, a, b, kvh, split, a.c.seq_len[b]);
   }
 }
 
@@ -914,12 +929,15 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int re
 
 template <int D, int KB, int VB, int GQ>
 static int resident_t(int dev) {
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, KB, VB, GQ>, 256, 0) !=
+  // The smaller of the contiguous and the paged instances.
+  int per_cu = 0, per_cu_paged = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, KB, VB, GQ, false>, 256, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_paged, decode_split_kernel<D, KB, VB, GQ, true>, 256, 0) !=
           hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  return per_cu * cus;
+  return std::min(per_cu, per_cu_paged) * cus;
 }
 
 template <int D, int KB, int VB>
@@ -946,9 +964,14 @@ int decode_resident_wgs(int D, int kb, int vb, int gq) {
 
 template <int D, int KB, int VB, int GQ>
 static void launch_t(const DecodeArgs& a, int phases, hipStream_t st) {
-  if (phases & 1)
-    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, GQ>), dim3(a.nsplit * a.c.hkv * a.c.batch), dim3(256), 0, st,
-                       a);
+  if (phases & 1) {
+    if (a.c.map.table)
+      hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, GQ, true>), dim3(a.nsplit * a.c.hkv * a.c.batch), dim3(256),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, GQ, false>), dim3(a.nsplit * a.c.hkv * a.c.batch), dim3(256),
+                         0, st, a);
+  }
   if (phases & 2) hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.hq, a.c.batch), dim3(256), 0, st, a);
 }
 

@@ -53,6 +53,27 @@ constexpr int width_index(int b) { return b == 8 ? 5 : b - 2; }
     }                                                                                 \
   } while (0)
 
+// Where a cache's records live.  Contiguous (table NULL): the (K record,
+// V record) pair of (request b, KV head h, group g) is pair number
+// (b Hkv + h) max_groups + g of the records buffer.  Paged (the block table
+// of a paged KV cache, one block per 128-token group holding the Hkv pairs of
+// that group): pair number table[b max_groups + g] Hkv + h of a pool of
+// num_blocks blocks.  A table entry outside [0, num_blocks) gives the group
+// no storage: it is not written, and decoding treats it as absent.
+struct RecordMap {
+  const int32_t* table;
+  int32_t num_blocks;
+};
+
+// Byte offset of the record pair of (b, h, g), or -1 if it has no storage.
+__device__ __forceinline__ int64_t pair_offset(const RecordMap& m, int b, int h, int g, int hkv, int max_groups,
+                                               int64_t group_bytes) {
+  if (!m.table) return (((int64_t)b * hkv + h) * max_groups + g) * group_bytes;
+  const int blk = m.table[(int64_t)b * max_groups + g];
+  if (blk < 0 || blk >= m.num_blocks) return -1;
+  return ((int64_t)blk * hkv + h) * group_bytes;
+}
+
 struct PrefillLens {
   int32_t len[kMaxPrefillBatch];
 };
@@ -62,6 +83,7 @@ struct SealPrefillArgs {
   const __half* v;
   int64_t src_tokens;
   uint8_t* records;
+  RecordMap map;
   int64_t group_bytes;
   int rec_k_bytes;
   int hkv;
@@ -79,6 +101,7 @@ struct SealStreamArgs {
   const __half* tail_v;
   const int32_t* seq_len;
   uint8_t* records;
+  RecordMap map;
   int64_t group_bytes;
   int rec_k_bytes;
   int hkv;
@@ -100,6 +123,7 @@ struct AppendSealArgs {
   const __half* v_new;
   uint8_t* records;
   int32_t* seq_len;
+  RecordMap map;
   int64_t group_bytes;
   int rec_k_bytes;
   int hkv;
@@ -114,6 +138,7 @@ struct CacheArgs {
   __half* tail_k;
   __half* tail_v;
   const uint8_t* records;
+  RecordMap map;
   int32_t* seq_len;
   int batch;
   int hkv;

@@ -66,11 +66,23 @@ kvarn_status check_cache(const kvarn_config* c, const kvarn_cache* k) {
   if (!k->sink_k || !k->sink_v || !k->tail_k || !k->tail_v || !k->seq_len)
     return fail(KVARN_EINVAL, "cache sink/tail/seq_len pointers must be non-NULL");
   if (k->max_groups > 0 && !k->records) return fail(KVARN_EINVAL, "cache records is NULL");
+  if (k->block_table) {
+    if (k->num_blocks <= 0)
+      return fail(KVARN_EINVAL, "a paged cache needs num_blocks > 0 (got %d)", k->num_blocks);
+    if (!aligned(k->block_table, 4)) return fail(KVARN_EINVAL, "cache block_table must be 4-byte aligned");
+  }
   if (!aligned(k->sink_k, 16) || !aligned(k->sink_v, 16) || !aligned(k->tail_k, 16) || !aligned(k->tail_v, 16) ||
       !aligned(k->records, 16) || !aligned(k->seq_len, 4))
     return fail(KVARN_EINVAL, "cache buffers must be 16-byte aligned");
   (void)c;
   return KVARN_OK;
+}
+
+kvarn::RecordMap record_map(const kvarn_cache* k) {
+  kvarn::RecordMap m;
+  m.table = k->block_table;
+  m.num_blocks = k->block_table ? k->num_blocks : 0;
+  return m;
 }
 
 kvarn::CacheArgs cache_args(const kvarn_config* c, const kvarn_cache* k) {
@@ -80,6 +92,7 @@ kvarn::CacheArgs cache_args(const kvarn_config* c, const kvarn_cache* k) {
   a.tail_k = (__half*)k->tail_k;
   a.tail_v = (__half*)k->tail_v;
   a.records = (const uint8_t*)k->records;
+  a.map = record_map(k);
   a.seq_len = k->seq_len;
   a.batch = k->batch;
   a.hkv = c->num_kv_heads;
@@ -172,6 +185,7 @@ kvarn_status kvarn_append_seal(const kvarn_config* cfg, const kvarn_cache* cache
   a.k_new = (const __half*)k_new;
   a.v_new = (const __half*)v_new;
   a.records = (uint8_t*)cache->records;
+  a.map = c.map;
   a.seq_len = cache->seq_len;
   a.group_bytes = c.group_bytes;
   a.rec_k_bytes = c.rec_k_bytes;
@@ -195,6 +209,7 @@ kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache,
   a.tail_v = c.tail_v;
   a.seq_len = c.seq_len;
   a.records = (uint8_t*)cache->records;
+  a.map = c.map;
   a.group_bytes = c.group_bytes;
   a.rec_k_bytes = c.rec_k_bytes;
   a.hkv = c.hkv;
@@ -247,6 +262,7 @@ kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, co
       a.v = (const __half*)v;
       a.src_tokens = src_tokens;
       a.records = (uint8_t*)cache->records;
+      a.map = c.map;
       a.group_bytes = c.group_bytes;
       a.rec_k_bytes = c.rec_k_bytes;
       a.hkv = c.hkv;

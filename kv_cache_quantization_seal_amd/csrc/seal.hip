@@ -476,8 +476,10 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
   const int bhl = r % a.nbh, kind = r / a.nbh;
   if (kSink + kGroup * (g + 1) > a.lens.len[bhl / a.hkv]) return;
   const int64_t bh = (int64_t)a.b0 * a.hkv + bhl;
+  const int64_t off = pair_offset(a.map, (int)(bh / a.hkv), (int)(bh % a.hkv), g, a.hkv, a.max_groups, a.group_bytes);
+  if (off < 0) return;
   const __half* src = (kind ? a.v : a.k) + (bh * a.src_tokens + kSink + (int64_t)kGroup * g) * D;
-  uint8_t* rec = a.records + (bh * a.max_groups + g) * a.group_bytes + (kind ? a.rec_k_bytes : 0);
+  uint8_t* rec = a.records + off + (kind ? a.rec_k_bytes : 0);
   uint4 raw[4];
   load_tile<D>(raw, src, threadIdx.x);
   seal_rotate<D>(raw, sm, threadIdx.x);
@@ -498,8 +500,10 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealS
   if (n < kSink + kGroup || ((n - kSink) % kGroup) != 0) return;
   const int g = (n - kSink) / kGroup - 1;
   if (g >= a.max_groups) return;
+  const int64_t off = pair_offset(a.map, b, bh - b * a.hkv, g, a.hkv, a.max_groups, a.group_bytes);
+  if (off < 0) return;
   const __half* src = (kind ? a.tail_v : a.tail_k) + (int64_t)bh * kGroup * D;
-  uint8_t* rec = a.records + ((int64_t)bh * a.max_groups + g) * a.group_bytes + (kind ? a.rec_k_bytes : 0);
+  uint8_t* rec = a.records + off + (kind ? a.rec_k_bytes : 0);
   uint4 raw[4];
   load_tile<D>(raw, src, threadIdx.x);
   seal_rotate<D>(raw, sm, threadIdx.x);
@@ -545,9 +549,11 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void append_seal_kernel(Appen
   if (n1 < kSink + kGroup || (n1 - kSink) % kGroup != 0) return;
   const int g = (n1 - kSink) / kGroup - 1;
   if (g >= a.max_groups) return;
+  const int64_t off = pair_offset(a.map, b, bh - b * a.hkv, g, a.hkv, a.max_groups, a.group_bytes);
+  if (off < 0) return;
   __syncthreads();  // the row written above is part of the tile read below
   const __half* tile = (kind ? a.tail_v : a.tail_k) + (int64_t)bh * kGroup * D;
-  uint8_t* rec = a.records + ((int64_t)bh * a.max_groups + g) * a.group_bytes + (kind ? a.rec_k_bytes : 0);
+  uint8_t* rec = a.records + off + (kind ? a.rec_k_bytes : 0);
   uint4 raw[4];
   load_tile<D>(raw, tile, tid);
   seal_rotate<D>(raw, sm, tid);

@@ -43,7 +43,8 @@ class Config(ctypes.Structure):
 class CacheView(ctypes.Structure):
     _fields_ = [("sink_k", ctypes.c_void_p), ("sink_v", ctypes.c_void_p), ("tail_k", ctypes.c_void_p),
                 ("tail_v", ctypes.c_void_p), ("records", ctypes.c_void_p),
-                ("seq_len", ctypes.c_void_p), ("batch", ctypes.c_int32), ("max_groups", ctypes.c_int32)]
+                ("seq_len", ctypes.c_void_p), ("batch", ctypes.c_int32), ("max_groups", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("num_blocks", ctypes.c_int32)]
 
 
 def lib():
@@ -129,9 +130,16 @@ def decode_workspace_bytes(cfg: Config, batch: int, max_groups: int) -> int:
 
 
 class KVarNCache:
-    """Device-resident KVarN cache of one attention layer (torch-allocated)."""
+    """Device-resident KVarN cache of one attention layer (torch-allocated).
 
-    def __init__(self, cfg: Config, batch: int, max_groups: int, device="cuda"):
+    With ``num_blocks`` the records live in a pool of that many blocks (one
+    block = the Hkv record pairs of one 128-token group) addressed through
+    ``block_table`` (int32 [batch][max_groups], initially block
+    ``b * max_groups + g`` for group g of request b; the caller may rewrite
+    it).  Without it the records are one contiguous [B][Hkv][max_groups]
+    array."""
+
+    def __init__(self, cfg: Config, batch: int, max_groups: int, device="cuda", num_blocks: Optional[int] = None):
         self.cfg = cfg
         self.batch = batch
         self.max_groups = max_groups
@@ -143,13 +151,20 @@ class KVarNCache:
         self.tail_v = torch.zeros(batch, hkv, GROUP, d, **f16)
         self.rec_k_bytes = record_bytes(d, cfg.k_bits)
         self.group_bytes = group_bytes(cfg)
-        self.records = torch.zeros(max(1, batch * hkv * max_groups * self.group_bytes), dtype=torch.uint8,
-                                   device=device)
+        self.num_blocks = num_blocks
+        pairs = batch * hkv * max_groups if num_blocks is None else num_blocks * hkv
+        self.records = torch.zeros(max(1, pairs * self.group_bytes), dtype=torch.uint8, device=device)
+        self.block_table = None
+        if num_blocks is not None:
+            self.block_table = torch.arange(batch * max_groups, dtype=torch.int32, device=device).reshape(
+                batch, max_groups)
         self.seq_len = torch.zeros(batch, dtype=torch.int32, device=device)
         ws = decode_workspace_bytes(cfg, batch, max_groups)
         self.workspace = torch.zeros(max(256, ws), dtype=torch.uint8, device=device)  # counters start at 0
         self.view = CacheView(_ptr(self.sink_k), _ptr(self.sink_v), _ptr(self.tail_k), _ptr(self.tail_v),
-                              _ptr(self.records), _ptr(self.seq_len), batch, max_groups)
+                              _ptr(self.records), _ptr(self.seq_len), batch, max_groups,
+                              None if self.block_table is None else _ptr(self.block_table),
+                              0 if num_blocks is None else int(num_blocks))
 
     @property
     def capacity(self) -> int:
@@ -157,7 +172,11 @@ class KVarNCache:
 
     def record(self, b: int, h: int, g: int, kind: str) -> torch.Tensor:
         """Bytes of one stored record (a view)."""
-        base = ((b * self.cfg.num_kv_heads + h) * self.max_groups + g) * self.group_bytes
+        if self.block_table is None:
+            pair = (b * self.cfg.num_kv_heads + h) * self.max_groups + g
+        else:
+            pair = int(self.block_table[b, g]) * self.cfg.num_kv_heads + h
+        base = pair * self.group_bytes
         if kind == "k":
             return self.records[base:base + self.rec_k_bytes]
         return self.records[base + self.rec_k_bytes:base + self.group_bytes]

@@ -140,3 +140,17 @@ def test_append_seal_validates_before_launch():
 def test_width_pairs(kb, vb, ok):
     cfg = K.make_config(128, 8, 2, kb, vb)
     assert (K.check_config(cfg) == K.OK) == ok
+
+
+def test_paged_view_validates_before_launch():
+    """A block table needs a positive block count and 4-byte alignment."""
+    L = K.lib()
+    cfg = K.make_config(128, 32, 8, 2, 2)
+    r = ctypes.byref
+    field_names = [f[0] for f in K.CacheView._fields_]
+    assert field_names[-2:] == ["block_table", "num_blocks"]
+    assert L.kvarn_seal_group(r(cfg), r(_view(block_table=FAKE, num_blocks=0)), None) == K.EINVAL
+    assert L.kvarn_append_seal(r(cfg), r(_view(block_table=FAKE + 2, num_blocks=8)), FAKE, FAKE, None) == K.EINVAL
+    ws = K.decode_workspace_bytes(cfg, 2, 4)
+    assert L.kvarn_decode_attn(r(cfg), r(_view(block_table=FAKE, num_blocks=-1)), FAKE, FAKE, 0.1, FAKE, ws,
+                               None) == K.EINVAL
