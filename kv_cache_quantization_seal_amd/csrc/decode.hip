@@ -50,7 +50,10 @@ namespace kvarn {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
-constexpr int kExactTok = 16;  // exact tokens per wave per round
+constexpr int kExactTok = 16;     // exact tokens per wave per round
+constexpr int kExactRounds = 1;   // rounds per wave
+constexpr int kExactPerSplit = kWaves * kExactTok * kExactRounds;  // exact tokens per exact split
+constexpr int kExactSplits = 2 * kGroup / kExactPerSplit;          // sink (128) + tail (< 128)
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -578,9 +581,10 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 
 // ---------------------------------------------------------------------------
 // Exact split: the sink and the tail, fp16, original frame.  Exact split es
-// covers exact tokens [128 es, 128 es + 128); wave w takes 32 of them in two
-// rounds of 16; lane (token, quarter) holds a quarter of a K row and of a V
-// row.  QK: fp32 FMAs against the LDS query; PV: V rows staged in LDS.
+// covers exact tokens [P es, P es + P), P = kExactPerSplit (the sink's tokens
+// first, then the tail's); wave w takes kExactRounds rounds of 16 of them;
+// lane (token, quarter) holds a quarter of a K row and of a V row.  QK: fp32
+// FMAs against the LDS query; PV: V rows staged in LDS.
 // ---------------------------------------------------------------------------
 template <int D, int GQ>
 __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int split, int n) {
@@ -604,11 +608,11 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
     qh[i] = idx < GQ * D ? a.q[((int64_t)b * a.hq + kvh * GQ) * D + idx] : __half(0.f);
   }
   __builtin_amdgcn_sched_barrier(0);
-  uint4 kr[2][QD / 8], vr[2][QD / 8];
-  bool valid[2];
+  uint4 kr[kExactRounds][QD / 8], vr[kExactRounds][QD / 8];
+  bool valid[kExactRounds];
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int e = kGroup * es + 32 * w + kExactTok * round + tl;
+  for (int round = 0; round < kExactRounds; ++round) {
+    const int e = kExactPerSplit * es + kExactTok * (kExactRounds * w + round) + tl;
     valid[round] = e < n_exact;
     const bool in_tail = valid[round] && e >= n_sink;
     const int64_t row = bh * kGroup + (valid[round] ? (in_tail ? e - n_sink : e) : 0);
@@ -637,8 +641,8 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
     for (int c = 0; c < CPLX; ++c) o[h][c] = 0.f;
   }
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int e0 = kGroup * es + 32 * w + kExactTok * round;
+  for (int round = 0; round < kExactRounds; ++round) {
+    const int e0 = kExactPerSplit * es + kExactTok * (kExactRounds * w + round);
     const bool ok = valid[round];
     float dot[GQ];
 #pragma unroll
@@ -908,7 +912,7 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int re
   // workgroups (short, dispatched first) are not counted.
   const int64_t pairs = (int64_t)batch * hkv;
   const int64_t target = resident_wgs;
-  p.n_exact_splits = 2;  // exact tokens [0,128) and [128,256)
+  p.n_exact_splits = kExactSplits;  // exact tokens [0, 256) in runs of kExactPerSplit
   int gpw = 1;
   if (max_groups > 0) {
     while (4 * gpw < max_groups) {
