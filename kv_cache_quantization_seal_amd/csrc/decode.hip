@@ -9,11 +9,11 @@
 // original frame; records are read directly, never expanded in memory (same
 // page, §2.1 "Sink, Body, And Tail").
 //
-// Record splits.  A workgroup (4 waves) walks a range of 128-token groups of
-// one (request, KV head).  Each group's K and V records are copied into one
-// of two LDS slots through two register stages (the next two groups' loads
-// are in flight while the current one is computed) and the four waves share
-// the work:
+// Record splits.  A record workgroup is four independent waves; each wave
+// takes an even share of the sealed groups of one (request, KV head) and
+// processes each group alone, its operands loaded from HBM straight into
+// registers in MFMA operand order (the next group's loads are issued while
+// the current one is computed):
 //   logit_t = s^K_t * sum_j q~_j (code_tj - mid),  q~ = q_r * c^K * scale,
 //   w_t = p_t * s^V_t,  o_rot_j += c^V_j * sum_t w_t (code_tj - mid).
 // Both sums run on v_mfma_i32_16x16x64_i8 with the codes as exact int8
@@ -21,11 +21,8 @@
 // x * inv ~ a0 + a1/128 + a2/128^2 (|error| <= 0.5/128^2 of the group maximum
 // scaled to the top-limb range); the 16 MFMA rows carry (head, limb) pairs,
 // so each lane holds every limb of one head and recombines them exactly in
-// int32, with one conversion to fp32.
-//   wave h < GQ : q~ limbs of head h;
-//   wave w      : QK for token tiles nt = 2w, 2w+1; PV for channel tiles
-//                 ct = w*(D/64) .. w*(D/64) + D/64 - 1.
-// Softmax maxima per head are exchanged through LDS (base-2 online softmax).
+// int32, with one conversion to fp32.  Softmax is base-2 online softmax per
+// wave; the four waves merge through LDS once, at the end of the split.
 //
 // Operand layouts (lane l, lane group G = l/16, n = l%16):
 //   * B operand of QK = K codes: column n of N-tile nt is token tok(nt, n);
@@ -51,9 +48,9 @@ namespace kvarn {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kExactTok = 16;     // exact tokens per wave per round
-constexpr int kExactRounds = 1;   // rounds per wave
-constexpr int kExactPerSplit = kWaves * kExactTok * kExactRounds;  // exact tokens per exact split
-constexpr int kExactSplits = 2 * kGroup / kExactPerSplit;          // sink (128) + tail (< 128)
+// The exact tokens of a pair (sink 128 + tail < 128) go to 4 exact splits of
+// one round (64 tokens each) or to 2 exact splits of two rounds (128 each);
+// the plan chooses (plan_decode).
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -295,10 +292,14 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   const bool arow_valid = hm < GQ && im < 3;
   WaveLds<D, GQ>& wv = sm.wv[w];
 
+  // The pair's sealed groups (from its current length, not the capacity the
+  // grid was planned for) are shared evenly over its record waves: wave
+  // wi = 4 split + w takes groups [G wi / nw, G (wi+1) / nw), nw = 4 n_rec_splits,
+  // i.e. floor or ceil of G / nw consecutive groups (at most groups_per_wave).
   const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
-  const int gw0 = split * a.groups_per_split + w * a.groups_per_wave;
-  const int ga = min(gw0, n_groups);
-  const int gb = min(gw0 + a.groups_per_wave, n_groups);
+  const int nw = a.n_rec_splits * kWaves, wi = split * kWaves + w;
+  const int ga = (int)((int64_t)n_groups * wi / nw);
+  const int gb = (int)((int64_t)n_groups * (wi + 1) / nw);
 
   // Per-lane byte offsets within a group (loop-invariant).
   // Tokens tok(0..7, n) are tok0 + tstep(nt): tok0 = 16(n/2) + 2(n&1) and
@@ -581,13 +582,14 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 
 // ---------------------------------------------------------------------------
 // Exact split: the sink and the tail, fp16, original frame.  Exact split es
-// covers exact tokens [P es, P es + P), P = kExactPerSplit (the sink's tokens
+// covers exact tokens [P es, P es + P), P = 64 kExactRounds (the sink's tokens
 // first, then the tail's); wave w takes kExactRounds rounds of 16 of them;
 // lane (token, quarter) holds a quarter of a K row and of a V row.  QK: fp32
 // FMAs against the LDS query; PV: V rows staged in LDS.
 // ---------------------------------------------------------------------------
-template <int D, int GQ>
+template <int D, int GQ, int kExactRounds>
 __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int split, int n) {
+  constexpr int kExactPerSplit = kWaves * kExactTok * kExactRounds;  // exact tokens of this split
   constexpr int QD = D / 4;     // channels per lane (quarter row)
   constexpr int CPLX = D / 64;  // channels per lane in the PV part
   const int tid = threadIdx.x;
@@ -765,7 +767,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (bx < nex * npair) {
     const int pair = bx / nex, es = bx - pair * nex;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
-    exact_split<D, GQ>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b]);
+    if (nex == 4)
+      exact_split<D, GQ, 1>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b]);
+    else
+      exact_split<D, GQ, 2>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b]);
   } else {
     const int r = bx - nex * npair;
     const int pair = r / a.n_rec_splits, split = r - pair * a.n_rec_splits;
@@ -905,14 +910,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs) {
   DecodePlan p;
-  // Each record workgroup is four independent waves walking consecutive runs
-  // of groups_per_wave groups of one (request, KV head).  The record
-  // workgroups should be resident at once, so the smallest run length whose
-  // record grid fits `resident_wgs` maximises parallelism; the exact
-  // workgroups (short, dispatched first) are not counted.
+  // Each record workgroup is four independent waves; at run time each wave
+  // takes an even share of its pair's sealed groups, at most groups_per_wave
+  // of them (the grid is planned for the capacity max_groups).  The record
+  // workgroups should be resident at once, so the smallest groups_per_wave
+  // whose record grid fits the target maximises parallelism.
+  //   * Few pairs: four one-round exact splits per pair, not counted in the
+  //     target -- they are short and dispatched first, and the record
+  //     workgroups that do not fit start as they retire.
+  //   * Many pairs (four exact workgroups per pair would hold more than half
+  //     of the resident slots): two two-round exact splits per pair, counted,
+  //     so that every workgroup is resident at once; otherwise most record
+  //     workgroups would start only after the exact ones retire.
   const int64_t pairs = (int64_t)batch * hkv;
-  const int64_t target = resident_wgs;
-  p.n_exact_splits = kExactSplits;  // exact tokens [0, 256) in runs of kExactPerSplit
+  const bool many = 2 * 4 * pairs > (int64_t)resident_wgs;
+  p.n_exact_splits = many ? 2 : 4;
+  const int64_t target = many ? std::max<int64_t>(pairs, resident_wgs - 2 * pairs) : resident_wgs;
   int gpw = 1;
   if (max_groups > 0) {
     while (4 * gpw < max_groups) {

@@ -113,3 +113,15 @@ def test_two_phase_equals_fused():
     torch.cuda.synchronize()
     assert torch.allclose(fused, two, atol=1e-6, rtol=1e-5)
     assert torch.equal(fused, again)
+
+
+@pytest.mark.parametrize("hq,kb,vb", [(32, 2, 2), (16, 4, 4)])
+def test_many_pairs(hq, kb, vb):
+    # 16 requests x 8 KV heads = 128 pairs: four exact workgroups per pair
+    # would hold more than half of the resident slots, so the plan takes two
+    # exact splits of 128 tokens (two rounds per wave) per pair.  Lengths
+    # cover an empty request, sink-only, exact tail lengths and group edges.
+    lens = [0, 1, 128, 129, 200, 255, 256, 300, 383, 384, 400, 511, 512, 513, 600, 640]
+    err = _run(128, hq, 8, kb, vb, lens, seed=hq + kb)
+    print(f"128 pairs hq={hq} k{kb} v{vb}: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
