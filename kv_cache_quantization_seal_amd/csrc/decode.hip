@@ -880,7 +880,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
   // Inverse rotation of the record part (H symmetric): channel c = P*l + i;
   // butterflies over the bits of i in registers, over the bits of l across
-  // lanes.
+  // lanes without LDS traffic: DPP for lane bits 1, 2, 4, 8 (the upper lane
+  // of a pair keeps lower - upper), the row and half swaps for 16 and 32
+  // (each lane gets the pair's sum s; the upper lane keeps s - 2 x).
 #pragma unroll
   for (int st = 1; st < P; st <<= 1) {
 #pragma unroll
@@ -893,13 +895,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     }
   }
 #pragma unroll
-  for (int st = 1; st < kWave; st <<= 1) {
+  for (int st = 1; st < 16; st <<= 1) {
     const bool hi = l & st;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const float pv = __shfl_xor(x[i], st, kWave);
+      const int v = __float_as_int(x[i]);
+      int o;
+      if (st == 1) {
+        o = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+      } else if (st == 2) {
+        o = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+      } else if (st == 4) {
+        o = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+        o = __builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false);  // row_shr:4, banks 1, 3
+      } else {
+        o = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true);   // row_ror:8
+      }
+      const float pv = __int_as_float(o);
       x[i] = hi ? pv - x[i] : x[i] + pv;
     }
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const float s16 = xor16_sum(x[i]);
+    x[i] = (l & 16) ? fmaf(-2.0f, x[i], s16) : s16;
+    const float s32 = xor32_sum(x[i]);
+    x[i] = (l & 32) ? fmaf(-2.0f, x[i], s32) : s32;
   }
   const float rs = (D == 128) ? 0.08838834764831845f : 0.0625f;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
