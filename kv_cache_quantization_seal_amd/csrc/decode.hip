@@ -929,7 +929,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   for (int i = 0; i < P; ++i) out[i] = (x[i] * rs + e[i]) * inv;
 }
 
-DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs) {
+DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs, int cus) {
   DecodePlan p;
   // Each record workgroup is four independent waves; at run time each wave
   // takes an even share of its pair's sealed groups, at most groups_per_wave
@@ -955,9 +955,24 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int re
       ++gpw;
     }
   }
+  int nrec = max_groups > 0 ? (max_groups + 4 * gpw - 1) / (4 * gpw) : 0;
+  // A record grid just above a whole number k of workgroups per CU leaves a
+  // few CUs with one more busy workgroup than the rest, and they finish last
+  // (Llama-3.1-8B shape, capacity 257 groups: 520 record workgroups, 13.4 us;
+  // 512, 11.3 us).  If dropping one split per pair reaches k per CU, drop it:
+  // the waves share the groups actually sealed, so in the usual case (fewer
+  // groups than the capacity) no wave gets more.  Larger excesses are kept:
+  // there the extra waves carry their share of the traffic.
+  if (cus > 0 && nrec > 1) {
+    const int64_t r = pairs * nrec, k = r / cus;
+    if (k >= 1 && r % cus != 0 && pairs * (nrec - 1) <= k * cus) {
+      --nrec;
+      gpw = (max_groups + 4 * nrec - 1) / (4 * nrec);
+    }
+  }
   p.groups_per_wave = gpw;
   p.groups_per_split = 4 * gpw;
-  p.n_rec_splits = max_groups > 0 ? (max_groups + 4 * gpw - 1) / (4 * gpw) : 0;
+  p.n_rec_splits = nrec;
   p.nsplit = p.n_rec_splits + p.n_exact_splits;
   const size_t rows = (size_t)batch * hq * p.nsplit;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
@@ -981,6 +996,16 @@ static int resident_t(int dev) {
 template <int D, int KB, int VB>
 static int resident_g(int gq, int dev) {
   return gq == 1 ? resident_t<D, KB, VB, 1>(dev) : gq == 2 ? resident_t<D, KB, VB, 2>(dev) : resident_t<D, KB, VB, 4>(dev);
+}
+
+int decode_cu_count() {
+  static std::atomic<int> cache[16];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 16 && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 16) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 int decode_resident_wgs(int D, int kb, int vb, int gq) {

@@ -174,9 +174,14 @@ struct DecodePlan {
 // this (the workspace query, which has no device, plans with it).
 constexpr int kMaxResidentWgs = 4096;
 
-DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs);
+// cus: compute units of the launch's device, or 0 (a device-free plan, used
+// for the workspace bound; rounding to whole workgroups per CU only ever
+// removes splits).
+DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs, int cus);
 // Resident split workgroups on the current device for this configuration.
 int decode_resident_wgs(int D, int kb, int vb, int gq);
+// Compute units of the current device (0 if unknown).
+int decode_cu_count();
 
 hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* dst, int64_t stride, float* dbg, int n,
                              int iters, hipStream_t st);

@@ -131,7 +131,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int3
   // Planned for the most resident workgroups any device allows: a launch
   // plans for fewer, hence fewer splits and no more workspace.
   return kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch, max_groups,
-                            kvarn::kMaxResidentWgs)
+                            kvarn::kMaxResidentWgs, 0)
       .ws_bytes;
 }
 
@@ -290,7 +290,7 @@ static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* ca
   const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
                                                   cfg->num_q_heads / cfg->num_kv_heads);
   const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
-                                                 cache->max_groups, resident);
+                                                 cache->max_groups, resident, kvarn::decode_cu_count());
   if (!workspace || ws_bytes < p.ws_bytes)
     return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, p.ws_bytes);
   if (!aligned(workspace, 256)) return fail(KVARN_EINVAL, "workspace must be 256-byte aligned");

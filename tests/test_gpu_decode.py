@@ -125,3 +125,14 @@ def test_many_pairs(hq, kb, vb):
     err = _run(128, hq, 8, kb, vb, lens, seed=hq + kb)
     print(f"128 pairs hq={hq} k{kb} v{vb}: max abs err {err:.3e}")
     assert err <= ATTN_ATOL
+
+
+def test_grid_rounded_to_whole_cus():
+    # 2 requests x 4 KV heads with capacity for 130 groups plans 33 record
+    # splits per pair (264 workgroups, just above one per CU on a 256-CU
+    # device), which the plan rounds down to 32: each record wave then takes
+    # one or two of a request's 129 sealed groups.
+    lens = [128 + 128 * 129 + 5, 128 + 128 * 100 + 77]
+    err = _run(128, 16, 4, 2, 2, lens, seed=13, max_groups=130)
+    print(f"rounded grid: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
