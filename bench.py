@@ -544,6 +544,66 @@ def main():
 
     t_kernel = time_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]))
     t_combine = time_graph(lambda r: caches[r % ncopy].decode_combine(outs[r % ncopy]))
+
+    # ---- one streaming seal event (the append that completes a group, K and
+    # V of every KV head sealed in the same launch) against an append that
+    # seals nothing: every layer cache is put 127 tokens into its tail (the
+    # tail rows are real tokens of the stream), then one graph of append+seal
+    # launches over the layer caches is timed, each launch sealing a group.
+    n_due = lens0[0] + 127
+    def set_len(n):
+        for c in caches:
+            c.seq_len.fill_(n)
+    for c in caches:   # the prompt's last 127 tokens stand in for the tail
+        c.tail_k[:, :, :127].copy_(k_all[:, :, lens0[0] - 127:lens0[0]])
+        c.tail_v[:, :, :127].copy_(v_all[:, :, lens0[0] - 127:lens0[0]])
+    ev_times = {}
+    for label, n in (("seal_event", n_due), ("append_only", lens0[0])):
+        set_len(n)
+        torch.cuda.synchronize()
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs, stream=stream):
+            for r in range(ncopy):
+                caches[r].append_seal(new_k[0], new_v[0])
+        set_len(n)
+        torch.cuda.synchronize()
+        gs.replay()
+        set_len(n)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            gs.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        ev_times[label] = ev0.elapsed_time(ev1) * 1e3 / ncopy
+        del gs
+        n_after = int(caches[-1].seq_len[0].item())
+        if n_after != n + 1:
+            raise RuntimeError(f"{label}: length {n_after} after the append, expected {n + 1}")
+    reset()
+    seal_event = {"us_seal_event": ev_times["seal_event"], "us_append_only": ev_times["append_only"],
+                  "tiles": 2 * B * hkv,
+                  "note": "kvarn_append_seal launches back to back in a graph over the layer caches: each "
+                          "completes a group (K and V of every KV head sealed) vs each only appends"}
+    print(f"[bench] seal event: {seal_event['us_seal_event']:.2f} us per append+seal launch that seals "
+          f"{2 * B * hkv} tiles; {seal_event['us_append_only']:.2f} us when nothing is due",
+          file=sys.stderr, flush=True)
+
+    # ---- streaming-read ceiling: the library's plain read kernel over 4 GiB
+    # (reported beside the 8 TB/s peak; not the target)
+    rd = torch.zeros(2**32, dtype=torch.uint8, device=dev)
+    rd_sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    K.read_probe(rd, rd_sink)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        K.read_probe(rd, rd_sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_ceiling = rd.numel() * 5 / (e0.elapsed_time(e1) / 1e3)
+    del rd, rd_sink
+    print(f"[bench] streaming-read ceiling (kvarn_read_probe over 4 GiB): {read_ceiling / 1e12:.2f} TB/s",
+          file=sys.stderr, flush=True)
     bytes_launch = algorithmic_decode_bytes(wl, lens0, k_rec, v_rec)
     achieved = bytes_launch / t_kernel
     traffic = read_traffic(wl.name)
@@ -605,7 +665,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
                      "kernel": "decode_split_kernel", "bytes_per_launch": bytes_launch,
-                     "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6},
+                     "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6,
+                     "read_ceiling_GBps": read_ceiling / 1e9, "frac_of_read_ceiling": achieved / read_ceiling},
+        "seal_event": seal_event,
         "seal": seal,
         "dequant": dequant,
         "paged": paged_line,

@@ -194,6 +194,7 @@ hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const v
                                const PrefillLens& lens, int b0, int nb, hipStream_t st);
 // phases: 1 = split kernel (partials into the workspace), 2 = combine kernel, 3 = both.
 hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int phases, hipStream_t st);
+hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, int cus, hipStream_t st);
 hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
                           hipStream_t st);
 

@@ -364,4 +364,13 @@ kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
                     "kvarn_dequant_records launch");
 }
 
+kvarn_status kvarn_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(KVARN_EINVAL, "buf and sink must be non-NULL");
+  if (!aligned(buf, 16) || bytes % 16) return fail(KVARN_EINVAL, "buf must be 16-byte aligned and bytes a multiple of 16");
+  if (!aligned(sink, 4)) return fail(KVARN_EINVAL, "sink must be 4-byte aligned");
+  return hip_status(kvarn::launch_read_probe(buf, bytes, sink, kvarn::decode_cu_count(), (hipStream_t)stream),
+                    "kvarn_read_probe launch");
+}
+
 }  // extern "C"

@@ -24,7 +24,7 @@ EXPORTS = (
     "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
     "kvarn_prefill",
     "kvarn_decode_attn", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
-    "kvarn_dequant_records",
+    "kvarn_dequant_records", "kvarn_read_probe",
 )
 
 
@@ -76,6 +76,7 @@ def lib():
         L.kvarn_decode_attn_combine.argtypes = [cp(Config), cp(CacheView), vp, vp, sz, vp]
         L.kvarn_seal_tiles.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp, i32, vp]
         L.kvarn_dequant_records.argtypes = [i32, i32, i32, vp, i64, vp, i32, vp]
+        L.kvarn_read_probe.argtypes = [vp, sz, vp, vp]
         for name in EXPORTS:
             if name not in ("kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
                             "kvarn_last_error", "kvarn_status_string"):
@@ -248,3 +249,12 @@ def dequant_records(recs: torch.Tensor, head_dim: int, bits: int, kind: str, out
     _check(lib().kvarn_dequant_records(head_dim, bits, 0 if kind == "k" else 1, ctypes.c_void_p(recs.data_ptr()),
                                        recs.stride(0), _ptr(out), n, _stream(stream)))
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream every byte of `buf` (device, contiguous, 16-byte aligned) through
+    the library's plain read kernel (a measurement aid: the achievable
+    streaming-read bandwidth); `sink` is a device tensor of at least 4 bytes."""
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf and sink must be contiguous device tensors")
+    _check(lib().kvarn_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))

@@ -154,3 +154,13 @@ def test_paged_view_validates_before_launch():
     ws = K.decode_workspace_bytes(cfg, 2, 4)
     assert L.kvarn_decode_attn(r(cfg), r(_view(block_table=FAKE, num_blocks=-1)), FAKE, FAKE, 0.1, FAKE, ws,
                                None) == K.EINVAL
+
+
+def test_read_probe_validates():
+    L = K.lib()
+    assert L.kvarn_read_probe(FAKE, 0, FAKE, None) == K.OK   # nothing to read: no launch
+    assert L.kvarn_read_probe(None, 16, FAKE, None) == K.EINVAL
+    assert L.kvarn_read_probe(FAKE, 16, None, None) == K.EINVAL
+    assert L.kvarn_read_probe(FAKE, 24, FAKE, None) == K.EINVAL
+    assert L.kvarn_read_probe(FAKE + 8, 16, FAKE, None) == K.EINVAL
+    assert L.kvarn_read_probe(FAKE, 16, FAKE + 2, None) == K.EINVAL

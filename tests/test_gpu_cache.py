@@ -163,3 +163,14 @@ def test_dequant_records(d, bits, kind):
         ref = O.dequant_record(recs[i].tobytes(), d, bits, kind)
         err = np.abs(got[i] - ref)
         assert np.all(err <= 2.0 ** -11 * np.abs(ref) + 1e-4 * np.abs(ref).max())
+
+
+def test_read_probe_reads_and_writes_nothing():
+    # The measurement probe streams the buffer; its sink is written only for
+    # an improbable xor of a thread's data, which all-ones pieces never give.
+    buf = torch.full((1 << 22,), -1, dtype=torch.int32, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    K.read_probe(buf, sink)
+    K.read_probe(buf[:4], sink)   # fewer pieces than threads of one workgroup
+    torch.cuda.synchronize()
+    assert sink.tolist() == [7, 7, 7, 7]
