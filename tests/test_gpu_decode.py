@@ -136,3 +136,12 @@ def test_grid_rounded_to_whole_cus():
     err = _run(128, 16, 4, 2, 2, lens, seed=13, max_groups=130)
     print(f"rounded grid: max abs err {err:.3e}")
     assert err <= ATTN_ATOL
+
+
+def test_more_splits_than_the_combine_batch():
+    # One pair with 511 sealed groups plans over 80 splits (128 record + 4
+    # exact), so the combine also takes its loop over the splits past its
+    # first batch of loads.
+    err = _run(128, 4, 1, 2, 2, [128 + 128 * 511 + 37], seed=17)
+    print(f"511 groups, one pair: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
