@@ -69,6 +69,8 @@ WORKLOADS: Dict[str, Workload] = {
     "llama31_8b_32k": Workload("llama31_8b_32k", 1, 1, 32, 8, 128, 32768, 0, 2, 2, 256),
     # Qwen3-4B attention shape, batch 16 at 16k, staggered so seals interleave.
     "qwen3_4b_16k_b16": Workload("qwen3_4b_16k_b16", 2, 16, 32, 8, 128, 16384, 8, 2, 2, 256),
+    # The same with every request at 16k: all 16 requests seal on the same step.
+    "qwen3_4b_16k_b16_aligned": Workload("qwen3_4b_16k_b16_aligned", 5, 16, 32, 8, 128, 16384, 0, 2, 2, 256),
     # Phi-4-14B attention shape, 4-bit K and V, batch 8 at 32k, tails 0..112.
     "phi4_14b_32k_b8": Workload("phi4_14b_32k_b8", 3, 8, 40, 10, 128, 32768, 16, 4, 4, 0),
     # Head dim 256, 64k context, K 4-bit / V 2-bit, 2% outlier channels x20.
