@@ -242,8 +242,8 @@ kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
 /*
  * Measurement aid (no KVarN computation): stream `bytes` bytes of device
  * memory at `buf` (16-byte aligned, bytes a multiple of 16) through a plain
- * read kernel of many resident workgroups, each thread reading 16-byte pieces
- * in a grid-stride loop.  The data are combined so that the loads cannot be
+ * read kernel (32 workgroups per CU), each thread reading 16-byte pieces with
+ * nontemporal loads in a grid-stride loop.  The data are combined so that the loads cannot be
  * dropped; `sink` (device, 4 bytes) is written only if the combination of a
  * thread's data equals an improbable constant, so the kernel's traffic is
  * the reads.  Timing it gives the achievable streaming-read bandwidth, the
