@@ -944,6 +944,14 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int re
   //     so that every workgroup is resident at once; otherwise most record
   //     workgroups would start only after the exact ones retire.
   const int64_t pairs = (int64_t)batch * hkv;
+  // Unless the exact workgroups need the third slot (many pairs), plan for at
+  // most two record workgroups per CU: fewer, longer-running waves overlap
+  // their groups' loads with the previous group's work and share the SIMDs
+  // with fewer other waves.  Same-box A/B of the split kernel: Llama-3.1-8B
+  // 11.45 -> 10.84 us (256 record workgroups of two groups per wave instead
+  // of 512 of one), Phi-4 69.3 -> 65.5 us; at Qwen3-4B (many pairs) the cap
+  // would cost 44.3 -> 45.8 us, so it is not applied there.
+  if (cus > 0 && !(2 * 4 * pairs > (int64_t)resident_wgs)) resident_wgs = std::min(resident_wgs, 2 * cus);
   const bool many = 2 * 4 * pairs > (int64_t)resident_wgs;
   p.n_exact_splits = many ? 2 : 4;
   const int64_t target = many ? std::max<int64_t>(pairs, resident_wgs - 2 * pairs) : resident_wgs;
