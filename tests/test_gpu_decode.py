@@ -145,3 +145,13 @@ def test_more_splits_than_the_combine_batch():
     err = _run(128, 4, 1, 2, 2, [128 + 128 * 511 + 37], seed=17)
     print(f"511 groups, one pair: max abs err {err:.3e}")
     assert err <= ATTN_ATOL
+
+
+def test_waves_of_three_groups():
+    # 4 requests x 2 KV heads, capacity 701 groups: the plan gives each
+    # record wave up to three groups (one stage refilled twice); the other
+    # requests leave their waves with zero or one group.
+    lens = [128 + 128 * 700 + 7, 200, 0, 129 + 128]
+    err = _run(128, 8, 2, 2, 2, lens, seed=19, max_groups=701)
+    print(f"waves of three groups: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
