@@ -113,15 +113,40 @@ __global__ __launch_bounds__(4 * D) void dequant_kernel(const uint8_t* __restric
   const int t = threadIdx.x / NB, bl = threadIdx.x % NB;
   const float st = h2f(s16[t]);
   float x[32];
+  uint32_t code[32];
+  if constexpr (KIND == 0) {
+    // Token t's codes 32 bl .. 32 bl + 31 are BITS consecutive dwords of
+    // its row (row and run starts are multiples of 32 bits): load them once,
+    // then one bit-field extract (or funnel shift) per code at a fixed place.
+    const uint32_t* w = rs_ + (t * ROWBITS + 32 * BITS * bl) / 32;
+    uint32_t r[BITS];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int j = 32 * bl + i;
-    const int bit = (KIND == 0 ? t : j) * ROWBITS + BITS * (KIND == 0 ? j : t);
-    uint64_t pair = rs_[bit / 32];
-    if (bit % 32 + BITS > 32) pair |= (uint64_t)rs_[bit / 32 + 1] << 32;
-    const uint32_t code = (uint32_t)(pair >> (bit % 32)) & ((1u << BITS) - 1);
-    x[i] = st * ((float)code - MID) * h2f(c16[j]);
+    for (int k = 0; k < BITS; ++k) r[k] = w[k];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int b0 = BITS * i, k = b0 / 32, sh = b0 % 32;
+      if (sh + BITS <= 32)
+        code[i] = __builtin_amdgcn_ubfe(r[k], sh, BITS);
+      else
+        code[i] = __builtin_amdgcn_alignbit(r[k + 1], r[k], sh) & ((1u << BITS) - 1);
+    }
+  } else {
+    // Channel rows: channel j's code of token t sits at the same place in
+    // every row (bit BITS t), rows 4 BITS dwords apart.  A code that crosses
+    // into the next dword (odd widths) reads it too; that dword is still in
+    // the record (the scales follow the codes).
+    const int dw = (BITS * t) >> 5, sh = (BITS * t) & 31;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t* w = rs_ + (32 * bl + i) * (ROWBITS / 32) + dw;
+      if constexpr (32 % BITS == 0)
+        code[i] = __builtin_amdgcn_ubfe(w[0], sh, BITS);
+      else
+        code[i] = __builtin_amdgcn_alignbit(w[1], w[0], sh) & ((1u << BITS) - 1);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = st * ((float)code[i] - MID) * h2f(c16[32 * bl + i]);
 #pragma unroll
   for (int s = 1; s < 32; s <<= 1) {
 #pragma unroll
