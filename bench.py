@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--workload", default="llama31_8b_32k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seal-groups", type=int, default=48)
-    ap.add_argument("--other-workloads", default="qwen3_4b_16k_b16,qwen3_4b_16k_b16_aligned,phi4_14b_32k_b8,longctx_d256_64k_b4",
+    ap.add_argument("--other-workloads", default="qwen3_4b_16k_b16,qwen3_4b_16k_b16_aligned,phi4_14b_32k_b8,longctx_d256_64k_b4,"
+                    "llama31_8b_32k_k3v2,llama31_8b_32k_k6v5",
                     help="comma-separated workloads measured after the headline one and reported under "
                          "'workloads' (empty: none)")
     ap.add_argument("--other-steps", type=int, default=256, help="decode steps timed per other workload")

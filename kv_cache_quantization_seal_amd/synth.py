@@ -67,6 +67,9 @@ WORKLOADS: Dict[str, Workload] = {
     "tiny_parity": Workload("tiny_parity", 0, 1, 1, 1, 128, 512, 0, 2, 2, 0),
     # Llama-3.1-8B attention shape: 32 q / 8 kv heads, 32k context, 256 steps.
     "llama31_8b_32k": Workload("llama31_8b_32k", 1, 1, 32, 8, 128, 32768, 0, 2, 2, 256),
+    # The same shape at two of the K/V width presets (3-2 and 6-5 bits).
+    "llama31_8b_32k_k3v2": Workload("llama31_8b_32k_k3v2", 6, 1, 32, 8, 128, 32768, 0, 3, 2, 256),
+    "llama31_8b_32k_k6v5": Workload("llama31_8b_32k_k6v5", 7, 1, 32, 8, 128, 32768, 0, 6, 5, 256),
     # Qwen3-4B attention shape, batch 16 at 16k, staggered so seals interleave.
     "qwen3_4b_16k_b16": Workload("qwen3_4b_16k_b16", 2, 16, 32, 8, 128, 16384, 8, 2, 2, 256),
     # The same with every request at 16k: all 16 requests seal on the same step.
