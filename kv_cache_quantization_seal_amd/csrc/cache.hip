@@ -170,12 +170,12 @@ __global__ __launch_bounds__(4 * D) void dequant_kernel(const uint8_t* __restric
     for (int i = 0; i < 32; ++i) x[i] = fmaf((bl & 4) ? -1.0f : 1.0f, dq_pair<4>(x[i]), x[i]);
   }
   const float rs = ((D == 128) ? 0.08838834764831845f : 0.0625f) * ((__popc(bl) & 1) ? -1.0f : 1.0f);
-  // D 128: through LDS, so that each store instruction writes consecutive
-  // 16-byte pieces across the lanes (a lane's own 64 bytes leave 48-byte gaps
-  // between lanes); 8192 2-bit records: 98 -> 68 us.  At D 256 (a 64 KB
-  // tile) the staged form was slower for K records (202 -> 248 us), so there
-  // the lanes store their own 64 bytes.
-  if constexpr (D == 128) {
+  // Through LDS, so that each store instruction writes consecutive 16-byte
+  // pieces across the lanes (a lane's own 64 bytes leave 48-byte gaps between
+  // lanes); 8192 2-bit records at D 128: 98 -> 68 us, V records at D 256:
+  // 197 -> 178 us.  For K records at D 256 (a 64 KB tile) the staged form was
+  // slower (202 -> 248 us), so there the lanes store their own 64 bytes.
+  if constexpr (D == 128 || KIND == 1) {
     __shared__ uint4 os_[kGroup * D / 8];  // the fp16 output tile, row-major
     uint4* orow = os_ + (t * D + 32 * bl) / 8;
 #pragma unroll
