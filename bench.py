@@ -34,13 +34,17 @@ import time
 import numpy as np
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
-VALU_FP32_PEAK = 157.3e12  # flop/s, fp32 vector (packed) MI355X
+# fp32 vector peak without packed instructions (disabled in this build):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz.  The 157.3 TFLOP/s
+# vendor figure counts packed FMAs, which no kernel here issues.
+VALU_FP32_PEAK = 78.6e12
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=8192)
+    ap.add_argument("--steps", type=int, default=8192,
+                    help="decode steps timed (at most copies x 256 fit the workload's capacity)")
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--copies", type=int, default=32)
     ap.add_argument("--workload", default="llama31_8b_32k")
@@ -260,22 +264,27 @@ def _enc(out, bits, kind):
     return dict(codes=out["codes"], s16=out["s16"], c16=out["c16"], bits=bits, kind=kind)
 
 
-def measure_workload(torch, K, synth, dev, name, steps, hbm_target_bytes=768 * 2**20):
-    """Decode step (append + seal-if-due + decode attention) and bulk seal of
-    one more workload, measured like the headline one: K/V drawn on the device
-    with the synthetic recipe, enough layer caches (at least 2) to exceed
-    `hbm_target_bytes` so steps read HBM rather than the Infinity Cache, a HIP
-    graph of `steps` steps rotating over them, then HIP-event timing of the
-    split kernel alone."""
+def measure_workload(torch, K, probe, synth, dev, name, steps, hbm_target_bytes=768 * 2**20):
+    """Decode step and bulk seal of one more workload, measured like the
+    headline one: K/V drawn on the device with the synthetic recipe, enough
+    layer caches (at least 2) to exceed `hbm_target_bytes` so steps read HBM
+    rather than the Infinity Cache, a HIP graph of `steps` steps rotating over
+    them, then HIP-event timing of the split kernel alone (median of 50
+    replays).  A step is append + seal-if-due + decode attention for workloads
+    that decode (at most their own number of steps per cache, so the cache
+    capacity is the workload's own and the decode plan is the one the
+    full-size parity test checks), and decode attention alone for the
+    steady-state workload."""
     wl = synth.WORKLOADS[name]
     B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     lens0 = [wl.start_len(b) for b in range(B)]
     k_rec, v_rec = K.record_bytes(d, wl.k_bits), K.record_bytes(d, wl.v_bits)
     bytes_launch = algorithmic_decode_bytes(wl, lens0, k_rec, v_rec)
     ncopy = max(2, -(-hbm_target_bytes // bytes_launch))
-    tokens = max(1, -(-steps // ncopy))
+    decoding = wl.steps > 0
+    tokens = min(wl.steps, max(1, -(-steps // ncopy))) if decoding else 1
+    max_groups = wl.max_groups()
     lmax = max(lens0) + tokens
-    max_groups = (lmax - 128) // 128 + 1
     kd, vd = synth.kv_streams_device(wl, lmax, dev)
     idx = torch.tensor([[n + t for n in lens0] for t in range(tokens)], device=dev)   # [T][B]
     ar = torch.arange(B, device=dev)
@@ -283,29 +292,29 @@ def measure_workload(torch, K, synth, dev, name, steps, hbm_target_bytes=768 * 2
     new_v = torch.stack([vd[ar, :, idx[t]] for t in range(tokens)]).contiguous()
     q_all = torch.from_numpy(np.stack([synth.queries(wl, b, tokens) for b in range(B)], axis=1)).to(dev)
     cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
+    plan = K.decode_plan(cfg, B, max_groups)
     caches = [K.KVarNCache(cfg, B, max_groups, device=dev) for _ in range(ncopy)]
     for c in caches:
         c.prefill(kd, vd, lens0)
     torch.cuda.synchronize()
-    # bulk seal, timed on cache 0
+    stream = torch.cuda.Stream()
+    # bulk seal, timed on cache 0 (median of 50 graph replays)
     n_groups_seal = sum(hkv * ((n - 128) // 128) for n in lens0 if n > 128)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    caches[0].prefill(kd, vd, lens0)
-    e1.record()
-    torch.cuda.synchronize()
-    t_prefill = e0.elapsed_time(e1) / 1e3
-    del kd, vd
+    g_seal = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_seal, stream=stream):
+        caches[0].prefill(kd, vd, lens0, stream=stream)
+    t_prefill = float(np.median(_timed_replays(torch, stream, g_seal, 50)))
+    del g_seal, kd, vd
     seq0 = caches[0].seq_len.clone()
     outs = [torch.empty(B, hq, d, dtype=torch.float32, device=dev) for _ in range(ncopy)]
+    flush_buf = torch.zeros(2**30, dtype=torch.uint8, device=dev)
+    flush_sink = torch.zeros(4, dtype=torch.int32, device=dev)
 
     def reset():
         for c in caches:
             c.seq_len.copy_(seq0)
 
-    stream = torch.cuda.Stream()
-
-    def timed_graph(fn, n):
+    def timed_graph(fn, n, reps):
         reset()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -315,39 +324,64 @@ def measure_workload(torch, K, synth, dev, name, steps, hbm_target_bytes=768 * 2
         reset()
         torch.cuda.synchronize()
         g.replay()
-        reset()
         torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / n
+        ts = _timed_replays(torch, stream, g, reps, before=lambda: (reset(), probe.read(flush_buf, flush_sink)),
+                            per=n)
+        del g
+        return _stats(ts)
 
     def step(s):
         c = caches[s % ncopy]
         t = s // ncopy
-        c.append_seal(new_k[t], new_v[t])
+        if decoding:
+            c.append_seal(new_k[t], new_v[t])
         c.decode_attn(q_all[t], out=outs[s % ncopy])
 
-    t_step = timed_graph(step, tokens * ncopy)
-    t_split = timed_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]), 4 * ncopy)
+    st_step = timed_graph(step, tokens * ncopy, 20)
+    st_split = timed_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]), 8 * ncopy, 50)
+    t_step, t_split = st_step["median"], st_split["median"]
     achieved = bytes_launch / t_split
     seal_bytes_per_group = 2 * 128 * d * 2 + k_rec + v_rec
+    us = lambda st: {k: (v * 1e6 if k != "reps" else v) for k, v in st.items()}
     out = {
-        "tokens_per_s": B / t_step, "ms_per_step": t_step * 1e3,
+        "tokens_per_s": B / t_step, "ms_per_step": t_step * 1e3, "step_us_stats": us(st_step),
         "config": {"batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "context": lens0[0],
                    "context_stagger": wl.stagger, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
-                   "layer_caches": ncopy, "steps": tokens * ncopy},
+                   "layer_caches": ncopy, "steps": tokens * ncopy, "max_groups": max_groups,
+                   "step": ("append + seal-if-due + decode attention" if decoding else "decode attention")},
+        "decode_plan": plan,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "kernel": "decode_split_kernel",
-                     "bytes_per_launch": bytes_launch, "us_per_launch": t_split * 1e6},
+                     "bytes_per_launch": bytes_launch, "us_per_launch": t_split * 1e6, "us_stats": us(st_split)},
         "seal": {"groups_per_s": n_groups_seal / t_prefill,
                  "hbm_frac": n_groups_seal * seal_bytes_per_group / t_prefill / HBM_PEAK},
     }
-    del caches, outs, new_k, new_v, q_all
+    del caches, outs, new_k, new_v, q_all, flush_buf
     torch.cuda.empty_cache()
     return out
+
+
+def _stats(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(xs)), "p10": float(np.percentile(xs, 10)),
+            "p90": float(np.percentile(xs, 90)), "reps": int(xs.size)}
+
+
+def _timed_replays(torch, stream, g, reps, before=None, per=1):
+    """Replay graph g `reps` times on `stream`, each bracketed by its own HIP
+    events (recorded on that stream); `before` runs untimed before every
+    replay.  Returns the per-replay times in seconds divided by `per`."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for e0, e1 in evs:
+            if before is not None:
+                before()   # queued on `stream`, ahead of the replay
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) / 1e3 / per for e0, e1 in evs]
 
 
 def main():
@@ -361,6 +395,7 @@ def main():
         return
     import torch
     from kv_cache_quantization_seal_amd import kvarn as K
+    from kv_cache_quantization_seal_amd import probe
     from kv_cache_quantization_seal_amd import synth
 
     if args.copy_calibration > 0:
@@ -377,11 +412,24 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     ncopy = args.copies
-    tokens = -(-max(args.steps, args.warmup) // ncopy)  # tokens appended per layer cache
-    tokens = max(tokens, 1)
+    # The cache capacity is the workload's own (every group its decode steps
+    # seal), independent of --steps, so every run launches the decode plan
+    # that the full-size parity test checks and the profile measures.
+    max_groups = wl.max_groups()
+    cap = 128 + 128 * max_groups + 127
     lens0 = [wl.start_len(b) for b in range(B)]
-    lmax = max(lens0) + tokens
-    max_groups = (lmax - 128) // 128 + 1
+    # Layer caches start at spread phases of the group cycle: layer c holds
+    # 127 - floor(128 c / copies) more tail tokens than the context, so layer 0
+    # seals on its first step.  Layers advance in lockstep (step s appends to
+    # layer s % copies), so any window of steps sees the seal cadence of a
+    # steady decode (one seal per 128 tokens per layer), and at least one.
+    phases = [127 - (128 * c) // ncopy for c in range(ncopy)]
+    tokens = max(1, -(-max(args.steps, args.warmup) // ncopy))  # tokens appended per layer cache
+    if max(lens0) + max(phases) + tokens > cap:
+        sys.exit(f"--steps {args.steps} appends {tokens} tokens per layer cache, more than the "
+                 f"{wl.name} capacity ({cap} tokens) leaves room for; use at most "
+                 f"{(cap - max(lens0) - max(phases)) * ncopy} steps")
+    lmax = max(lens0) + max(phases) + tokens
     # The CPU oracle baseline runs first, before the GPU is initialized (its
     # worker pool is spawned).
     cpu_line = None
@@ -393,7 +441,8 @@ def main():
     torch.cuda.init()
     dev = torch.device("cuda:0")
     print(f"[bench] workload {wl.name}: B={B} Hq={hq} Hkv={hkv} D={d} ctx={lens0[0]} "
-          f"k{wl.k_bits}/v{wl.v_bits}, copies={ncopy}, steps={args.steps}", file=sys.stderr, flush=True)
+          f"k{wl.k_bits}/v{wl.v_bits}, copies={ncopy}, steps={args.steps}, max_groups={max_groups}",
+          file=sys.stderr, flush=True)
 
     # ---- inputs (seeded, synthetic), generated on the host then uploaded ----
     t0 = time.time()
@@ -407,26 +456,41 @@ def main():
     print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     k_all = torch.from_numpy(kh).to(dev)
     v_all = torch.from_numpy(vh).to(dev)
-    new_k = torch.stack([k_all[b, :, lens0[b]:lens0[b] + tokens] for b in range(B)])  # [B][Hkv][T][D]
-    new_v = torch.stack([v_all[b, :, lens0[b]:lens0[b] + tokens] for b in range(B)])
-    new_k = new_k.permute(2, 0, 1, 3).contiguous()  # [T][B][Hkv][D]
-    new_v = new_v.permute(2, 0, 1, 3).contiguous()
+    del kh, vh
+    lens_c = [[n + ph for n in lens0] for ph in phases]
+    ar = torch.arange(B, device=dev)
+    # new_k[c][t]: the token layer c appends at its t-th step, [B][Hkv][D].
+    new_k = torch.empty((ncopy, tokens, B, hkv, d), dtype=torch.float16, device=dev)
+    new_v = torch.empty_like(new_k)
+    for c in range(ncopy):
+        for t in range(tokens):
+            pos = torch.tensor([n + t for n in lens_c[c]], device=dev)
+            new_k[c, t] = k_all[ar, :, pos]
+            new_v[c, t] = v_all[ar, :, pos]
     q_all = torch.from_numpy(qh).to(dev).contiguous()
     cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
+    plan = K.decode_plan(cfg, B, max_groups)
+    flush_buf = torch.zeros(2**30, dtype=torch.uint8, device=dev)
+    flush_sink = torch.zeros(4, dtype=torch.int32, device=dev)
 
-    # ---- bulk seal (prefill) of layer 0, timed -----------------------------
+    def flush():
+        """Stream 1 GiB so that nothing a timed region reads is left in the
+        256 MB Infinity Cache by the work before it."""
+        probe.read(flush_buf, flush_sink)
+
+    # ---- bulk seal (prefill of the 32k prompt), timed -----------------------
     cache0 = K.KVarNCache(cfg, B, max_groups, device=dev)
     cache0.prefill(k_all, v_all, lens0)
     torch.cuda.synchronize()
     n_groups_seal = sum(hkv * ((n - 128) // 128) for n in lens0 if n > 128)
-    seal_reps = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(seal_reps):
-        cache0.prefill(k_all, v_all, lens0)
-    e1.record()
-    torch.cuda.synchronize()
-    t_prefill = e0.elapsed_time(e1) / 1e3 / seal_reps
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g_seal = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_seal, stream=stream):
+            cache0.prefill(k_all, v_all, lens0, stream=stream)
+    t_seals = _timed_replays(torch, stream, g_seal, 50)
+    del g_seal
+    t_prefill = float(np.median(t_seals))
     k_rec, v_rec = K.record_bytes(d, wl.k_bits), K.record_bytes(d, wl.v_bits)
     seal_bytes_per_group = 2 * 128 * d * 2 + k_rec + v_rec   # fp16 K+V tiles in, two records out
     sinkhorn_flops_per_group = 2 * 16 * 2 * 128 * d * 2        # 2 tiles x 16 iters x 2 mat-vecs x T*D FMAs
@@ -434,13 +498,17 @@ def main():
         "groups_per_s": n_groups_seal / t_prefill,
         "groups_per_call": n_groups_seal,
         "ms_per_call": t_prefill * 1e3,
+        "us_per_call_stats": {k: (v * 1e6 if k != "reps" else v) for k, v in _stats(t_seals).items()},
         "hbm_GBps": n_groups_seal * seal_bytes_per_group / t_prefill / 1e9,
         "hbm_frac": n_groups_seal * seal_bytes_per_group / t_prefill / HBM_PEAK,
         "sinkhorn_valu_frac": n_groups_seal * sinkhorn_flops_per_group / t_prefill / VALU_FP32_PEAK,
-        "note": "bulk ingest via kvarn_prefill (sink/tail copy + seal kernel), K and V tiles",
+        "valu_peak_TFLOPs": VALU_FP32_PEAK / 1e12,
+        "valu_ceiling_groups_per_s": VALU_FP32_PEAK / sinkhorn_flops_per_group,
+        "note": "bulk ingest via kvarn_prefill (sink/tail copy + seal kernel), K and V tiles; median of 50 "
+                "graph replays; VALU fraction of the Sinkhorn FMAs against the non-packed fp32 peak",
     }
-    print(f"[bench] seal: {seal['groups_per_s'] / 1e6:.2f} M groups/s ({seal['hbm_frac'] * 100:.1f}% of HBM)",
-          file=sys.stderr, flush=True)
+    print(f"[bench] seal: {seal['groups_per_s'] / 1e6:.2f} M groups/s ({seal['hbm_frac'] * 100:.1f}% of HBM, "
+          f"{seal['sinkhorn_valu_frac'] * 100:.1f}% of the VALU peak)", file=sys.stderr, flush=True)
 
     # ---- record -> fp16 conversion of every record slot of layer 0, timed ----
     gb = k_rec + v_rec
@@ -450,6 +518,7 @@ def main():
         K.dequant_records(slots[:, lo:], d, bits, kind, out=dq_out)
     torch.cuda.synchronize()
     dq_reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(dq_reps):
         for kind, lo, bits in (("k", 0, wl.k_bits), ("v", k_rec, wl.v_bits)):
@@ -465,26 +534,25 @@ def main():
     print(f"[bench] record -> fp16: {dequant['hbm_GBps']:.0f} GB/s ({dequant['hbm_frac'] * 100:.1f}% of HBM)",
           file=sys.stderr, flush=True)
 
-    # ---- layer caches ----------------------------------------------------
+    # ---- layer caches at their phases -------------------------------------
     caches = [cache0]
     for c in range(1, ncopy):
-        cc = K.KVarNCache(cfg, B, max_groups, device=dev)
-        for name in ("sink_k", "sink_v", "tail_k", "tail_v", "records", "seq_len"):
-            getattr(cc, name).copy_(getattr(cache0, name))
-        caches.append(cc)
-    seq0 = cache0.seq_len.clone()
+        caches.append(K.KVarNCache(cfg, B, max_groups, device=dev))
+    for c in range(ncopy):
+        caches[c].prefill(k_all, v_all, lens_c[c])
+    seq0 = [c.seq_len.clone() for c in caches]
     outs = [torch.empty(B, hq, d, dtype=torch.float32, device=dev) for _ in range(ncopy)]
     torch.cuda.synchronize()
 
     def reset():
-        for c in caches:
-            c.seq_len.copy_(seq0)
+        for c, s0 in zip(caches, seq0):
+            c.seq_len.copy_(s0)
 
     def step(s):
-        c = caches[s % ncopy]
+        c = s % ncopy
         tok = s // ncopy
-        c.append_seal(new_k[tok], new_v[tok])
-        c.decode_attn(q_all[tok], out=outs[s % ncopy])
+        caches[c].append_seal(new_k[c, tok], new_v[c, tok])
+        caches[c].decode_attn(q_all[tok], out=outs[c])
 
     if args.profile_steps > 0:
         for s in range(args.profile_steps):
@@ -494,7 +562,6 @@ def main():
         return
 
     # ---- graphs ------------------------------------------------------------
-    stream = torch.cuda.Stream()
     def capture(nsteps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
@@ -513,6 +580,7 @@ def main():
         g_warm.replay()
         torch.cuda.synchronize()
     reset()
+    flush()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -521,30 +589,34 @@ def main():
         ev1.record(stream)
     torch.cuda.synchronize()
     t_total = ev0.elapsed_time(ev1) / 1e3
+    seals_timed = sum(1 for s in range(args.steps)
+                      if (lens_c[s % ncopy][0] + s // ncopy + 1 - 128) % 128 == 0)
     steps_per_s = args.steps / t_total
     value = B * steps_per_s
+    # The same K steps again, 50 times (lengths reset, Infinity Cache flushed
+    # before each): distribution of the per-step time.
+    t_step_reps = _timed_replays(torch, stream, g_main, 50, before=lambda: (reset(), flush()), per=args.steps)
+    del g_main, g_warm
 
     # ---- live timing of the dominant kernel (the split kernel) and the combine
-    def time_graph(fn):
+    def time_graph(fn, reps_graph=50):
         reset()
         torch.cuda.synchronize()
-        reps = 8 * ncopy
+        n = 8 * ncopy
         gk = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gk, stream=stream):
-            for r in range(reps):
+            for r in range(n):
                 fn(r)
         torch.cuda.synchronize()
         gk.replay()  # warm
         torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            gk.replay()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / 1e3 / reps
+        ts = _timed_replays(torch, stream, gk, reps_graph, per=n)
+        del gk
+        return _stats(ts)
 
-    t_kernel = time_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]))
-    t_combine = time_graph(lambda r: caches[r % ncopy].decode_combine(outs[r % ncopy]))
+    st_kernel = time_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]))
+    st_combine = time_graph(lambda r: caches[r % ncopy].decode_combine(outs[r % ncopy]))
+    t_kernel, t_combine = st_kernel["median"], st_combine["median"]
 
     # ---- one streaming seal event (the append that completes a group, K and
     # V of every KV head sealed in the same launch) against an append that
@@ -555,6 +627,7 @@ def main():
     def set_len(n):
         for c in caches:
             c.seq_len.fill_(n)
+    saved_tails = [(c.tail_k.clone(), c.tail_v.clone()) for c in caches]
     for c in caches:   # the prompt's last 127 tokens stand in for the tail
         c.tail_k[:, :, :127].copy_(k_all[:, :, lens0[0] - 127:lens0[0]])
         c.tail_v[:, :, :127].copy_(v_all[:, :, lens0[0] - 127:lens0[0]])
@@ -565,52 +638,52 @@ def main():
         gs = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gs, stream=stream):
             for r in range(ncopy):
-                caches[r].append_seal(new_k[0], new_v[0])
-        set_len(n)
-        torch.cuda.synchronize()
-        gs.replay()
-        set_len(n)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            gs.replay()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        ev_times[label] = ev0.elapsed_time(ev1) * 1e3 / ncopy
+                caches[r].append_seal(new_k[0, 0], new_v[0, 0])
+        ts = _timed_replays(torch, stream, gs, 50, before=lambda: set_len(n), per=ncopy)
+        ev_times[label] = _stats([t * 1e6 for t in ts])
         del gs
         n_after = int(caches[-1].seq_len[0].item())
         if n_after != n + 1:
             raise RuntimeError(f"{label}: length {n_after} after the append, expected {n + 1}")
+    for c, (tk, tv) in zip(caches, saved_tails):
+        c.tail_k.copy_(tk)
+        c.tail_v.copy_(tv)
+    del saved_tails
     reset()
-    seal_event = {"us_seal_event": ev_times["seal_event"], "us_append_only": ev_times["append_only"],
+    seal_event = {"us_seal_event": ev_times["seal_event"]["median"],
+                  "us_append_only": ev_times["append_only"]["median"],
+                  "seal_event_stats_us": ev_times["seal_event"], "append_only_stats_us": ev_times["append_only"],
                   "tiles": 2 * B * hkv,
                   "note": "kvarn_append_seal launches back to back in a graph over the layer caches: each "
-                          "completes a group (K and V of every KV head sealed) vs each only appends"}
+                          "completes a group (K and V of every KV head sealed) vs each only appends; "
+                          "median of 50 replays"}
     print(f"[bench] seal event: {seal_event['us_seal_event']:.2f} us per append+seal launch that seals "
           f"{2 * B * hkv} tiles; {seal_event['us_append_only']:.2f} us when nothing is due",
           file=sys.stderr, flush=True)
 
-    # ---- streaming-read ceiling: the library's plain read kernel over 4 GiB
+    # ---- streaming-read ceiling: the plain read probe over 4 GiB
     # (reported beside the 8 TB/s peak; not the target)
+    del flush_buf
     rd = torch.zeros(2**32, dtype=torch.uint8, device=dev)
-    rd_sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    K.read_probe(rd, rd_sink)
+    probe.read(rd, flush_sink)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(5):
-        K.read_probe(rd, rd_sink)
+        probe.read(rd, flush_sink)
     e1.record()
     torch.cuda.synchronize()
     read_ceiling = rd.numel() * 5 / (e0.elapsed_time(e1) / 1e3)
-    del rd, rd_sink
-    print(f"[bench] streaming-read ceiling (kvarn_read_probe over 4 GiB): {read_ceiling / 1e12:.2f} TB/s",
+    del rd
+    print(f"[bench] streaming-read ceiling (read probe over 4 GiB): {read_ceiling / 1e12:.2f} TB/s",
           file=sys.stderr, flush=True)
-    bytes_launch = algorithmic_decode_bytes(wl, lens0, k_rec, v_rec)
+    # Algorithmic bytes of one split-kernel launch, averaged over the layer
+    # caches the timing graph rotates over (their phases differ in tail length).
+    bytes_launch = float(np.mean([algorithmic_decode_bytes(wl, lens_c[c], k_rec, v_rec) for c in range(ncopy)]))
     achieved = bytes_launch / t_kernel
     traffic = read_traffic(wl.name)
     print(f"[bench] decode split kernel: {t_kernel * 1e6:.2f} us/launch, {achieved / 1e12:.2f} TB/s "
           f"({achieved / HBM_PEAK * 100:.1f}% of HBM); combine {t_combine * 1e6:.2f} us; "
-          f"step {t_total / args.steps * 1e6:.2f} us", file=sys.stderr, flush=True)
+          f"step {t_total / args.steps * 1e6:.2f} us; plan {plan}", file=sys.stderr, flush=True)
 
     # ---- the same split kernel over paged records: every layer cache's
     # records moved to a shuffled block table over a pool with spare blocks.
@@ -630,9 +703,11 @@ def main():
     pdiff = (paged[0].decode_attn(q_all[0]) - caches[0].decode_attn(q_all[0])).abs().max().item()
     if not pdiff <= 1e-5:
         raise RuntimeError(f"paged decode differs from the contiguous one by {pdiff}")
-    t_paged = time_graph(lambda r: paged[r % ncopy].decode_partial(q_all[0]))
+    st_paged = time_graph(lambda r: paged[r % ncopy].decode_partial(q_all[0]))
+    t_paged = st_paged["median"]
     paged_line = {"us_per_launch": t_paged * 1e6, "GBps": bytes_launch / t_paged / 1e9,
                   "frac": bytes_launch / t_paged / HBM_PEAK,
+                  "us_stats": {k: (v * 1e6 if k != "reps" else v) for k, v in st_paged.items()},
                   "note": f"decode split kernel, records behind a shuffled block table over {nblk} blocks"}
     del paged
     print(f"[bench] paged records: split kernel {t_paged * 1e6:.2f} us/launch "
@@ -640,13 +715,14 @@ def main():
 
     others = {}
     for name in [x for x in args.other_workloads.split(",") if x and x != wl.name]:
-        others[name] = measure_workload(torch, K, synth, dev, name, args.other_steps)
+        others[name] = measure_workload(torch, K, probe, synth, dev, name, args.other_steps)
         o = others[name]
         print(f"[bench] {name}: {o['tokens_per_s']:.0f} tokens/s, step {o['ms_per_step'] * 1e3:.1f} us, split "
               f"{o['roofline']['us_per_launch']:.1f} us = {o['roofline']['achieved']:.0f} GB/s "
               f"({o['roofline']['frac'] * 100:.1f}% of HBM); seal {o['seal']['groups_per_s'] / 1e6:.2f} M groups/s",
               file=sys.stderr, flush=True)
 
+    us = lambda st: {k: (v * 1e6 if k != "reps" else v) for k, v in st.items()}
     line = {
         "metric": "quantized decode-attn tokens/s + % HBM peak; seal_group groups/s (1 MI355X)",
         "value": value,
@@ -662,11 +738,16 @@ def main():
         "data": "synthetic (seeded K/V/q with outlier channels and lognormal token norms)",
         "config": {"workload": wl.name, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
                    "context": lens0[0], "k_bits": wl.k_bits, "v_bits": wl.v_bits, "layer_caches": ncopy,
+                   "tail_phase": f"layer c starts 127 - floor(128 c / {ncopy}) tokens into its tail",
+                   "max_groups": max_groups, "seals_in_timed_steps": seals_timed,
                    "step": "append + seal-if-due + decode attention (one layer)"},
+        "step_us_stats": us(_stats(t_step_reps)),
+        "decode_plan": plan,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
                      "kernel": "decode_split_kernel", "bytes_per_launch": bytes_launch,
-                     "us_per_launch": t_kernel * 1e6, "combine_us_per_launch": t_combine * 1e6,
+                     "us_per_launch": t_kernel * 1e6, "us_stats": us(st_kernel),
+                     "combine_us_per_launch": t_combine * 1e6, "combine_us_stats": us(st_combine),
                      "read_ceiling_GBps": read_ceiling / 1e9, "frac_of_read_ceiling": achieved / read_ceiling},
         "seal_event": seal_event,
         "seal": seal,

@@ -125,6 +125,16 @@ size_t kvarn_group_bytes(const kvarn_config *cfg);
 /* Workspace that kvarn_decode_attn needs for this batch and max_groups. */
 size_t kvarn_decode_workspace_bytes(const kvarn_config *cfg, int32_t batch, int32_t max_groups);
 
+/*
+ * The launch plan kvarn_decode_attn uses for this configuration, batch and
+ * max_groups on the current device (a device-free plan if there is none):
+ * out (host int32 [5]) = {record splits per (request, KV head), exact splits
+ * per (request, KV head), groups per wave at most, record workgroups, exact
+ * workgroups}.  The plan depends on the capacity (max_groups), not on the
+ * lengths, so every call on one cache launches the same grid.
+ */
+kvarn_status kvarn_decode_plan(const kvarn_config *cfg, int32_t batch, int32_t max_groups, int32_t *out);
+
 /* Message of the last error on this thread ("" if none). */
 const char *kvarn_last_error(void);
 
@@ -139,24 +149,43 @@ const char *kvarn_status_string(kvarn_status s);
  * token goes to sink[n] if n < 128, else to tail[(n-128) mod 128]; then
  * seq_len[b] = n+1.  A request whose cache is full (n >= 128 +
  * 128*max_groups + 127, so the token would complete a group that has no
- * record slot) is left unchanged.  Call
- * kvarn_seal_group after every append so a full tail is sealed before the
- * next append overwrites it.
+ * record slot) is left unchanged.  Call kvarn_seal_group after every append
+ * so a full tail is sealed before the next append overwrites it.  Between
+ * the two calls, do not decode: decoding counts a group as sealed as soon as
+ * seq_len covers it, so it would read that group's record before it is
+ * written (and no longer read the tail).  kvarn_append_seal does both in one
+ * launch and has no such window.
  */
 kvarn_status kvarn_append(const kvarn_config *cfg, const kvarn_cache *cache,
                           const void *k_new, const void *v_new, void *stream);
 
 /*
- * Seal on arrival [P2 §2.1]: every request b whose newest token completed a
- * group (n = seq_len[b] >= 256 and (n-128) mod 128 == 0) has group
- * g = (n-128)/128 - 1 quantized from its tail into record g, for every KV
- * head, K and V: Hadamard rotation, `sinkhorn_iters` alternating token and
- * channel RMS rescalings, per-token round to nearest [P1 "What it is"; P2 §1].
- * The tail then counts as empty (no data moves).  Other requests are
- * untouched.  seq_len is read on the device, so no host synchronization is
- * needed.
+ * Seal on arrival [P2 §2.1: a group is quantized the moment its last token
+ * arrives].  The group sealed for request b is the one whose 128 tokens fill
+ * its tail: with n = seq_len[b] (read on the device, so no host
+ * synchronization is needed), the newest token completed group
+ * g = (n-128)/128 - 1 when n >= 256 and (n-128) mod 128 == 0.  That group is
+ * quantized from the tail into record g for every KV head, K and V: Hadamard
+ * rotation, `sinkhorn_iters` alternating token and channel RMS rescalings,
+ * per-token round to nearest [P1 "What it is"; P2 §1].  The tail then counts
+ * as empty (no data moves).
+ *
+ * Two forms:
+ *   - Predicate form: d_req == NULL, d_group == NULL, n == batch.  Every
+ *     request whose tail just filled is sealed; the others are untouched.
+ *   - List form: d_req, d_group: device int32 [n].  Entry i asks to seal
+ *     group d_group[i] of request d_req[i]; it is carried out only if that
+ *     group is the one whose tokens fill the request's tail (see above), and
+ *     skipped otherwise (stale or future groups, requests outside
+ *     [0, batch)), so a wrong list never writes a record from the wrong
+ *     tokens.  Entries may come in any order; a repeated entry writes the
+ *     same bytes twice.  One workgroup per entry, KV head and K|V, so a
+ *     caller that knows which requests are due launches only those.
+ * n == 0 (an empty list; its pointers may then be NULL) or max_groups == 0
+ * queues nothing.
  */
-kvarn_status kvarn_seal_group(const kvarn_config *cfg, const kvarn_cache *cache, void *stream);
+kvarn_status kvarn_seal_group(const kvarn_config *cfg, const kvarn_cache *cache,
+                              const int32_t *d_req, const int32_t *d_group, int32_t n, void *stream);
 
 /*
  * kvarn_append followed by kvarn_seal_group, in one launch (one workgroup
@@ -238,18 +267,6 @@ kvarn_status kvarn_seal_tiles(int32_t head_dim, int32_t bits, int32_t kind, int3
 kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
                                    const void *src, int64_t src_stride, void *dst,
                                    int32_t n, void *stream);
-
-/*
- * Measurement aid (no KVarN computation): stream `bytes` bytes of device
- * memory at `buf` (16-byte aligned, bytes a multiple of 16) through a plain
- * read kernel (32 workgroups per CU), each thread reading 16-byte pieces with
- * nontemporal loads in a grid-stride loop.  The data are combined so that the loads cannot be
- * dropped; `sink` (device, 4 bytes) is written only if the combination of a
- * thread's data equals an improbable constant, so the kernel's traffic is
- * the reads.  Timing it gives the achievable streaming-read bandwidth, the
- * ceiling reported beside the HBM peak for the decode kernel.
- */
-kvarn_status kvarn_read_probe(const void *buf, size_t bytes, void *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,8 +1,10 @@
 """Build libkvarn.so (HIP, gfx950) in-tree with hipcc.
 
 Each source compiles to an object in ``_build/`` (in parallel), then one link
-step produces ``kv_cache_quantization_seal_amd/libkvarn.so``.  Packed fp32
-instructions are disabled for every HIP translation unit.
+step produces ``kv_cache_quantization_seal_amd/libkvarn.so``.  The read probe
+(a measurement aid with no KVarN computation) links into its own
+``libkvarn_probe.so``.  Packed fp32 instructions are disabled for every HIP
+translation unit.
 """
 from __future__ import annotations
 
@@ -16,9 +18,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvarn.so")
+PROBE_LIB = os.path.join(PKG, "libkvarn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip"]
+PROBE_SOURCES = ["read_probe.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -42,20 +46,40 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def _stale(src: str) -> bool:
+    """True if src's object is missing or older than src or any header."""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".hpp")]
+    deps.append(os.path.join(ROOT, "include", "kvarn.h"))
+    return max(os.path.getmtime(p) for p in deps) > os.path.getmtime(obj)
+
+
+def build(verbose: bool = False, changed_only: bool = False) -> str:
+    """Compile every source (or, with changed_only, those whose object is
+    older than the source or a header) and link both libraries."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    todo = [s for s in srcs if _stale(s)] if changed_only else srcs
+    objs = {s: os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in srcs}
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(len(todo), os.cpu_count() or 1))) as ex:
+        list(ex.map(_compile, todo))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, changed_only="--changed" in sys.argv)

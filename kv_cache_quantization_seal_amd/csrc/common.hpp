@@ -49,21 +49,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<0x140>(v);
   return v;
 }
-// Maximum over the whole wave of an unsigned value (or of a non-negative
-// float's bit pattern, which orders like the value): DPP within each row,
-// then the four row results through scalar registers.  All lanes active.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, true));
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, true));
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, true));
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, true));
-  const uint32_t r0 = __builtin_amdgcn_readlane(u, 0), r1 = __builtin_amdgcn_readlane(u, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(u, 32), r3 = __builtin_amdgcn_readlane(u, 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  return __uint_as_float(wave_max_u32(__float_as_uint(v)));
-}
 // Sum of v over lanes l and l^16 (resp. l^32), in every lane, through the
 // gfx950 row/half swaps (no LDS traffic).
 __device__ __forceinline__ float xor16_sum(float v) {
@@ -87,23 +72,6 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   v = row16_sum(v);
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
-__device__ __forceinline__ float xor16_max(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // Position p (0..15) of an unpacked 16-code block -> code index within the
 // block, for the unpacking used by the decode kernel:
 //   2-bit: dword w -> bytes (w >> 2k) & 0x03030303, k = 0..3: byte b of
@@ -200,26 +168,6 @@ __device__ __forceinline__ uint32_t pack_low_bytes(float a, float b, float c, fl
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Split x (|x| <= 127.5) into three int8 limbs a0 + a1/254 + a2/254^2 with
-// round-to-nearest at each level; returns the limbs as exact floats.
-__device__ __forceinline__ void limbs3(float x, float& a0, float& a1, float& a2) {
-  a0 = rintf(x);
-  float r1 = (x - a0) * 254.0f;
-  a1 = rintf(r1);
-  float r2 = (r1 - a1) * 254.0f;
-  a2 = rintf(r2);
-}
-
-// Pack four exact small integers (as floats, in [-128, 127]) into one dword of
-// int8 bytes (byte 0 = first).
-__device__ __forceinline__ uint32_t pack4_i8(float a, float b, float c, float d) {
-  const uint32_t x0 = (uint32_t)((int)a) & 0xFFu;
-  const uint32_t x1 = (uint32_t)((int)b) & 0xFFu;
-  const uint32_t x2 = (uint32_t)((int)c) & 0xFFu;
-  const uint32_t x3 = (uint32_t)((int)d) & 0xFFu;
-  return x0 | (x1 << 8) | (x2 << 16) | (x3 << 24);
-}
-
 
 // Workgroup barrier that orders LDS accesses only: global loads and stores
 // issued before it stay in flight (a full __syncthreads also makes this
@@ -240,53 +188,5 @@ __device__ __forceinline__ void lds_barrier() {
 // row, for eight lanes reading one group of rows t, t+16, ..., t+112, and for
 // eight lanes of consecutive rows (the row pitch moves them one quad each).
 __device__ __forceinline__ int xgrp(int g, int t) { return g ^ (((g >> 3) ^ (t >> 4)) & 7); }
-
-// Natural-order Sylvester Hadamard transform (unnormalized) of token rows held
-// as 64-channel slices: thread (t, rb) holds channels [64 rb, 64 rb + 64) of
-// token t in x.  The butterflies over the six low channel-index bits run in
-// registers; for D > 64 the block-index bits are combined through LDS
-// (xs = [128][P] fp32 scratch, which this overwrites; with SWZ its 16-byte
-// groups sit at xgrp positions).  Contains barriers: all threads of the block
-// must call it.
-template <int D, int P, bool SWZ = false>
-__device__ __forceinline__ void rotate_row_slice(float (&x)[64], float* xs, int t, int rb) {
-  constexpr int NB = D / 64;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if (!(i & s)) {
-        const float a = x[i], b = x[i + s];
-        x[i] = a + b;
-        x[i + s] = a - b;
-      }
-    }
-  }
-  if constexpr (NB > 1) {
-    auto grp = [&](int g) { return xs + t * P + 4 * (SWZ ? xgrp(g, t) : g); };
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      *reinterpret_cast<float4*>(grp(16 * rb + k)) = make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
-    __syncthreads();
-    // y_{64 rb + i} = sum_o (-1)^popcount(rb & o) x_{64 o + i}
-    const float own = (__popc(rb) & 1) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] *= own;
-#pragma unroll
-    for (int o = 0; o < NB; ++o) {
-      if (o == rb) continue;
-      const float sg = (__popc(rb & o) & 1) ? -1.0f : 1.0f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float4 q = *reinterpret_cast<const float4*>(grp(16 * o + k));
-        x[4 * k] = fmaf(sg, q.x, x[4 * k]);
-        x[4 * k + 1] = fmaf(sg, q.y, x[4 * k + 1]);
-        x[4 * k + 2] = fmaf(sg, q.z, x[4 * k + 2]);
-        x[4 * k + 3] = fmaf(sg, q.w, x[4 * k + 3]);
-      }
-    }
-    __syncthreads();
-  }
-}
 
 }  // namespace kvarn

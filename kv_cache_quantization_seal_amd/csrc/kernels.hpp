@@ -100,6 +100,9 @@ struct SealStreamArgs {
   const __half* tail_k;
   const __half* tail_v;
   const int32_t* seq_len;
+  const int32_t* req;    // NULL: workgroup x / hkv is the request (the predicate form)
+  const int32_t* group;  // with req: the group each entry names
+  int batch;
   uint8_t* records;
   RecordMap map;
   int64_t group_bytes;
@@ -187,6 +190,7 @@ hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* d
                              int iters, hipStream_t st);
 hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& a, int max_groups_in_batch, int nbh,
                                hipStream_t st);
+// nbh = entries * hkv (entries = batch in the predicate form, n in the list form).
 hipError_t launch_seal_stream(int D, int kb, int vb, const SealStreamArgs& a, int nbh, hipStream_t st);
 hipError_t launch_append_seal(int D, int kb, int vb, const AppendSealArgs& a, int nbh, hipStream_t st);
 hipError_t launch_append(int D, const CacheArgs& c, const void* k, const void* v, hipStream_t st);
@@ -194,7 +198,6 @@ hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const v
                                const PrefillLens& lens, int b0, int nb, hipStream_t st);
 // phases: 1 = split kernel (partials into the workspace), 2 = combine kernel, 3 = both.
 hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int phases, hipStream_t st);
-hipError_t launch_read_probe(const void* buf, size_t bytes, void* sink, int cus, hipStream_t st);
 hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
                           hipStream_t st);
 

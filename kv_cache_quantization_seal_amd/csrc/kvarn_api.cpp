@@ -135,6 +135,24 @@ size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int3
       .ws_bytes;
 }
 
+kvarn_status kvarn_decode_plan(const kvarn_config* cfg, int32_t batch, int32_t max_groups, int32_t* out) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if (!out) return fail(KVARN_EINVAL, "out must be non-NULL");
+  if (batch <= 0 || max_groups < 0) return fail(KVARN_EINVAL, "batch must be > 0 and max_groups >= 0");
+  const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
+                                                  cfg->num_q_heads / cfg->num_kv_heads);
+  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch,
+                                                 max_groups, resident, kvarn::decode_cu_count());
+  const int64_t pairs = (int64_t)batch * cfg->num_kv_heads;
+  out[0] = p.n_rec_splits;
+  out[1] = p.n_exact_splits;
+  out[2] = p.groups_per_wave;
+  out[3] = (int32_t)(pairs * p.n_rec_splits);
+  out[4] = (int32_t)(pairs * p.n_exact_splits);
+  return ok();
+}
+
 const char* kvarn_last_error(void) { return g_err; }
 
 const char* kvarn_status_string(kvarn_status s) {
@@ -198,16 +216,30 @@ kvarn_status kvarn_append_seal(const kvarn_config* cfg, const kvarn_cache* cache
                     "kvarn_append_seal launch");
 }
 
-kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache, void* stream) {
+kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache, const int32_t* d_req,
+                              const int32_t* d_group, int32_t n, void* stream) {
   kvarn_status s = check_cfg(cfg);
   if (s != KVARN_OK) return s;
   if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (n < 0) return fail(KVARN_EINVAL, "n must be >= 0 (got %d)", n);
+  if (n == 0) return ok();  // an empty list (its pointers may be NULL): nothing to queue
+  if (!d_req != !d_group) return fail(KVARN_EINVAL, "d_req and d_group must both be NULL or both be non-NULL");
+  if (!d_req && n != cache->batch)
+    return fail(KVARN_EINVAL, "the predicate form (d_req NULL) needs n == batch (got n %d, batch %d)", n,
+                cache->batch);
+  if (d_req && (!aligned(d_req, 4) || !aligned(d_group, 4)))
+    return fail(KVARN_EINVAL, "d_req and d_group must be 4-byte aligned");
   if (cache->max_groups == 0) return ok();
+  const int64_t nbh = (int64_t)n * cfg->num_kv_heads;
+  if (nbh > 0x7fffffff) return fail(KVARN_ERANGE, "n * num_kv_heads too large");
   const kvarn::CacheArgs c = cache_args(cfg, cache);
   kvarn::SealStreamArgs a;
   a.tail_k = c.tail_k;
   a.tail_v = c.tail_v;
   a.seq_len = c.seq_len;
+  a.req = d_req;
+  a.group = d_group;
+  a.batch = cache->batch;
   a.records = (uint8_t*)cache->records;
   a.map = c.map;
   a.group_bytes = c.group_bytes;
@@ -215,8 +247,6 @@ kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache,
   a.hkv = c.hkv;
   a.max_groups = c.max_groups;
   a.iters = cfg->sinkhorn_iters;
-  const int64_t nbh = (int64_t)cache->batch * cfg->num_kv_heads;
-  if (nbh > 0x7fffffff) return fail(KVARN_ERANGE, "batch * num_kv_heads too large");
   return hip_status(kvarn::launch_seal_stream(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, (int)nbh,
                                               (hipStream_t)stream),
                     "kvarn_seal_group launch");
@@ -362,15 +392,6 @@ kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
     return fail(KVARN_EINVAL, "src_stride must be >= the record size and a multiple of 16");
   return hip_status(kvarn::launch_dequant(head_dim, bits, kind, src, src_stride, dst, n, (hipStream_t)stream),
                     "kvarn_dequant_records launch");
-}
-
-kvarn_status kvarn_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
-  if (bytes == 0) return ok();
-  if (!buf || !sink) return fail(KVARN_EINVAL, "buf and sink must be non-NULL");
-  if (!aligned(buf, 16) || bytes % 16) return fail(KVARN_EINVAL, "buf must be 16-byte aligned and bytes a multiple of 16");
-  if (!aligned(sink, 4)) return fail(KVARN_EINVAL, "sink must be 4-byte aligned");
-  return hip_status(kvarn::launch_read_probe(buf, bytes, sink, kvarn::decode_cu_count(), (hipStream_t)stream),
-                    "kvarn_read_probe launch");
 }
 
 }  // extern "C"

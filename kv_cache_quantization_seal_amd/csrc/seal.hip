@@ -490,19 +490,26 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
     seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
 }
 
+// Seal on arrival.  Workgroup (entry, KV head, K|V): in the predicate form
+// the entry is request x / hkv; in the list form it is list entry x / hkv,
+// naming request req[i] and group group[i].  Either way the group sealed is
+// the one whose 128 tokens fill the request's tail, g = (n - 128) / 128 - 1
+// with n = seq_len[b] >= 256 and (n - 128) % 128 == 0; a list entry naming
+// another group, or a request outside [0, batch), is skipped.
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealStreamArgs a) {
   __shared__ SealSmem<D> sm;
-  const int bh = blockIdx.x;
+  const int e = blockIdx.x / a.hkv, h = blockIdx.x - (blockIdx.x / a.hkv) * a.hkv;
   const int kind = blockIdx.y;
-  const int b = bh / a.hkv;
+  const int b = a.req ? a.req[e] : e;
+  if (b < 0 || b >= a.batch) return;
   const int n = a.seq_len[b];
   if (n < kSink + kGroup || ((n - kSink) % kGroup) != 0) return;
   const int g = (n - kSink) / kGroup - 1;
-  if (g >= a.max_groups) return;
-  const int64_t off = pair_offset(a.map, b, bh - b * a.hkv, g, a.hkv, a.max_groups, a.group_bytes);
+  if (g >= a.max_groups || (a.req && a.group[e] != g)) return;
+  const int64_t off = pair_offset(a.map, b, h, g, a.hkv, a.max_groups, a.group_bytes);
   if (off < 0) return;
-  const __half* src = (kind ? a.tail_v : a.tail_k) + (int64_t)bh * kGroup * D;
+  const __half* src = (kind ? a.tail_v : a.tail_k) + ((int64_t)b * a.hkv + h) * kGroup * D;
   uint8_t* rec = a.records + off + (kind ? a.rec_k_bytes : 0);
   uint4 raw[4];
   load_tile<D>(raw, src, threadIdx.x);

@@ -21,10 +21,11 @@ SINK = 128
 SINKHORN_ITERS = 16
 EXPORTS = (
     "kvarn_check_config", "kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
+    "kvarn_decode_plan",
     "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
     "kvarn_prefill",
     "kvarn_decode_attn", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
-    "kvarn_dequant_records", "kvarn_read_probe",
+    "kvarn_dequant_records",
 )
 
 
@@ -64,19 +65,19 @@ def lib():
         L.kvarn_group_bytes.restype = sz
         L.kvarn_decode_workspace_bytes.argtypes = [cp(Config), i32, i32]
         L.kvarn_decode_workspace_bytes.restype = sz
+        L.kvarn_decode_plan.argtypes = [cp(Config), i32, i32, cp(i32)]
         L.kvarn_last_error.restype = ctypes.c_char_p
         L.kvarn_status_string.argtypes = [ctypes.c_int]
         L.kvarn_status_string.restype = ctypes.c_char_p
         L.kvarn_append.argtypes = [cp(Config), cp(CacheView), vp, vp, vp]
         L.kvarn_append_seal.argtypes = [cp(Config), cp(CacheView), vp, vp, vp]
-        L.kvarn_seal_group.argtypes = [cp(Config), cp(CacheView), vp]
+        L.kvarn_seal_group.argtypes = [cp(Config), cp(CacheView), vp, vp, i32, vp]
         L.kvarn_prefill.argtypes = [cp(Config), cp(CacheView), vp, vp, i64, cp(i32), vp]
         L.kvarn_decode_attn.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp, sz, vp]
         L.kvarn_decode_attn_partial.argtypes = [cp(Config), cp(CacheView), vp, f32, vp, sz, vp]
         L.kvarn_decode_attn_combine.argtypes = [cp(Config), cp(CacheView), vp, vp, sz, vp]
         L.kvarn_seal_tiles.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp, i32, vp]
         L.kvarn_dequant_records.argtypes = [i32, i32, i32, vp, i64, vp, i32, vp]
-        L.kvarn_read_probe.argtypes = [vp, sz, vp, vp]
         for name in EXPORTS:
             if name not in ("kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
                             "kvarn_last_error", "kvarn_status_string"):
@@ -128,6 +129,14 @@ def check_config(cfg: Config) -> int:
 
 def decode_workspace_bytes(cfg: Config, batch: int, max_groups: int) -> int:
     return int(lib().kvarn_decode_workspace_bytes(ctypes.byref(cfg), batch, max_groups))
+
+
+def decode_plan(cfg: Config, batch: int, max_groups: int) -> dict:
+    """The decode launch plan on the current device (see kvarn_decode_plan)."""
+    out = (ctypes.c_int32 * 5)()
+    _check(lib().kvarn_decode_plan(ctypes.byref(cfg), batch, max_groups, out))
+    return {"record_splits": out[0], "exact_splits": out[1], "groups_per_wave": out[2],
+            "record_workgroups": out[3], "exact_workgroups": out[4], "max_groups": max_groups}
 
 
 class KVarNCache:
@@ -191,8 +200,17 @@ class KVarNCache:
         _check(lib().kvarn_append_seal(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k_new), _ptr(v_new),
                                        _stream(stream)))
 
-    def seal_group(self, stream=None) -> None:
-        _check(lib().kvarn_seal_group(ctypes.byref(self.cfg), ctypes.byref(self.view), _stream(stream)))
+    def seal_group(self, req: Optional[torch.Tensor] = None, group: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+        """Seal every request whose tail just filled (no lists), or the listed
+        (request, group) entries (device int32 tensors of equal length)."""
+        if (req is None) != (group is None):
+            raise ValueError("req and group must be given together")
+        n = self.batch if req is None else int(req.numel())
+        if req is not None and (req.dtype != torch.int32 or group.dtype != torch.int32 or group.numel() != n):
+            raise ValueError("req and group must be int32 tensors of equal length")
+        _check(lib().kvarn_seal_group(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(req), _ptr(group), n,
+                                      _stream(stream)))
 
     def prefill(self, k: torch.Tensor, v: torch.Tensor, lengths: Sequence[int], stream=None) -> None:
         arr = (ctypes.c_int32 * self.batch)(*[int(x) for x in lengths])
@@ -249,12 +267,3 @@ def dequant_records(recs: torch.Tensor, head_dim: int, bits: int, kind: str, out
     _check(lib().kvarn_dequant_records(head_dim, bits, 0 if kind == "k" else 1, ctypes.c_void_p(recs.data_ptr()),
                                        recs.stride(0), _ptr(out), n, _stream(stream)))
     return out
-
-
-def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    """Stream every byte of `buf` (device, contiguous, 16-byte aligned) through
-    the library's plain read kernel (a measurement aid: the achievable
-    streaming-read bandwidth); `sink` is a device tensor of at least 4 bytes."""
-    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
-        raise ValueError("buf and sink must be contiguous device tensors")
-    _check(lib().kvarn_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))

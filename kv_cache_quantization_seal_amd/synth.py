@@ -59,6 +59,11 @@ class Workload:
     def max_len(self) -> int:
         return self.start_len(self.batch - 1) + self.steps
 
+    def max_groups(self) -> int:
+        """Record slots per request that hold every group the workload seals:
+        capacity 128 + 128 max_groups + 127 >= max_len()."""
+        return max(1, (self.max_len() - 128) // 128 + 1)
+
 
 # Shapes follow the model families the pages evaluate on
 # (KVarN summary page, "Key result": Qwen3-4B, Llama-3.1-8B, Phi-4-14B).

@@ -77,9 +77,17 @@ def test_entry_points_validate_before_launch():
     assert L.kvarn_append(r(cfg), r(_view(sink_k=None)), FAKE, FAKE, None) == K.EINVAL
     assert L.kvarn_append(r(cfg), r(_view(batch=0)), FAKE, FAKE, None) == K.EINVAL
     assert L.kvarn_append(r(cfg), r(_view(sink_v=FAKE + 2)), FAKE, FAKE, None) == K.EINVAL
-    assert L.kvarn_seal_group(r(cfg), r(_view(max_groups=-1)), None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view(max_groups=-1)), None, None, 2, None) == K.EINVAL
     bad = K.make_config(96, 32, 8, 2, 2)
-    assert L.kvarn_seal_group(r(bad), r(_view()), None) == K.EUNSUPPORTED
+    assert L.kvarn_seal_group(r(bad), r(_view()), None, None, 2, None) == K.EUNSUPPORTED
+    # Predicate form: n must be the batch; list form: both lists or neither.
+    assert L.kvarn_seal_group(r(cfg), r(_view()), None, None, 1, None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view()), FAKE, None, 1, None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view()), None, FAKE, 1, None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view()), FAKE, FAKE, -1, None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view()), FAKE + 2, FAKE, 1, None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view()), FAKE, FAKE, 0, None) == K.OK   # empty list: no launch
+    assert L.kvarn_seal_group(r(cfg), r(_view()), None, None, 0, None) == K.OK
     ws = K.decode_workspace_bytes(cfg, 2, 4)
     assert L.kvarn_decode_attn(r(cfg), r(_view()), FAKE, FAKE, 0.1, FAKE, ws - 1, None) == K.EWORKSPACE
     assert L.kvarn_decode_attn(r(cfg), r(_view()), FAKE, FAKE, 0.1, None, ws, None) == K.EWORKSPACE
@@ -149,7 +157,7 @@ def test_paged_view_validates_before_launch():
     r = ctypes.byref
     field_names = [f[0] for f in K.CacheView._fields_]
     assert field_names[-2:] == ["block_table", "num_blocks"]
-    assert L.kvarn_seal_group(r(cfg), r(_view(block_table=FAKE, num_blocks=0)), None) == K.EINVAL
+    assert L.kvarn_seal_group(r(cfg), r(_view(block_table=FAKE, num_blocks=0)), None, None, 2, None) == K.EINVAL
     assert L.kvarn_append_seal(r(cfg), r(_view(block_table=FAKE + 2, num_blocks=8)), FAKE, FAKE, None) == K.EINVAL
     ws = K.decode_workspace_bytes(cfg, 2, 4)
     assert L.kvarn_decode_attn(r(cfg), r(_view(block_table=FAKE, num_blocks=-1)), FAKE, FAKE, 0.1, FAKE, ws,
@@ -157,10 +165,14 @@ def test_paged_view_validates_before_launch():
 
 
 def test_read_probe_validates():
-    L = K.lib()
-    assert L.kvarn_read_probe(FAKE, 0, FAKE, None) == K.OK   # nothing to read: no launch
-    assert L.kvarn_read_probe(None, 16, FAKE, None) == K.EINVAL
-    assert L.kvarn_read_probe(FAKE, 16, None, None) == K.EINVAL
-    assert L.kvarn_read_probe(FAKE, 24, FAKE, None) == K.EINVAL
-    assert L.kvarn_read_probe(FAKE + 8, 16, FAKE, None) == K.EINVAL
-    assert L.kvarn_read_probe(FAKE, 16, FAKE + 2, None) == K.EINVAL
+    """The read probe (its own library, not the KVarN ABI) rejects bad
+    arguments before anything is queued."""
+    from kv_cache_quantization_seal_amd import probe
+    L = probe.lib()
+    assert L.kvarn_probe_read(FAKE, 0, FAKE, None) == 0   # nothing to read: no launch
+    assert L.kvarn_probe_read(None, 16, FAKE, None) == -1
+    assert L.kvarn_probe_read(FAKE, 16, None, None) == -1
+    assert L.kvarn_probe_read(FAKE, 24, FAKE, None) == -1
+    assert L.kvarn_probe_read(FAKE + 8, 16, FAKE, None) == -1
+    assert L.kvarn_probe_read(FAKE, 16, FAKE + 2, None) == -1
+    assert "kvarn_probe_read" not in K.EXPORTS

@@ -105,6 +105,50 @@ def test_append_seal_stream_and_decode(fused):
     assert worst <= ATTN_ATOL
 
 
+@pytest.mark.parametrize("d,kb,vb", [(128, 2, 2), (256, 4, 2)])
+def test_seal_group_list_form(d, kb, vb):
+    """The (request, group) list form seals exactly the listed groups whose
+    tokens fill their request's tail, in any order and with repeats; stale,
+    future, wrong and out-of-range entries write nothing.  The records match
+    the oracle's seal of the tail and the predicate form's bytes."""
+    hkv = 2
+    wl = synth.Workload("l", 82 + d, 4, hkv, hkv, d, 400, 0, kb, vb, 0)
+    k, v = _streams(wl, 400)
+    cfg = K.make_config(d, hkv, hkv, kb, vb)
+    lens0 = [255, 383, 200, 127]
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    caches = [K.KVarNCache(cfg, 4, 3) for _ in range(2)]
+    for c in caches:
+        c.prefill(kd, vd, lens0)
+        knew = torch.stack([kd[r, :, lens0[r]] for r in range(4)]).contiguous()
+        vnew = torch.stack([vd[r, :, lens0[r]] for r in range(4)]).contiguous()
+        c.append(knew, vnew)   # requests 0 and 1 now hold a full, unsealed tail (groups 0 and 1)
+        # Mark the record slots that hold no sealed group yet.
+        for r, g in [(0, 0), (1, 1), (0, 1), (2, 0), (3, 0), (1, 2)]:
+            for h in range(hkv):
+                for kind in ("k", "v"):
+                    c.record(r, h, g, kind).fill_(0xA5)
+    torch.cuda.synchronize()
+    lists = torch.tensor([[1, 0, 1, 2, 5, -1, 0, 3], [1, 0, 1, 0, 0, 0, 1, 0]], dtype=torch.int32, device="cuda")
+    caches[0].seal_group(lists[0].contiguous(), lists[1].contiguous())
+    caches[1].seal_group()   # predicate form
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    caches[0].seal_group(empty, empty)   # nothing queued
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].records, caches[1].records)
+    assert [int(x) for x in caches[0].seq_len.cpu()] == [256, 384, 201, 128]
+    for r, g in [(0, 0), (1, 1)]:
+        for h in range(hkv):
+            sl = slice(128 + 128 * g, 256 + 128 * g)
+            for kind, x, bits in (("k", k, kb), ("v", v, vb)):
+                rec = caches[0].record(r, h, g, kind).cpu().numpy().tobytes()
+                check_sealed_tile(rec, None, O.seal_tile(x[r, h, sl], bits), d, bits, kind)
+    for r, g in [(0, 1), (2, 0), (3, 0), (1, 2)]:
+        for h in range(hkv):
+            for kind in ("k", "v"):
+                assert bool((caches[0].record(r, h, g, kind) == 0xA5).all()), (r, g, h, kind)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_append_refuses_past_capacity(fused):
     d = 128
@@ -170,7 +214,8 @@ def test_read_probe_reads_and_writes_nothing():
     # an improbable xor of a thread's data, which all-ones pieces never give.
     buf = torch.full((1 << 22,), -1, dtype=torch.int32, device="cuda")
     sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
-    K.read_probe(buf, sink)
-    K.read_probe(buf[:4], sink)   # fewer pieces than threads of one workgroup
+    from kv_cache_quantization_seal_amd import probe
+    probe.read(buf, sink)
+    probe.read(buf[:4], sink)   # fewer pieces than threads of one workgroup
     torch.cuda.synchronize()
     assert sink.tolist() == [7, 7, 7, 7]

@@ -1,5 +1,8 @@
 """Full-size sampled parity: every workload at its real shape and batch, in
-the launch configuration the benchmark times.
+the launch configuration the benchmark times: the cache capacity is the
+workload's own (``Workload.max_groups``, which bench.py also uses, so both
+launch the same decode plan, printed here) and every decode step of the
+workload runs as one fused append-and-seal launch.
 
 The whole cache is built on the GPU (bulk prefill seal of every pair); the
 oracle then checks sampled (request, KV head) pairs end to end from the same
@@ -7,9 +10,10 @@ fp16 streams: its own seal of every group and its own decode attention,
 against the GPU's decode output (2e-3 max-abs), and the GPU records of a
 few sampled groups against the oracle's seal of those tiles (packing
 bit-exact, codes and scales per the tile rules).  The Llama-3.1-8B and
-Qwen3-4B shapes also run 128 decode steps first, each one fused
-append-and-seal launch (the benchmark's), over which every request seals one
-more group.
+Qwen3-4B shapes run their 256 decode steps (two more groups sealed per
+request), the long-context D 256 shape its 128 steps (one more group per
+request, streaming seal at K 4-bit / V 2-bit); the Phi-4 shape is steady-state
+attention.
 
 Pairs that are not sampled hold data from the device-side generator (same
 recipe, different draws); attention per pair is independent of the others.
@@ -26,26 +30,28 @@ from tests.gpu_util import ATTN_ATOL, check_sealed_tile
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # name: (sampled pairs, pseudo-decode steps)
-    "llama31_8b_32k": ([(0, 0), (0, 7)], 128),
-    "qwen3_4b_16k_b16": ([(0, 0), (15, 7)], 128),
-    "phi4_14b_32k_b8": ([(0, 0), (7, 9)], 0),
-    "longctx_d256_64k_b4": ([(3, 15)], 0),
+    # name: sampled (request, KV head) pairs; every case runs the workload's own steps
+    "llama31_8b_32k": [(0, 0), (0, 7)],
+    "qwen3_4b_16k_b16": [(0, 0), (15, 7)],
+    "phi4_14b_32k_b8": [(0, 0), (7, 9)],
+    "longctx_d256_64k_b4": [(3, 15), (0, 2)],
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_full_size_sampled(name):
     wl = synth.WORKLOADS[name]
-    pairs, steps = CASES[name]
+    pairs, steps = CASES[name], wl.steps
     B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     gq = hq // hkv
     dev = torch.device("cuda:0")
     lens0 = [wl.start_len(b) for b in range(B)]
     length = max(lens0) + steps + 1
     Kd, Vd = synth.kv_streams_device(wl, length, dev, pairs_from_host=pairs)
-    max_groups = (max(lens0) + steps - 128) // 128 + 1
+    max_groups = wl.max_groups()
+    assert 128 + 128 * max_groups + 127 >= max(lens0) + steps
     cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
+    print(f"{name}: decode plan {K.decode_plan(cfg, B, max_groups)}")
     cache = K.KVarNCache(cfg, B, max_groups, device=dev)
     cache.prefill(Kd, Vd, lens0)
     for s in range(steps):
@@ -72,7 +78,8 @@ def test_full_size_sampled(name):
         err = float(np.abs(out[b, h * gq:(h + 1) * gq] - ref).max())
         worst = max(worst, err)
         ng = (n - 128) // 128
-        for g in sorted({0, ng // 2, ng - 1}):
+        # first, middle, and the groups the decode steps sealed
+        for g in sorted({0, ng // 2} | set(range((lens0[b] - 128) // 128, ng))):
             lo = 128 + 128 * g
             for kind, x, bits in (("k", k, wl.k_bits), ("v", v, wl.v_bits)):
                 rec = bytes(cache.record(b, h, g, kind).cpu().numpy())
