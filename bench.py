@@ -57,6 +57,16 @@ def parse():
     ap.add_argument("--other-steps", type=int, default=256, help="decode steps timed per other workload")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run this many eager steps only (for rocprofv3) and exit")
+    ap.add_argument("--profile-seal", type=int, default=0, metavar="N",
+                    help="if > 0: run N bulk seals (kvarn_prefill of the workload's prompt, K and V) only "
+                         "(for rocprofv3) and exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="print, per kernel whose name contains --kernel, the median over dispatches of every "
+                         "counter found in the rocprofv3 --pmc output directories DIR..., and exit")
+    ap.add_argument("--kernel", default="seal_prefill_kernel", help="kernel name filter for --counter-summary")
+    ap.add_argument("--trace", choices=["decode", "seal"],
+                    help="load the trace build (libkvarn_trace.so), run the decode split kernel or the bulk seal "
+                         "of the workload cold a few times, print per-wave phase timestamps as JSON, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 8 device-to-device copies of MIB MiB (a plain copy kernel of known "
                          "size, the reference for the HBM counters) and exit")
@@ -162,6 +172,83 @@ def traffic_summary(args):
         fh.write(f"algorithmic_bytes_per_launch = {alg}\n")
         fh.write(f"traffic_over_algorithmic = {(fetch + write) / alg:.3f}\n")
     print(open(traffic_file(wl.name)).read())
+
+
+def counter_summary(args):
+    """Median per dispatch of every PMC counter in the given rocprofv3 output
+    directories, for the dispatches of kernels matching --kernel; prints
+    'counter = value' lines (the figures the profile summaries quote)."""
+    import csv
+    import glob
+    vals = {}
+    names = set()
+    for d in args.counter_summary:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if args.kernel in r.get("Kernel_Name", ""):
+                        names.add(r["Kernel_Name"].split("(")[0])
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        sys.exit(f"no counter rows for kernels matching {args.kernel!r} in {args.counter_summary}")
+    print(f"# kernels: {', '.join(sorted(names))}")
+    for k in sorted(vals):
+        v = np.asarray(vals[k])
+        print(f"{k} = {np.median(v):.6g}  (dispatches {v.size}, min {v.min():.6g}, max {v.max():.6g})")
+
+
+def trace_run(args, reps=8):
+    """Per-wave phase timestamps from the trace build: each repetition
+    flushes the Infinity Cache, clears the trace buffer, launches the kernel
+    once on a layer cache not used before and reads the marks back."""
+    import torch
+    from kv_cache_quantization_seal_amd import kvarn as K
+    from kv_cache_quantization_seal_amd import probe, synth, wavetrace
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    B, hq, hkv, d = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens = [wl.start_len(b) for b in range(B)]
+    kd, vd = synth.kv_streams_device(wl, max(lens), dev)
+    cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
+    mg = wl.max_groups()
+    flush_buf = torch.zeros(2**30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    caches = [K.KVarNCache(cfg, B, mg, device=dev) for _ in range(reps)]
+    for c in caches:
+        c.prefill(kd, vd, lens)
+    q = torch.from_numpy(np.stack([synth.queries(wl, b, 1)[0] for b in range(B)])).to(dev)
+    plan = K.decode_plan(cfg, B, mg)
+    torch.cuda.synchronize()
+    summaries = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(reps):
+        probe.read(flush_buf, sink)
+        torch.cuda.synchronize()
+        which = wavetrace.DECODE if args.trace == "decode" else wavetrace.SEAL
+        wavetrace.clear(which)
+        e0.record()
+        if args.trace == "decode":
+            caches[r].decode_partial(q)
+        else:
+            caches[r].prefill(kd, vd, lens)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        if args.trace == "decode":
+            n_ex, n_rec = plan["exact_workgroups"], plan["record_workgroups"]
+            rec = wavetrace.read(which, 4 * (n_ex + n_rec))
+            names = {0: "start", 1: "query", 2: "first_ck", 3: "first_qk", 4: "first_pv", 5: "groups_done",
+                     6: "partial_written"}
+            groups = {"exact": range(0, 4 * n_ex), "record": range(4 * n_ex, 4 * (n_ex + n_rec))}
+        else:
+            n_tiles = 2 * B * hkv * max(0, (max(lens) - 128) // 128)
+            rec = wavetrace.read(which, n_tiles * d // 16)
+            names = {0: "start", 1: "rotated", 2: "iterated", 3: "stored"}
+            groups = None
+        summ = wavetrace.summarize(rec, names, groups)
+        summ["event_us"] = us
+        summaries.append(summ)
+    print(json.dumps({"workload": wl.name, "trace": args.trace, "plan": plan, "reps": summaries}))
 
 
 def _cpu_model():
@@ -393,10 +480,32 @@ def main():
     if args.traffic_summary:
         traffic_summary(args)
         return
+    if args.counter_summary:
+        counter_summary(args)
+        return
+    if args.trace:
+        os.environ["KVARN_LIBRARY"] = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                   "kv_cache_quantization_seal_amd", "libkvarn_trace.so")
+        trace_run(args)
+        return
     import torch
     from kv_cache_quantization_seal_amd import kvarn as K
     from kv_cache_quantization_seal_amd import probe
     from kv_cache_quantization_seal_amd import synth
+
+    if args.profile_seal > 0:
+        # Bulk seal of the workload's prompt only: the seal kernel's
+        # dispatches for a profiler, nothing else of note on the GPU.
+        wl = synth.WORKLOADS[args.workload]
+        lens = [wl.start_len(b) for b in range(wl.batch)]
+        kd, vd = synth.kv_streams_device(wl, max(lens), torch.device("cuda:0"))
+        cfg = K.make_config(wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.k_bits, wl.v_bits)
+        cache = K.KVarNCache(cfg, wl.batch, wl.max_groups(), device="cuda:0")
+        for _ in range(args.profile_seal):
+            cache.prefill(kd, vd, lens)
+        torch.cuda.synchronize()
+        print(f"[bench] seal profile run: {args.profile_seal} bulk seals of {wl.name}", file=sys.stderr, flush=True)
+        return
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * 2**20

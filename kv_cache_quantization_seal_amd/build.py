@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvarn.so")
 PROBE_LIB = os.path.join(PKG, "libkvarn_probe.so")
+TRACE_LIB = os.path.join(PKG, "libkvarn_trace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip"]
@@ -34,9 +35,10 @@ FLAGS = [
 EXTRA = {"decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, trace: bool = False) -> str:
+    obj = os.path.join(BUILD, ("trace_" if trace else "") + os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *(["-DKVARN_WAVE_TRACE"] if trace else []),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:
@@ -81,5 +83,21 @@ def build(verbose: bool = False, changed_only: bool = False) -> str:
     return LIB
 
 
+def build_trace(verbose: bool = False) -> str:
+    """The trace build: the same sources with per-wave phase timestamps
+    compiled in (KVARN_WAVE_TRACE), linked as libkvarn_trace.so.  A
+    diagnostic library, never loaded unless asked for (KVARN_LIBRARY)."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(len(SOURCES), os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, trace=True), SOURCES))
+    _link(objs, TRACE_LIB)
+    if verbose:
+        print(f"built {TRACE_LIB}")
+    return TRACE_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True, changed_only="--changed" in sys.argv)
+    if "--trace" in sys.argv:
+        build_trace(verbose=True)
+    else:
+        build(verbose=True, changed_only="--changed" in sys.argv)

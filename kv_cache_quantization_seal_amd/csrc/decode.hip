@@ -42,6 +42,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "trace.hpp"
 
 namespace kvarn {
 
@@ -291,6 +292,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   const int hm = n >> 2, im = n & 3;  // A-operand row of this lane: (head, limb)
   const bool arow_valid = hm < GQ && im < 3;
   WaveLds<D, GQ>& wv = sm.wv[w];
+  const int tslot = (int)blockIdx.x * kWaves + w;  // trace build only
 
   // The pair's sealed groups (from its current length, not the capacity the
   // grid was planned for) are shared evenly over its record waves: wave
@@ -390,6 +392,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
   // q~ producer values (scaled query in the log2 domain, rotated), per wave.
   float qr[QB];
   rotate_query<D, QB, KB>(qw, qvalid, j, a.scale, qr);
+  trace_mark(tslot, 1);  // query loaded and rotated
   auto ckh = [](int i) {
     return QB == 8 ? ((KB == 2 || KB == 4) ? 2 * (i & 3) + (i >> 2) : i) : unpack_index<KB>(i);
   };
@@ -415,6 +418,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
       ym = fmaxf(ym, fabsf(y[i]));
     }
     const float E = row16_max(ym);  // row G == head G: also the QK scale of this lane
+    if (gn == ga + 1) trace_mark(tslot, 2);  // first group's c^K arrived
     {
       const float inv = E > 0.f ? QMAX * __builtin_amdgcn_rcpf(E) : 0.f;
       uint32_t b0[QB / 4], b1[QB / 4], b2[QB / 4];
@@ -472,6 +476,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
       logit[nt] = (hvalid && live) ? (float)yv * (half_of(S.sk, shalf(nt)) * kscale) : -INFINITY;
       lmax = fmaxf(lmax, logit[nt]);
     }
+    if (gn == ga + 1) trace_mark(tslot, 3);  // first group's QK done
     load_k(S, offn);
 
     // Softmax update; w = p * s^V with its exact per-head maximum W.
@@ -541,11 +546,13 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
       const int yv = (int)((x << 1) + neglt);
       o_acc[ct] = fmaf((float)yv * vscale, half_of(S.cv, ct), o_acc[ct]);
     }
+    if (gn == ga + 1) trace_mark(tslot, 4);  // first group's PV done
     load_v(S, offn);
     wave_sync();  // this group's limbs have been read before the next group writes
   };
 
   for (int g = ga; g < gb; ++g) process(SA, g + 1);
+  trace_mark(tslot, 5);  // every group done
 
   // Merge the four waves' partials (m replicated per head; l summed over the
   // row; o over disjoint channels) and write this split's partial.
@@ -578,6 +585,7 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
     a.ws_o[row * D + ch] = O;
     if (ch == 0) store_partial_ml(a, b, kvh * GQ + h, split, M, L);
   }
+  trace_mark(tslot, 6);  // partial written
 }
 
 // ---------------------------------------------------------------------------
@@ -633,6 +641,8 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
     if (idx < GQ * D) sm.qx[idx / D][idx % D] = __half2float(qh[i]) * a.scale * kLog2e;
   }
   __syncthreads();
+  const int tslot = (int)blockIdx.x * kWaves + w;  // trace build only
+  trace_mark(tslot, 1);  // query staged
 
   float m_run[GQ], l_run[GQ], o[GQ][CPLX];
 #pragma unroll
@@ -717,6 +727,7 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
     }
     wave_sync();  // the staging rows are rewritten next round
   }
+  trace_mark(tslot, 5);  // every round done
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
     if (l == 0) {
@@ -746,6 +757,7 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
     a.ws_o[row * D + ch] = O;
     if (ch == 0) store_partial_ml(a, b, kvh * GQ + h, split, M, L);
   }
+  trace_mark(tslot, 6);  // partial written
 }
 
 template <int D, int KB, int VB, int GQ>
@@ -761,6 +773,7 @@ union DecodeSmemU {
 template <int D, int KB, int VB, int GQ, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecodeSmemU<D, KB, VB, GQ> sm;
+  trace_begin((int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6));
   const int nex = a.nsplit - a.n_rec_splits;
   const int npair = a.c.batch * a.c.hkv;
   const int bx = blockIdx.x;
@@ -1052,6 +1065,10 @@ static void launch_g(int gq, const DecodeArgs& a, int phases, hipStream_t st) {
   else if (gq == 2) launch_t<D, KB, VB, 2>(a, phases, st);
   else launch_t<D, KB, VB, 4>(a, phases, st);
 }
+
+#ifdef KVARN_WAVE_TRACE
+hipError_t trace_io_decode(void* host, size_t bytes) { return trace_io_local(host, bytes); }
+#endif
 
 hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int phases, hipStream_t st) {
 #define CALL(d, k, v) launch_g<d, k, v>(gq, a, phases, st)

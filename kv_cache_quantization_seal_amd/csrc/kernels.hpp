@@ -201,4 +201,11 @@ hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int
 hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
                           hipStream_t st);
 
+#ifdef KVARN_WAVE_TRACE
+// Trace build only: copy (host non-NULL) or clear (host NULL) the per-wave
+// timestamp buffer of the decode / seal kernels (see trace.hpp).
+hipError_t trace_io_decode(void* host, size_t bytes);
+hipError_t trace_io_seal(void* host, size_t bytes);
+#endif
+
 }  // namespace kvarn

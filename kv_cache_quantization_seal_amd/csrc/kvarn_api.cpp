@@ -394,4 +394,14 @@ kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
                     "kvarn_dequant_records launch");
 }
 
+#ifdef KVARN_WAVE_TRACE
+// Trace build (libkvarn_trace.so) only, not part of the KVarN ABI: per-wave
+// phase timestamps of the decode split kernel (which 0) or the bulk seal
+// kernel (which 1).  host NULL clears the buffer; otherwise copies `bytes`
+// bytes of it.  Synchronous; returns 0 or a HIP error code.
+int kvarn_trace_io(int which, void* host, size_t bytes) {
+  return (int)(which == 0 ? kvarn::trace_io_decode(host, bytes) : kvarn::trace_io_seal(host, bytes));
+}
+#endif
+
 }  // extern "C"

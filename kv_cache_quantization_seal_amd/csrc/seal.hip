@@ -44,6 +44,7 @@
 //   per SIMD, on a CU.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "trace.hpp"
 
 namespace kvarn {
 
@@ -472,6 +473,8 @@ template <int D, int KB, int VB>
 __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(SealPrefillArgs a) {
   __shared__ SealSmem<D> sm;
   const int idx = blockIdx.x;
+  const int tslot = idx * (kSealThreadsPerD * D / 64) + (int)(threadIdx.x >> 6);  // trace build only
+  trace_begin(tslot);
   const int g = idx % a.gmax, r = idx / a.gmax;
   const int bhl = r % a.nbh, kind = r / a.nbh;
   if (kSink + kGroup * (g + 1) > a.lens.len[bhl / a.hkv]) return;
@@ -483,11 +486,14 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
   uint4 raw[4];
   load_tile<D>(raw, src, threadIdx.x);
   seal_rotate<D>(raw, sm, threadIdx.x);
+  trace_mark(tslot, 1);  // tile loaded and rotated
   seal_iterate<D>(a.iters, sm, threadIdx.x);
+  trace_mark(tslot, 2);  // iterations done
   if (kind == 0)
     seal_finish<D, KB, true>(rec, nullptr, sm, threadIdx.x);
   else
     seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
+  trace_mark(tslot, 3);  // record stores issued
 }
 
 // Seal on arrival.  Workgroup (entry, KV head, K|V): in the predicate form
@@ -604,6 +610,10 @@ static void launch_stream_t(const SealStreamArgs& a, int gx, hipStream_t st) {
   hipLaunchKernelGGL((seal_stream_kernel<D, KB, VB>), dim3(gx, 2), dim3(kSealThreadsPerD * D), 0, st, a);
 }
 
+
+#ifdef KVARN_WAVE_TRACE
+hipError_t trace_io_seal(void* host, size_t bytes) { return trace_io_local(host, bytes); }
+#endif
 
 hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& args, int max_groups_in_batch, int nbh,
                                hipStream_t st) {

@@ -12,7 +12,10 @@ from typing import Optional, Sequence
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvarn.so")
+# KVARN_LIBRARY may name another build of the same ABI (the trace build,
+# libkvarn_trace.so, for per-wave timestamps); the default is libkvarn.so.
+_LIB_PATH = os.environ.get("KVARN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libkvarn.so")
 _lib = None
 
 OK, EINVAL, EUNSUPPORTED, ERANGE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
