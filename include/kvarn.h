@@ -231,6 +231,23 @@ kvarn_status kvarn_decode_attn(const kvarn_config *cfg, const kvarn_cache *cache
                                void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * kvarn_decode_attn without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels and results as kvarn_decode_attn; the workspace is a
+ * fixed device array of KVARN_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per device, held until the process ends.  A batch and capacity whose
+ * workspace (kvarn_decode_workspace_bytes) exceeds it returns
+ * KVARN_EWORKSPACE before anything is queued.  Every call on a device shares
+ * that device's array: calls that overlap on one device (different streams,
+ * or threads) race and must be serialized by the caller; calls in one stream
+ * are ordered.  No state carries from one call to the next.
+ */
+#define KVARN_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvarn_status kvarn_decode_attn_noalloc(const kvarn_config *cfg, const kvarn_cache *cache,
+                                       const void *q, float *out, float softmax_scale, void *stream);
+
+/*
  * The two phases of kvarn_decode_attn, for callers that schedule them apart
  * (kvarn_decode_attn == partial then combine, same arguments):
  *   partial: the split-K kernel; writes per-split (max, sum, output) partials

@@ -3,12 +3,22 @@
 // leaves the GPU untouched (and needs no GPU at all).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kvarn.h"
 #include "kernels.hpp"
+
+// Scratch of kvarn_decode_attn_noalloc: the decode workspace (per-split
+// partial outputs, maxima and sums) in a file-scope device array, so that
+// entry point needs no allocation.  Each device holds its own copy for the
+// life of the process; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device.
+constexpr size_t kNoAllocScratchBytes = (size_t)KVARN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -342,6 +352,55 @@ static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* ca
   return hip_status(kvarn::launch_decode(cfg->head_dim, cfg->k_bits, cfg->v_bits,
                                          cfg->num_q_heads / cfg->num_kv_heads, a, phases, (hipStream_t)stream),
                     what);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+static void* scratch_ptr(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+kvarn_status kvarn_decode_attn_noalloc(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,
+                                       float softmax_scale, void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (!q || !out) return fail(KVARN_EINVAL, "q and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVARN_EINVAL, "q and out must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale)) return fail(KVARN_EINVAL, "softmax_scale is NaN");
+  const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
+                                                  cfg->num_q_heads / cfg->num_kv_heads);
+  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
+                                                 cache->max_groups, resident, kvarn::decode_cu_count());
+  if (p.ws_bytes > kNoAllocScratchBytes)
+    return fail(KVARN_EWORKSPACE,
+                "kvarn_decode_attn_noalloc: this batch and capacity need %zu bytes of decode scratch, more than "
+                "the library's fixed %zu bytes (use kvarn_decode_attn with a workspace)",
+                p.ws_bytes, kNoAllocScratchBytes);
+  hipError_t e = hipSuccess;
+  void* ws = scratch_ptr(&e);
+  if (!ws) return fail(KVARN_EHIP, "kvarn_decode_attn_noalloc: scratch lookup: %s", hipGetErrorString(e));
+  return decode_common(cfg, cache, q, out, softmax_scale, ws, kNoAllocScratchBytes, 3, stream,
+                       "kvarn_decode_attn_noalloc launch");
 }
 
 kvarn_status kvarn_decode_attn(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,

@@ -27,7 +27,7 @@ EXPORTS = (
     "kvarn_decode_plan",
     "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
     "kvarn_prefill",
-    "kvarn_decode_attn", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
+    "kvarn_decode_attn", "kvarn_decode_attn_noalloc", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
     "kvarn_dequant_records",
 )
 
@@ -77,6 +77,7 @@ def lib():
         L.kvarn_seal_group.argtypes = [cp(Config), cp(CacheView), vp, vp, i32, vp]
         L.kvarn_prefill.argtypes = [cp(Config), cp(CacheView), vp, vp, i64, cp(i32), vp]
         L.kvarn_decode_attn.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp, sz, vp]
+        L.kvarn_decode_attn_noalloc.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp]
         L.kvarn_decode_attn_partial.argtypes = [cp(Config), cp(CacheView), vp, f32, vp, sz, vp]
         L.kvarn_decode_attn_combine.argtypes = [cp(Config), cp(CacheView), vp, vp, sz, vp]
         L.kvarn_seal_tiles.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp, i32, vp]
@@ -229,6 +230,16 @@ class KVarNCache:
         _check(lib().kvarn_decode_attn(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q), _ptr(out),
                                        float(scale), _ptr(self.workspace), self.workspace.numel(),
                                        _stream(stream)))
+        return out
+
+    def decode_attn_noalloc(self, q: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None,
+                            stream=None) -> torch.Tensor:
+        """decode_attn through kvarn_decode_attn_noalloc (the library's fixed
+        scratch instead of this cache's workspace; allocates nothing)."""
+        if scale is None:
+            scale = self.cfg.head_dim ** -0.5
+        _check(lib().kvarn_decode_attn_noalloc(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q), _ptr(out),
+                                               float(scale), _stream(stream)))
         return out
 
     def decode_partial(self, q: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:

@@ -96,6 +96,21 @@ def test_entry_points_validate_before_launch():
     assert L.kvarn_decode_attn(r(cfg), r(_view()), FAKE, FAKE, float("nan"), FAKE, ws, None) == K.EINVAL
 
 
+def test_decode_noalloc_validates_before_launch():
+    """The no-alloc decode rejects bad arguments, and a cache whose workspace
+    exceeds the library's fixed scratch, before anything is queued."""
+    L = K.lib()
+    r = ctypes.byref
+    cfg = K.make_config(128, 32, 8, 2, 2)
+    assert L.kvarn_decode_attn_noalloc(r(cfg), r(_view()), None, FAKE, 0.1, None) == K.EINVAL
+    assert L.kvarn_decode_attn_noalloc(r(cfg), r(_view()), FAKE, FAKE + 4, 0.1, None) == K.EINVAL
+    assert L.kvarn_decode_attn_noalloc(r(cfg), r(_view()), FAKE, FAKE, float("nan"), None) == K.EINVAL
+    big = K.make_config(256, 64, 16, 2, 2)
+    assert L.kvarn_decode_attn_noalloc(r(big), r(_view(batch=128, max_groups=1)), FAKE, FAKE, 0.1,
+                                       None) == K.EWORKSPACE
+    assert "scratch" in L.kvarn_last_error().decode()
+
+
 def test_prefill_range_checks():
     L = K.lib()
     cfg = K.make_config(128, 8, 2, 2, 2)
