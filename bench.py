@@ -64,6 +64,8 @@ def parse():
                     help="print, per kernel whose name contains --kernel, the median over dispatches of every "
                          "counter found in the rocprofv3 --pmc output directories DIR..., and exit")
     ap.add_argument("--kernel", default="seal_prefill_kernel", help="kernel name filter for --counter-summary")
+    ap.add_argument("--trace-max-groups", type=int, default=0,
+                    help="with --trace: cache capacity in groups (default: the workload's own)")
     ap.add_argument("--trace", choices=["decode", "seal"],
                     help="load the trace build (libkvarn_trace.so), run the decode split kernel or the bulk seal "
                          "of the workload cold a few times, print per-wave phase timestamps as JSON, and exit")
@@ -210,7 +212,7 @@ def trace_run(args, reps=8):
     lens = [wl.start_len(b) for b in range(B)]
     kd, vd = synth.kv_streams_device(wl, max(lens), dev)
     cfg = K.make_config(d, hq, hkv, wl.k_bits, wl.v_bits)
-    mg = wl.max_groups()
+    mg = args.trace_max_groups or wl.max_groups()
     flush_buf = torch.zeros(2**30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     caches = [K.KVarNCache(cfg, B, mg, device=dev) for _ in range(reps)]

@@ -189,6 +189,54 @@ def seal_tile(x: np.ndarray, bits: int, iters: int = SINKHORN_ITERS) -> dict:
 
 
 # --------------------------------------------------------------------------
+# Comparison quantizers for the error-accumulation harness (not KVarN): the
+# baselines the pages set KVarN against -- RTN without the variance
+# normalization, with per-channel or per-token steps (P1 "What it is": KIVI-
+# style per-channel keys; P2 §1: per-token scales and their error).  Each
+# returns the fake-quantized tile (dequantized, float64, original frame).
+# --------------------------------------------------------------------------
+def fake_quant_rtn(x: np.ndarray, bits: int, axis: str, rotate: bool = False,
+                   scale16: bool = True) -> np.ndarray:
+    """Symmetric mid-rise RTN of a tile x [T][D] with one step per token row
+    (axis 'token') or per channel column (axis 'channel'), optionally in the
+    Hadamard frame (rotate=True: quantize x H/sqrt(D), rotate back).  The step
+    of a row/column is 2 max|.|/(2^b - 1) (no clipping), rounded to fp16 when
+    scale16, as the record stores its scales; ties round half to even."""
+    if axis not in ("token", "channel"):
+        raise ValueError("axis must be 'token' or 'channel'")
+    y = np.asarray(x, dtype=np.float64)
+    if rotate:
+        y = rotate_rows(y)
+    if axis == "channel":
+        y = y.T
+    levels = (1 << bits) - 1
+    mid = levels / 2.0
+    delta = 2.0 * np.max(np.abs(y), axis=1) / levels
+    # Codes from the unrounded step, reconstruction from the stored one
+    # (as for KVarN's records, reading R8).
+    stored = delta.astype(np.float16).astype(np.float64) if scale16 else delta
+    out = np.zeros_like(y)
+    for i in range(y.shape[0]):
+        if delta[i] > 0:
+            q = np.clip(np.rint(y[i] / delta[i] + mid), 0, levels)
+            out[i] = (q - mid) * stored[i]
+    if axis == "channel":
+        out = out.T
+    if rotate:
+        out = out @ rotation(out.shape[1]).T
+    return out
+
+
+def fake_quant_kvarn(x: np.ndarray, bits: int, kind: str, iters: int = SINKHORN_ITERS) -> np.ndarray:
+    """KVarN's record of a tile, decoded back (original frame, float64):
+    seal_tile with ``iters`` iterations (0 = rotation-only: per-token RTN in
+    the Hadamard frame), encoded and dequantized from the stored scales."""
+    out = seal_tile(np.asarray(x, dtype=np.float16), bits, iters)
+    rec = encode_record(out["codes"], out["s16"], out["c16"], bits, kind)
+    return dequant_record(rec, x.shape[1], bits, kind)
+
+
+# --------------------------------------------------------------------------
 # Packing and the record layout (P2 §2.1 "payload with its scale metadata"; R9)
 # --------------------------------------------------------------------------
 def pack_row(codes: np.ndarray, bits: int) -> bytes:
