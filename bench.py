@@ -226,7 +226,7 @@ def trace_run(args, reps=8):
     for r in range(reps):
         probe.read(flush_buf, sink)
         torch.cuda.synchronize()
-        which = wavetrace.DECODE if args.trace == "decode" else wavetrace.SEAL
+        which = wavetrace.decode(wl.k_bits) if args.trace == "decode" else wavetrace.SEAL
         wavetrace.clear(which)
         e0.record()
         if args.trace == "decode":

@@ -38,9 +38,8 @@
  *       frame): s_t * (code_tj - (2^b-1)/2) * c_j; original frame: times
  *       H_D/sqrt(D).
  *   - Code widths b are 2, 3, 4, 5, 6 or 8 bits [P2 §5 "Changing Only The
- *     Format", §6 "Splitting K And V"].  The (k_bits, v_bits) pairs built
- *     are every symmetric width, 2/4, 4/2, and the presets 3/2, 5/4 and 6/5;
- *     other pairs return KVARN_EUNSUPPORTED.
+ *     Format", §6 "Splitting K And V"], chosen for K and V independently:
+ *     every ordered (k_bits, v_bits) pair of them is supported.
  */
 #ifndef KVARN_H
 #define KVARN_H
@@ -70,7 +69,7 @@ typedef struct {
   int32_t head_dim;       /* D: 128 or 256 */
   int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;   /* Hkv; Hq/Hkv must be 1, 2 or 4 */
-  int32_t k_bits;         /* 2, 3, 4, 5, 6 or 8 (see the pairs above) */
+  int32_t k_bits;         /* 2, 3, 4, 5, 6 or 8 */
   int32_t v_bits;         /* 2, 3, 4, 5, 6 or 8 */
   int32_t group;          /* must be 128 */
   int32_t sink;           /* must be 128 */

@@ -22,7 +22,8 @@ PROBE_LIB = os.path.join(PKG, "libkvarn_probe.so")
 TRACE_LIB = os.path.join(PKG, "libkvarn_trace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip"]
+SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip",
+           "decode_k2.hip", "decode_k3.hip", "decode_k4.hip", "decode_k5.hip", "decode_k6.hip", "decode_k8.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
@@ -32,7 +33,7 @@ FLAGS = [
 ]
 # Decode inputs are finite by contract: with NaNs not honoured and the IEEE
 # mode bit off, float max/min need no quieting of their operands.
-EXTRA = {"decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+EXTRA = {s: ["-fno-honor-nans", "-mno-amdgpu-ieee"] for s in SOURCES if s.startswith("decode")}
 
 
 def _compile(src: str, trace: bool = False) -> str:

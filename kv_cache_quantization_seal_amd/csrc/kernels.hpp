@@ -9,39 +9,14 @@ namespace kvarn {
 
 constexpr int kMaxPrefillBatch = 256;  // requests per prefill launch
 
-// Code widths (bits) and the (K, V) width pairs the kernels are built for:
-// every symmetric width, the pairs of widths 2 and 4, and the asymmetric
-// presets 3-2, 5-4 and 6-5.
+// Code widths (bits); K and V take any two of them [every ordered pair is
+// built: the seal kernels take the widths at run time, the decode split
+// kernel has one instance per pair].
 constexpr bool width_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
-constexpr bool pair_ok(int kb, int vb) {
-  return (kb == vb && width_ok(kb)) || (kb == 2 && vb == 4) || (kb == 4 && vb == 2) || (kb == 3 && vb == 2) ||
-         (kb == 5 && vb == 4) || (kb == 6 && vb == 5);
-}
+constexpr bool pair_ok(int kb, int vb) { return width_ok(kb) && width_ok(vb); }
 // Index of a width in 2, 3, 4, 5, 6, 8.
 constexpr int width_index(int b) { return b == 8 ? 5 : b - 2; }
 
-// CALL(d, kb, vb) for the instance matching (D, KB, VB); nothing for a pair
-// that pair_ok rejects (the host checks first).
-#define KVARN_PAIRS_FOR_D(d, KB, VB, CALL)      \
-  if (KB == 2 && VB == 2) CALL(d, 2, 2);        \
-  else if (KB == 2 && VB == 4) CALL(d, 2, 4);   \
-  else if (KB == 4 && VB == 2) CALL(d, 4, 2);   \
-  else if (KB == 4 && VB == 4) CALL(d, 4, 4);   \
-  else if (KB == 3 && VB == 3) CALL(d, 3, 3);   \
-  else if (KB == 5 && VB == 5) CALL(d, 5, 5);   \
-  else if (KB == 6 && VB == 6) CALL(d, 6, 6);   \
-  else if (KB == 8 && VB == 8) CALL(d, 8, 8);   \
-  else if (KB == 3 && VB == 2) CALL(d, 3, 2);   \
-  else if (KB == 5 && VB == 4) CALL(d, 5, 4);   \
-  else if (KB == 6 && VB == 5) CALL(d, 6, 5);
-#define KVARN_DISPATCH_DKV(D, KB, VB, CALL)     \
-  do {                                          \
-    if (D == 128) {                             \
-      KVARN_PAIRS_FOR_D(128, KB, VB, CALL)      \
-    } else {                                    \
-      KVARN_PAIRS_FOR_D(256, KB, VB, CALL)      \
-    }                                           \
-  } while (0)
 #define KVARN_DISPATCH_DB(D, B, CALL)                                                 \
   do {                                                                                \
     if (D == 128) {                                                                   \
@@ -90,6 +65,8 @@ struct SealPrefillArgs {
   int max_groups;
   int b0;
   int iters;
+  int k_bits;  // code widths of the K and V records
+  int v_bits;
   int gmax;     // groups per (request, head) in this launch (set by the launcher)
   int nbh;      // requests * KV heads in this launch (set by the launcher)
   int n_tiles;  // 2 * nbh * gmax (set by the launcher)
@@ -110,6 +87,8 @@ struct SealStreamArgs {
   int hkv;
   int max_groups;
   int iters;
+  int k_bits;  // code widths of the K and V records
+  int v_bits;
 };
 
 // Append + seal in one launch.  While it runs, seq_len[b] carries a count of
@@ -133,6 +112,8 @@ struct AppendSealArgs {
   int max_groups;
   int cap;  // tokens a request can hold: 128 + 128 max_groups + 127
   int iters;
+  int k_bits;  // code widths of the K and V records
+  int v_bits;
 };
 
 struct CacheArgs {
@@ -188,23 +169,40 @@ int decode_cu_count();
 
 hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* dst, int64_t stride, float* dbg, int n,
                              int iters, hipStream_t st);
-hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& a, int max_groups_in_batch, int nbh,
-                               hipStream_t st);
+hipError_t launch_seal_prefill(int D, const SealPrefillArgs& a, int max_groups_in_batch, int nbh, hipStream_t st);
 // nbh = entries * hkv (entries = batch in the predicate form, n in the list form).
-hipError_t launch_seal_stream(int D, int kb, int vb, const SealStreamArgs& a, int nbh, hipStream_t st);
-hipError_t launch_append_seal(int D, int kb, int vb, const AppendSealArgs& a, int nbh, hipStream_t st);
+hipError_t launch_seal_stream(int D, const SealStreamArgs& a, int nbh, hipStream_t st);
+hipError_t launch_append_seal(int D, const AppendSealArgs& a, int nbh, hipStream_t st);
 hipError_t launch_append(int D, const CacheArgs& c, const void* k, const void* v, hipStream_t st);
 hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const void* v, int64_t src_tokens,
                                const PrefillLens& lens, int b0, int nb, hipStream_t st);
 // phases: 1 = split kernel (partials into the workspace), 2 = combine kernel, 3 = both.
 hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int phases, hipStream_t st);
+// The split kernel for K width b (decode_k<b>.hip): launch, and the resident
+// workgroups on device `dev`.
+#define KVARN_DECLARE_SPLIT(b)                                                                  \
+  hipError_t launch_split_k##b(int D, int vb, int gq, const DecodeArgs& a, hipStream_t st); \
+  int resident_split_k##b(int D, int vb, int gq, int dev);
+KVARN_DECLARE_SPLIT(2)
+KVARN_DECLARE_SPLIT(3)
+KVARN_DECLARE_SPLIT(4)
+KVARN_DECLARE_SPLIT(5)
+KVARN_DECLARE_SPLIT(6)
+KVARN_DECLARE_SPLIT(8)
+#undef KVARN_DECLARE_SPLIT
 hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
                           hipStream_t st);
 
 #ifdef KVARN_WAVE_TRACE
 // Trace build only: copy (host non-NULL) or clear (host NULL) the per-wave
-// timestamp buffer of the decode / seal kernels (see trace.hpp).
-hipError_t trace_io_decode(void* host, size_t bytes);
+// timestamp buffer of the decode split kernel for K width b, or of the seal
+// kernels (see trace.hpp).
+hipError_t trace_io_decode_k2(void* host, size_t bytes);
+hipError_t trace_io_decode_k3(void* host, size_t bytes);
+hipError_t trace_io_decode_k4(void* host, size_t bytes);
+hipError_t trace_io_decode_k5(void* host, size_t bytes);
+hipError_t trace_io_decode_k6(void* host, size_t bytes);
+hipError_t trace_io_decode_k8(void* host, size_t bytes);
 hipError_t trace_io_seal(void* host, size_t bytes);
 #endif
 

@@ -50,10 +50,6 @@ kvarn_status check_cfg(const kvarn_config* c) {
   if (!bits_ok(c->k_bits) || !bits_ok(c->v_bits))
     return fail(KVARN_EUNSUPPORTED, "k_bits and v_bits must be 2, 3, 4, 5, 6 or 8 (got %d, %d)", c->k_bits,
                 c->v_bits);
-  if (!kvarn::pair_ok(c->k_bits, c->v_bits))
-    return fail(KVARN_EUNSUPPORTED,
-                "K/V widths %d/%d are not built (symmetric widths, 2/4, 4/2, 3/2, 5/4 and 6/5 are)", c->k_bits,
-                c->v_bits);
   if (c->num_q_heads <= 0 || c->num_kv_heads <= 0)
     return fail(KVARN_EINVAL, "head counts must be positive (got %d, %d)", c->num_q_heads, c->num_kv_heads);
   if (c->num_q_heads % c->num_kv_heads)
@@ -221,8 +217,9 @@ kvarn_status kvarn_append_seal(const kvarn_config* cfg, const kvarn_cache* cache
   a.max_groups = c.max_groups;
   a.cap = (int)cap;
   a.iters = cfg->sinkhorn_iters;
-  return hip_status(kvarn::launch_append_seal(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, (int)nbh,
-                                              (hipStream_t)stream),
+  a.k_bits = cfg->k_bits;
+  a.v_bits = cfg->v_bits;
+  return hip_status(kvarn::launch_append_seal(cfg->head_dim, a, (int)nbh, (hipStream_t)stream),
                     "kvarn_append_seal launch");
 }
 
@@ -257,8 +254,9 @@ kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache,
   a.hkv = c.hkv;
   a.max_groups = c.max_groups;
   a.iters = cfg->sinkhorn_iters;
-  return hip_status(kvarn::launch_seal_stream(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, (int)nbh,
-                                              (hipStream_t)stream),
+  a.k_bits = cfg->k_bits;
+  a.v_bits = cfg->v_bits;
+  return hip_status(kvarn::launch_seal_stream(cfg->head_dim, a, (int)nbh, (hipStream_t)stream),
                     "kvarn_seal_group launch");
 }
 
@@ -309,8 +307,10 @@ kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, co
       a.max_groups = c.max_groups;
       a.b0 = b0;
       a.iters = cfg->sinkhorn_iters;
+      a.k_bits = cfg->k_bits;
+      a.v_bits = cfg->v_bits;
       a.lens = lens;
-      e = kvarn::launch_seal_prefill(cfg->head_dim, cfg->k_bits, cfg->v_bits, a, max_g, nb * c.hkv, st);
+      e = kvarn::launch_seal_prefill(cfg->head_dim, a, max_g, nb * c.hkv, st);
       if (e != hipSuccess) return hip_status(e, "kvarn_prefill seal launch");
     }
   }
@@ -455,11 +455,21 @@ kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
 
 #ifdef KVARN_WAVE_TRACE
 // Trace build (libkvarn_trace.so) only, not part of the KVarN ABI: per-wave
-// phase timestamps of the decode split kernel (which 0) or the bulk seal
-// kernel (which 1).  host NULL clears the buffer; otherwise copies `bytes`
-// bytes of it.  Synchronous; returns 0 or a HIP error code.
+// phase timestamps of the bulk seal kernel (which 1) or of the decode split
+// kernel for K width b (which 100 + b).  host NULL clears the buffer;
+// otherwise copies `bytes` bytes of it.  Synchronous; returns 0 or a HIP
+// error code (hipErrorInvalidValue for an unknown `which`).
 int kvarn_trace_io(int which, void* host, size_t bytes) {
-  return (int)(which == 0 ? kvarn::trace_io_decode(host, bytes) : kvarn::trace_io_seal(host, bytes));
+  switch (which) {
+    case 1: return (int)kvarn::trace_io_seal(host, bytes);
+    case 102: return (int)kvarn::trace_io_decode_k2(host, bytes);
+    case 103: return (int)kvarn::trace_io_decode_k3(host, bytes);
+    case 104: return (int)kvarn::trace_io_decode_k4(host, bytes);
+    case 105: return (int)kvarn::trace_io_decode_k5(host, bytes);
+    case 106: return (int)kvarn::trace_io_decode_k6(host, bytes);
+    case 108: return (int)kvarn::trace_io_decode_k8(host, bytes);
+  }
+  return (int)hipErrorInvalidValue;
 }
 #endif
 

@@ -447,6 +447,21 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
   }
 }
 
+// seal_finish for a width known only at run time (uniform over the
+// workgroup): one branch per width, so a kernel serves every (K, V) width
+// pair without an instance per pair.
+template <int D, bool TOKEN_MAJOR>
+__device__ __forceinline__ void seal_finish_bits(int bits, uint8_t* __restrict__ rec, SealSmem<D>& sm, int tid) {
+  switch (bits) {
+    case 2: seal_finish<D, 2, TOKEN_MAJOR>(rec, nullptr, sm, tid); break;
+    case 3: seal_finish<D, 3, TOKEN_MAJOR>(rec, nullptr, sm, tid); break;
+    case 4: seal_finish<D, 4, TOKEN_MAJOR>(rec, nullptr, sm, tid); break;
+    case 5: seal_finish<D, 5, TOKEN_MAJOR>(rec, nullptr, sm, tid); break;
+    case 6: seal_finish<D, 6, TOKEN_MAJOR>(rec, nullptr, sm, tid); break;
+    default: seal_finish<D, 8, TOKEN_MAJOR>(rec, nullptr, sm, tid); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_tiles_kernel(const 
 // tile during the iterations measured slower: the older workgroup of a CU
 // takes issue priority and finishes its share early, leaving the younger
 // one alone on the CU for the last tiles.)
-template <int D, int KB, int VB>
+template <int D>
 __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(SealPrefillArgs a) {
   __shared__ SealSmem<D> sm;
   const int idx = blockIdx.x;
@@ -490,9 +505,9 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
   seal_iterate<D>(a.iters, sm, threadIdx.x);
   trace_mark(tslot, 2);  // iterations done
   if (kind == 0)
-    seal_finish<D, KB, true>(rec, nullptr, sm, threadIdx.x);
+    seal_finish_bits<D, true>(a.k_bits, rec, sm, threadIdx.x);
   else
-    seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
+    seal_finish_bits<D, false>(a.v_bits, rec, sm, threadIdx.x);
   trace_mark(tslot, 3);  // record stores issued
 }
 
@@ -502,7 +517,7 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
 // the one whose 128 tokens fill the request's tail, g = (n - 128) / 128 - 1
 // with n = seq_len[b] >= 256 and (n - 128) % 128 == 0; a list entry naming
 // another group, or a request outside [0, batch), is skipped.
-template <int D, int KB, int VB>
+template <int D>
 __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealStreamArgs a) {
   __shared__ SealSmem<D> sm;
   const int e = blockIdx.x / a.hkv, h = blockIdx.x - (blockIdx.x / a.hkv) * a.hkv;
@@ -522,9 +537,9 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealS
   seal_rotate<D>(raw, sm, threadIdx.x);
   seal_iterate<D>(a.iters, sm, threadIdx.x);
   if (kind == 0)
-    seal_finish<D, KB, true>(rec, nullptr, sm, threadIdx.x);
+    seal_finish_bits<D, true>(a.k_bits, rec, sm, threadIdx.x);
   else
-    seal_finish<D, VB, false>(rec, nullptr, sm, threadIdx.x);
+    seal_finish_bits<D, false>(a.v_bits, rec, sm, threadIdx.x);
 }
 
 // Append one token and seal the group it completes, in one launch: workgroup
@@ -535,7 +550,7 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_stream_kernel(SealS
 // 1 << kArriveShift to seq_len[b] (a device-scope atomic that also returns
 // n in the low bits), and the one that finds the count complete removes the
 // count and adds the token.
-template <int D, int KB, int VB>
+template <int D>
 __global__ __launch_bounds__(kSealThreadsPerD * D) void append_seal_kernel(AppendSealArgs a) {
   __shared__ SealSmem<D> sm;
   __shared__ int s_n;
@@ -572,9 +587,9 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void append_seal_kernel(Appen
   seal_rotate<D>(raw, sm, tid);
   seal_iterate<D>(a.iters, sm, tid);
   if (kind == 0)
-    seal_finish<D, KB, true>(rec, nullptr, sm, tid);
+    seal_finish_bits<D, true>(a.k_bits, rec, sm, tid);
   else
-    seal_finish<D, VB, false>(rec, nullptr, sm, tid);
+    seal_finish_bits<D, false>(a.v_bits, rec, sm, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -601,51 +616,39 @@ hipError_t launch_seal_tiles(int D, int bits, int kind, const void* src, void* d
   return e;
 }
 
-template <int D, int KB, int VB>
+template <int D>
 static void launch_prefill_t(const SealPrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((seal_prefill_kernel<D, KB, VB>), dim3(a.n_tiles), dim3(kSealThreadsPerD * D), 0, st, a);
-}
-template <int D, int KB, int VB>
-static void launch_stream_t(const SealStreamArgs& a, int gx, hipStream_t st) {
-  hipLaunchKernelGGL((seal_stream_kernel<D, KB, VB>), dim3(gx, 2), dim3(kSealThreadsPerD * D), 0, st, a);
+  hipLaunchKernelGGL((seal_prefill_kernel<D>), dim3(a.n_tiles), dim3(kSealThreadsPerD * D), 0, st, a);
 }
 
-
-#ifdef KVARN_WAVE_TRACE
-hipError_t trace_io_seal(void* host, size_t bytes) { return trace_io_local(host, bytes); }
-#endif
-
-hipError_t launch_seal_prefill(int D, int kb, int vb, const SealPrefillArgs& args, int max_groups_in_batch, int nbh,
-                               hipStream_t st) {
+hipError_t launch_seal_prefill(int D, const SealPrefillArgs& args, int max_groups_in_batch, int nbh, hipStream_t st) {
   if (max_groups_in_batch <= 0 || nbh <= 0) return hipSuccess;
   SealPrefillArgs a = args;
   a.gmax = max_groups_in_batch;
   a.nbh = nbh;
   a.n_tiles = 2 * nbh * max_groups_in_batch;
-#define CALL(d, k, v) launch_prefill_t<d, k, v>(a, st)
-  KVARN_DISPATCH_DKV(D, kb, vb, CALL);
-#undef CALL
+  if (D == 128)
+    launch_prefill_t<128>(a, st);
+  else
+    launch_prefill_t<256>(a, st);
   return hipGetLastError();
 }
 
-template <int D, int KB, int VB>
-static void launch_append_seal_t(const AppendSealArgs& a, int gx, hipStream_t st) {
-  hipLaunchKernelGGL((append_seal_kernel<D, KB, VB>), dim3(gx, 2), dim3(kSealThreadsPerD * D), 0, st, a);
-}
-
-hipError_t launch_append_seal(int D, int kb, int vb, const AppendSealArgs& a, int nbh, hipStream_t st) {
+hipError_t launch_append_seal(int D, const AppendSealArgs& a, int nbh, hipStream_t st) {
   if (nbh <= 0) return hipSuccess;
-#define CALL(d, k, v) launch_append_seal_t<d, k, v>(a, nbh, st)
-  KVARN_DISPATCH_DKV(D, kb, vb, CALL);
-#undef CALL
+  if (D == 128)
+    hipLaunchKernelGGL((append_seal_kernel<128>), dim3(nbh, 2), dim3(kSealThreadsPerD * 128), 0, st, a);
+  else
+    hipLaunchKernelGGL((append_seal_kernel<256>), dim3(nbh, 2), dim3(kSealThreadsPerD * 256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_seal_stream(int D, int kb, int vb, const SealStreamArgs& a, int nbh, hipStream_t st) {
+hipError_t launch_seal_stream(int D, const SealStreamArgs& a, int nbh, hipStream_t st) {
   if (nbh <= 0) return hipSuccess;
-#define CALL(d, k, v) launch_stream_t<d, k, v>(a, nbh, st)
-  KVARN_DISPATCH_DKV(D, kb, vb, CALL);
-#undef CALL
+  if (D == 128)
+    hipLaunchKernelGGL((seal_stream_kernel<128>), dim3(nbh, 2), dim3(kSealThreadsPerD * 128), 0, st, a);
+  else
+    hipLaunchKernelGGL((seal_stream_kernel<256>), dim3(nbh, 2), dim3(kSealThreadsPerD * 256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -48,7 +48,6 @@ def test_group_and_workspace_bytes():
 
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, K.EUNSUPPORTED), ("k_bits", 7, K.EUNSUPPORTED), ("v_bits", 1, K.EUNSUPPORTED),
-    ("k_bits", 8, K.EUNSUPPORTED),  # K8 with V2 is not a built pair
     ("group", 64, K.EUNSUPPORTED), ("sink", 0, K.EUNSUPPORTED), ("num_q_heads", 12, K.EINVAL),
     ("num_q_heads", 64, K.EUNSUPPORTED), ("num_kv_heads", 0, K.EINVAL), ("sinkhorn_iters", -1, K.EINVAL),
 ])
@@ -158,11 +157,13 @@ def test_append_seal_validates_before_launch():
     assert "2^23" in L.kvarn_last_error().decode()
 
 
-@pytest.mark.parametrize("kb,vb,ok", [(3, 3, True), (5, 4, True), (6, 5, True), (3, 2, True), (8, 8, True),
-                                      (2, 8, False), (4, 5, False), (5, 6, False), (7, 7, False)])
-def test_width_pairs(kb, vb, ok):
-    cfg = K.make_config(128, 8, 2, kb, vb)
-    assert (K.check_config(cfg) == K.OK) == ok
+@pytest.mark.parametrize("kb", [2, 3, 4, 5, 6, 8])
+def test_every_width_pair_is_supported(kb):
+    for vb in (2, 3, 4, 5, 6, 8):
+        assert K.check_config(K.make_config(128, 8, 2, kb, vb)) == K.OK
+        assert K.check_config(K.make_config(256, 8, 2, kb, vb)) == K.OK
+    for vb in (1, 7, 9):
+        assert K.check_config(K.make_config(128, 8, 2, kb, vb)) == K.EUNSUPPORTED
 
 
 def test_paged_view_validates_before_launch():

@@ -53,7 +53,8 @@ def _check_cache(cache, k, v, lens, kb, vb, d):
                 check_sealed_tile(rv, None, O.seal_tile(v[b, h, sl], vb), d, vb, "v")
 
 
-@pytest.mark.parametrize("d,kb,vb", [(128, 2, 2), (256, 4, 2), (128, 5, 4), (256, 3, 3)])
+@pytest.mark.parametrize("d,kb,vb", [(128, 2, 2), (256, 4, 2), (128, 5, 4), (256, 3, 3),
+                                     (128, 8, 2), (256, 2, 6), (128, 6, 3)])
 def test_prefill_ragged(d, kb, vb):
     lens = [0, 1, 127, 128, 129, 255, 256, 257, 383, 600]
     wl = synth.Workload("p", 70 + d, len(lens), 4, 2, d, 600, 0, kb, vb, 0)
@@ -166,7 +167,8 @@ def test_append_refuses_past_capacity(fused):
     assert int(cache.seq_len.item()) == cap
 
 
-@pytest.mark.parametrize("d,kb,vb,hkv", [(128, 2, 4, 4), (256, 4, 2, 2), (128, 6, 5, 2), (128, 8, 8, 1)])
+@pytest.mark.parametrize("d,kb,vb,hkv", [(128, 2, 4, 4), (256, 4, 2, 2), (128, 6, 5, 2), (128, 8, 8, 1),
+                                         (128, 3, 8, 2), (256, 5, 3, 1)])
 def test_append_seal_matches_two_calls(d, kb, vb, hkv):
     """The fused launch leaves every buffer bit-identical to append followed by
     seal_group, step after step, for requests at different points of their

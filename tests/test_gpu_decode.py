@@ -2,7 +2,8 @@
 
 Decode is checked on caches the oracle built (sink, tail and records encoded
 by the oracle, so independent of the GPU seal), over ragged lengths, GQA
-ratios 1/2/4, head dims 128/256 and every built K/V width pair (2 to 8 bits).
+ratios 1/2/4, head dims 128/256 and every ordered K/V width pair (2, 3, 4,
+5, 6, 8 bits).
 Tolerance: 2e-3 max-abs on the fp32 output.
 """
 import numpy as np
@@ -83,6 +84,25 @@ def test_ragged_lengths_gqa4(lens):
 def test_shapes_and_widths(d, hq, hkv, kb, vb):
     err = _run(d, hq, hkv, kb, vb, [700, 389], seed=d + kb * 10 + vb)
     print(f"d={d} hq={hq} hkv={hkv} k{kb} v{vb}: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+
+
+WIDTHS = (2, 3, 4, 5, 6, 8)
+
+
+@pytest.mark.parametrize("kb", WIDTHS)
+@pytest.mark.parametrize("vb", WIDTHS)
+def test_every_width_pair_d128(kb, vb):
+    # every ordered (K, V) pair: 2 requests, GQA 2, three groups and a tail
+    err = _run(128, 4, 2, kb, vb, [550, 301], seed=100 + 10 * kb + vb)
+    print(f"d=128 k{kb} v{vb}: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 8), (8, 2), (3, 6), (6, 3), (5, 2), (2, 5), (4, 6), (8, 4)])
+def test_width_pairs_d256(kb, vb):
+    err = _run(256, 4, 1, kb, vb, [420], seed=200 + 10 * kb + vb)
+    print(f"d=256 k{kb} v{vb}: max abs err {err:.3e}")
     assert err <= ATTN_ATOL
 
 
