@@ -649,6 +649,35 @@ def main():
     caches = [cache0]
     for c in range(1, ncopy):
         caches.append(K.KVarNCache(cfg, B, max_groups, device=dev))
+    # ---- multi-layer bulk seal: one prompt into every layer cache, one
+    # kvarn_prefill_layers call (one seal launch per 16 layers) against a
+    # loop of per-layer kvarn_prefill calls, for a short and the full prompt.
+    seal_layers = {}
+    for label, plen in (("prompt_2k", [min(2048, n) for n in lens0]), ("prompt_full", lens0)):
+        g_layers = sum(hkv * ((n - 128) // 128) for n in plen if n > 128) * ncopy
+        graphs = {}
+        for mode in ("per_layer", "one_call"):
+            gg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gg, stream=stream):
+                if mode == "per_layer":
+                    for c in caches:
+                        c.prefill(k_all, v_all, plen, stream=stream)
+                else:
+                    K.prefill_layers(caches, [k_all] * ncopy, [v_all] * ncopy, plen, stream=stream)
+            graphs[mode] = gg
+        res = {"groups_per_call": g_layers, "layers": ncopy, "prompt_tokens": plen[0]}
+        for mode, gg in graphs.items():
+            t = float(np.median(_timed_replays(torch, stream, gg, 20)))
+            res[mode] = {"us_per_call": t * 1e6, "groups_per_s": g_layers / t,
+                         "hbm_frac": g_layers * seal_bytes_per_group / t / HBM_PEAK}
+        del graphs
+        seal_layers[label] = res
+        print(f"[bench] multi-layer seal, {plen[0]}-token prompt x {ncopy} layers: one call "
+              f"{res['one_call']['groups_per_s'] / 1e6:.2f} M groups/s vs per-layer "
+              f"{res['per_layer']['groups_per_s'] / 1e6:.2f} M groups/s", file=sys.stderr, flush=True)
+    seal_layers["note"] = ("kvarn_prefill_layers over all layer caches (one seal launch per 16 layers) vs one "
+                           "kvarn_prefill per layer, both captured in a HIP graph; median of 20 replays")
+
     for c in range(ncopy):
         caches[c].prefill(k_all, v_all, lens_c[c])
     seq0 = [c.seq_len.clone() for c in caches]
@@ -862,6 +891,7 @@ def main():
                      "read_ceiling_GBps": read_ceiling / 1e9, "frac_of_read_ceiling": achieved / read_ceiling},
         "seal_event": seal_event,
         "seal": seal,
+        "seal_layers": seal_layers,
         "dequant": dequant,
         "paged": paged_line,
         "workloads": others,

@@ -214,6 +214,21 @@ kvarn_status kvarn_prefill(const kvarn_config *cfg, const kvarn_cache *cache,
                            const int32_t *len_host, void *stream);
 
 /*
+ * kvarn_prefill for n_layers layer caches of one model at once (the same
+ * prompt lengths in every layer): one copy launch and one seal launch per 16
+ * layers instead of two launches per layer, so a short prompt, whose groups
+ * alone would leave most compute units idle, fills the GPU with the tiles of
+ * all its layers [P2 §2.1; the sealing of P1 "What it is", P2 §1].
+ * caches: host array [n_layers] of cache views sharing batch and max_groups
+ * (each with its own buffers, paged or not); k, v: host arrays [n_layers] of
+ * device fp16 [batch][Hkv][src_tokens][D] pointers; len_host as for
+ * kvarn_prefill.  Results equal n_layers kvarn_prefill calls.
+ */
+kvarn_status kvarn_prefill_layers(const kvarn_config *cfg, const kvarn_cache *caches, int32_t n_layers,
+                                  const void *const *k, const void *const *v, int64_t src_tokens,
+                                  const int32_t *len_host, void *stream);
+
+/*
  * Decode attention [P2 §1, §2.1]: for every request b and query head h
  * (KV head floor(h*Hkv/Hq)), attends the query q (device fp16 [batch][Hq][D],
  * post-RoPE) over all seq_len[b] cached positions: the exact sink and tail in

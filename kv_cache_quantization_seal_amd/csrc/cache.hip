@@ -45,27 +45,27 @@ __global__ __launch_bounds__(256) void append_kernel(CacheArgs c, const uint4* _
   if (threadIdx.x == 0 && !full) c.seq_len[b] = n + 1;
 }
 
-// One workgroup per (KV head, request): sink and tail copies of a prompt.
+// One workgroup per (KV head, request, layer): sink and tail copies of a
+// prompt, then the request's length.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_copy_kernel(CacheArgs c, const uint4* __restrict__ k,
-                                                           const uint4* __restrict__ v, int64_t src_tokens,
-                                                           PrefillLens lens, int b0) {
+__global__ __launch_bounds__(256) void prefill_copy_kernel(SealPrefillArgs a) {
   constexpr int CH = D / 8;
   const int h = blockIdx.x;
   const int bl = blockIdx.y;
-  const int b = b0 + bl;
-  const int len = lens.len[bl];
+  const PrefillLayer& L = a.layer[blockIdx.z];
+  const int b = a.b0 + bl;
+  const int len = a.lens.len[bl];
   const int n_sink = len < kSink ? len : kSink;
   const int n_groups = len > kSink ? (len - kSink) / kGroup : 0;
   const int tail_lo = kSink + kGroup * n_groups;
   const int n_tail = len > kSink ? len - tail_lo : 0;
-  const int64_t bh = (int64_t)b * c.hkv + h;
-  uint4* sk = reinterpret_cast<uint4*>(c.sink_k) + bh * kGroup * CH;
-  uint4* sv = reinterpret_cast<uint4*>(c.sink_v) + bh * kGroup * CH;
-  uint4* tk = reinterpret_cast<uint4*>(c.tail_k) + bh * kGroup * CH;
-  uint4* tv = reinterpret_cast<uint4*>(c.tail_v) + bh * kGroup * CH;
-  const uint4* ks = k + bh * src_tokens * CH;
-  const uint4* vs = v + bh * src_tokens * CH;
+  const int64_t bh = (int64_t)b * a.hkv + h;
+  uint4* sk = reinterpret_cast<uint4*>(L.sink_k) + bh * kGroup * CH;
+  uint4* sv = reinterpret_cast<uint4*>(L.sink_v) + bh * kGroup * CH;
+  uint4* tk = reinterpret_cast<uint4*>(L.tail_k) + bh * kGroup * CH;
+  uint4* tv = reinterpret_cast<uint4*>(L.tail_v) + bh * kGroup * CH;
+  const uint4* ks = reinterpret_cast<const uint4*>(L.k) + bh * a.src_tokens * CH;
+  const uint4* vs = reinterpret_cast<const uint4*>(L.v) + bh * a.src_tokens * CH;
   for (int i = threadIdx.x; i < n_sink * CH; i += blockDim.x) {
     sk[i] = ks[i];
     sv[i] = vs[i];
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void prefill_copy_kernel(CacheArgs c, const ui
     tk[i] = ks[(int64_t)tail_lo * CH + i];
     tv[i] = vs[(int64_t)tail_lo * CH + i];
   }
-  if (h == 0 && threadIdx.x == 0) c.seq_len[b] = len;
+  if (h == 0 && threadIdx.x == 0) L.seq_len[b] = len;
 }
 
 // Record -> fp16 original-frame rows.  The record is staged in LDS with
@@ -211,14 +211,12 @@ hipError_t launch_append(int D, const CacheArgs& c, const void* k, const void* v
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const void* v, int64_t src_tokens,
-                               const PrefillLens& lens, int b0, int nb, hipStream_t st) {
+hipError_t launch_prefill_copy(int D, const SealPrefillArgs& a, int nb, hipStream_t st) {
+  if (nb <= 0 || a.n_layers <= 0) return hipSuccess;
   if (D == 128)
-    hipLaunchKernelGGL(prefill_copy_kernel<128>, dim3(c.hkv, nb), dim3(256), 0, st, c, (const uint4*)k,
-                       (const uint4*)v, src_tokens, lens, b0);
+    hipLaunchKernelGGL(prefill_copy_kernel<128>, dim3(a.hkv, nb, a.n_layers), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(prefill_copy_kernel<256>, dim3(c.hkv, nb), dim3(256), 0, st, c, (const uint4*)k,
-                       (const uint4*)v, src_tokens, lens, b0);
+    hipLaunchKernelGGL(prefill_copy_kernel<256>, dim3(a.hkv, nb, a.n_layers), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -53,12 +53,22 @@ struct PrefillLens {
   int32_t len[kMaxPrefillBatch];
 };
 
-struct SealPrefillArgs {
-  const __half* k;
+// One layer cache of a (multi-layer) prefill: its prompt K/V and its cache.
+struct PrefillLayer {
+  const __half* k;   // [B][Hkv][src_tokens][D]
   const __half* v;
-  int64_t src_tokens;
   uint8_t* records;
   RecordMap map;
+  __half* sink_k;
+  __half* sink_v;
+  __half* tail_k;
+  __half* tail_v;
+  int32_t* seq_len;
+};
+constexpr int kMaxPrefillLayers = 16;  // layers per launch (kernel-argument space)
+
+struct SealPrefillArgs {
+  int64_t src_tokens;
   int64_t group_bytes;
   int rec_k_bytes;
   int hkv;
@@ -69,8 +79,10 @@ struct SealPrefillArgs {
   int v_bits;
   int gmax;     // groups per (request, head) in this launch (set by the launcher)
   int nbh;      // requests * KV heads in this launch (set by the launcher)
-  int n_tiles;  // 2 * nbh * gmax (set by the launcher)
+  int n_tiles;  // 2 * n_layers * nbh * gmax (set by the launcher)
+  int n_layers;
   PrefillLens lens;
+  PrefillLayer layer[kMaxPrefillLayers];
 };
 
 struct SealStreamArgs {
@@ -174,8 +186,9 @@ hipError_t launch_seal_prefill(int D, const SealPrefillArgs& a, int max_groups_i
 hipError_t launch_seal_stream(int D, const SealStreamArgs& a, int nbh, hipStream_t st);
 hipError_t launch_append_seal(int D, const AppendSealArgs& a, int nbh, hipStream_t st);
 hipError_t launch_append(int D, const CacheArgs& c, const void* k, const void* v, hipStream_t st);
-hipError_t launch_prefill_copy(int D, const CacheArgs& c, const void* k, const void* v, int64_t src_tokens,
-                               const PrefillLens& lens, int b0, int nb, hipStream_t st);
+// Sink and tail copies of a prompt into every layer of `a` (a.lens, a.b0,
+// a.n_layers, a.layer[], a.hkv, a.src_tokens), nb requests.
+hipError_t launch_prefill_copy(int D, const SealPrefillArgs& a, int nb, hipStream_t st);
 // phases: 1 = split kernel (partials into the workspace), 2 = combine kernel, 3 = both.
 hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int phases, hipStream_t st);
 // The split kernel for K width b (decode_k<b>.hip): launch, and the resident

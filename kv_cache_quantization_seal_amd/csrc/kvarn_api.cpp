@@ -260,61 +260,90 @@ kvarn_status kvarn_seal_group(const kvarn_config* cfg, const kvarn_cache* cache,
                     "kvarn_seal_group launch");
 }
 
-kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, const void* k, const void* v,
-                           int64_t src_tokens, const int32_t* len_host, void* stream) {
+kvarn_status kvarn_prefill_layers(const kvarn_config* cfg, const kvarn_cache* caches, int32_t n_layers,
+                                  const void* const* k, const void* const* v, int64_t src_tokens,
+                                  const int32_t* len_host, void* stream) {
   kvarn_status s = check_cfg(cfg);
   if (s != KVARN_OK) return s;
-  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
-  if (!k || !v || !len_host) return fail(KVARN_EINVAL, "k, v and len_host must be non-NULL");
-  if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVARN_EINVAL, "k and v must be 16-byte aligned");
+  if (n_layers < 0) return fail(KVARN_EINVAL, "n_layers must be >= 0 (got %d)", n_layers);
+  if (n_layers == 0) return ok();
+  if (!caches || !k || !v || !len_host) return fail(KVARN_EINVAL, "caches, k, v and len_host must be non-NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((s = check_cache(cfg, &caches[l])) != KVARN_OK) return s;
+    if (caches[l].batch != caches[0].batch || caches[l].max_groups != caches[0].max_groups)
+      return fail(KVARN_EINVAL, "layer %d: every layer cache must have the batch and max_groups of layer 0", l);
+    if (!k[l] || !v[l]) return fail(KVARN_EINVAL, "layer %d: k and v must be non-NULL", l);
+    if (!aligned(k[l], 16) || !aligned(v[l], 16))
+      return fail(KVARN_EINVAL, "layer %d: k and v must be 16-byte aligned", l);
+  }
   if (src_tokens < 0) return fail(KVARN_EINVAL, "src_tokens must be >= 0");
-  const int64_t cap = (int64_t)KVARN_SINK + (int64_t)KVARN_GROUP * cache->max_groups + KVARN_GROUP - 1;
-  for (int b = 0; b < cache->batch; ++b) {
+  const kvarn_cache* c0 = &caches[0];
+  const int64_t cap = (int64_t)KVARN_SINK + (int64_t)KVARN_GROUP * c0->max_groups + KVARN_GROUP - 1;
+  for (int b = 0; b < c0->batch; ++b) {
     if (len_host[b] < 0) return fail(KVARN_EINVAL, "len_host[%d] = %d is negative", b, len_host[b]);
     if (len_host[b] > src_tokens)
       return fail(KVARN_ERANGE, "len_host[%d] = %d exceeds src_tokens = %lld", b, len_host[b], (long long)src_tokens);
     if (len_host[b] > cap)
       return fail(KVARN_ERANGE, "len_host[%d] = %d exceeds the cache capacity %lld", b, len_host[b], (long long)cap);
   }
-  const kvarn::CacheArgs c = cache_args(cfg, cache);
+  const kvarn::CacheArgs c = cache_args(cfg, c0);
   hipStream_t st = (hipStream_t)stream;
-  for (int b0 = 0; b0 < cache->batch; b0 += kvarn::kMaxPrefillBatch) {
-    const int nb = cache->batch - b0 < kvarn::kMaxPrefillBatch ? cache->batch - b0 : kvarn::kMaxPrefillBatch;
-    kvarn::PrefillLens lens;
-    memset(&lens, 0, sizeof(lens));
-    int max_g = 0;
-    for (int i = 0; i < nb; ++i) {
-      lens.len[i] = len_host[b0 + i];
-      const int g = lens.len[i] > KVARN_SINK ? (lens.len[i] - KVARN_SINK) / KVARN_GROUP : 0;
-      if (g > max_g) max_g = g;
+  for (int l0 = 0; l0 < n_layers; l0 += kvarn::kMaxPrefillLayers) {
+    const int nl = n_layers - l0 < kvarn::kMaxPrefillLayers ? n_layers - l0 : kvarn::kMaxPrefillLayers;
+    kvarn::SealPrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.src_tokens = src_tokens;
+    a.group_bytes = c.group_bytes;
+    a.rec_k_bytes = c.rec_k_bytes;
+    a.hkv = c.hkv;
+    a.max_groups = c.max_groups;
+    a.iters = cfg->sinkhorn_iters;
+    a.k_bits = cfg->k_bits;
+    a.v_bits = cfg->v_bits;
+    a.n_layers = nl;
+    for (int i = 0; i < nl; ++i) {
+      const kvarn_cache* ci = &caches[l0 + i];
+      kvarn::PrefillLayer& L = a.layer[i];
+      L.k = (const __half*)k[l0 + i];
+      L.v = (const __half*)v[l0 + i];
+      L.records = (uint8_t*)ci->records;
+      L.map = record_map(ci);
+      L.sink_k = (__half*)ci->sink_k;
+      L.sink_v = (__half*)ci->sink_v;
+      L.tail_k = (__half*)ci->tail_k;
+      L.tail_v = (__half*)ci->tail_v;
+      L.seq_len = ci->seq_len;
     }
-    hipError_t e = kvarn::launch_prefill_copy(cfg->head_dim, c, k, v, src_tokens, lens, b0, nb, st);
-    if (e != hipSuccess) return hip_status(e, "kvarn_prefill copy launch");
-    if (max_g > 0) {
-      // The seal launch walks 2 * nb * Hkv * max_g tiles with int indices.
-      if ((int64_t)2 * nb * c.hkv * max_g >= ((int64_t)1 << 30))
-        return fail(KVARN_ERANGE, "prefill of %d requests x %d KV heads x %d groups is too large for one call", nb,
-                    c.hkv, max_g);
-      kvarn::SealPrefillArgs a;
-      a.k = (const __half*)k;
-      a.v = (const __half*)v;
-      a.src_tokens = src_tokens;
-      a.records = (uint8_t*)cache->records;
-      a.map = c.map;
-      a.group_bytes = c.group_bytes;
-      a.rec_k_bytes = c.rec_k_bytes;
-      a.hkv = c.hkv;
-      a.max_groups = c.max_groups;
+    for (int b0 = 0; b0 < c0->batch; b0 += kvarn::kMaxPrefillBatch) {
+      const int nb = c0->batch - b0 < kvarn::kMaxPrefillBatch ? c0->batch - b0 : kvarn::kMaxPrefillBatch;
+      memset(&a.lens, 0, sizeof(a.lens));
+      int max_g = 0;
+      for (int i = 0; i < nb; ++i) {
+        a.lens.len[i] = len_host[b0 + i];
+        const int g = a.lens.len[i] > KVARN_SINK ? (a.lens.len[i] - KVARN_SINK) / KVARN_GROUP : 0;
+        if (g > max_g) max_g = g;
+      }
       a.b0 = b0;
-      a.iters = cfg->sinkhorn_iters;
-      a.k_bits = cfg->k_bits;
-      a.v_bits = cfg->v_bits;
-      a.lens = lens;
-      e = kvarn::launch_seal_prefill(cfg->head_dim, a, max_g, nb * c.hkv, st);
-      if (e != hipSuccess) return hip_status(e, "kvarn_prefill seal launch");
+      hipError_t e = kvarn::launch_prefill_copy(cfg->head_dim, a, nb, st);
+      if (e != hipSuccess) return hip_status(e, "kvarn_prefill copy launch");
+      if (max_g > 0) {
+        // The seal launch walks 2 * layers * nb * Hkv * max_g tiles with int indices.
+        if ((int64_t)2 * nl * nb * c.hkv * max_g >= ((int64_t)1 << 30))
+          return fail(KVARN_ERANGE, "prefill of %d layers x %d requests x %d KV heads x %d groups is too large", nl,
+                      nb, c.hkv, max_g);
+        e = kvarn::launch_seal_prefill(cfg->head_dim, a, max_g, nb * c.hkv, st);
+        if (e != hipSuccess) return hip_status(e, "kvarn_prefill seal launch");
+      }
     }
   }
   return ok();
+}
+
+kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, const void* k, const void* v,
+                           int64_t src_tokens, const int32_t* len_host, void* stream) {
+  if (!cache) return fail(KVARN_EINVAL, "cache is NULL");
+  if (!k || !v) return fail(KVARN_EINVAL, "k, v and len_host must be non-NULL");
+  return kvarn_prefill_layers(cfg, cache, 1, &k, &v, src_tokens, len_host, stream);
 }
 
 static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,

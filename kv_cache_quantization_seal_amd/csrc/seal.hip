@@ -477,8 +477,9 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_tiles_kernel(const 
   seal_finish<D, BITS, KIND == 0>(dst + i * dst_stride, dbg ? dbg + i * (kGroup + D) : nullptr, sm, threadIdx.x);
 }
 
-// Bulk sealing: one workgroup per tile (group g, request-head bh, K|V), tile
-// index g + G (bh + NBH kind); groups a request does not have return at once.
+// Bulk sealing: one workgroup per tile (group g, request-head bh, K|V,
+// layer), tile index g + G (bh + NBH (kind + 2 layer)); groups a request does
+// not have return at once.
 // One tile per workgroup lets the dispatcher refill a CU as soon as either of
 // its two workgroups finishes.  (A persistent grid that prefetched its next
 // tile during the iterations measured slower: the older workgroup of a CU
@@ -491,13 +492,15 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
   const int tslot = idx * (kSealThreadsPerD * D / 64) + (int)(threadIdx.x >> 6);  // trace build only
   trace_begin(tslot);
   const int g = idx % a.gmax, r = idx / a.gmax;
-  const int bhl = r % a.nbh, kind = r / a.nbh;
+  const int bhl = r % a.nbh, r2 = r / a.nbh;
+  const int kind = r2 & 1, layer = r2 >> 1;
   if (kSink + kGroup * (g + 1) > a.lens.len[bhl / a.hkv]) return;
+  const PrefillLayer& L = a.layer[layer];
   const int64_t bh = (int64_t)a.b0 * a.hkv + bhl;
-  const int64_t off = pair_offset(a.map, (int)(bh / a.hkv), (int)(bh % a.hkv), g, a.hkv, a.max_groups, a.group_bytes);
+  const int64_t off = pair_offset(L.map, (int)(bh / a.hkv), (int)(bh % a.hkv), g, a.hkv, a.max_groups, a.group_bytes);
   if (off < 0) return;
-  const __half* src = (kind ? a.v : a.k) + (bh * a.src_tokens + kSink + (int64_t)kGroup * g) * D;
-  uint8_t* rec = a.records + off + (kind ? a.rec_k_bytes : 0);
+  const __half* src = (kind ? L.v : L.k) + (bh * a.src_tokens + kSink + (int64_t)kGroup * g) * D;
+  uint8_t* rec = L.records + off + (kind ? a.rec_k_bytes : 0);
   uint4 raw[4];
   load_tile<D>(raw, src, threadIdx.x);
   seal_rotate<D>(raw, sm, threadIdx.x);
@@ -626,7 +629,7 @@ hipError_t launch_seal_prefill(int D, const SealPrefillArgs& args, int max_group
   SealPrefillArgs a = args;
   a.gmax = max_groups_in_batch;
   a.nbh = nbh;
-  a.n_tiles = 2 * nbh * max_groups_in_batch;
+  a.n_tiles = 2 * a.n_layers * nbh * max_groups_in_batch;
   if (D == 128)
     launch_prefill_t<128>(a, st);
   else

@@ -26,7 +26,7 @@ EXPORTS = (
     "kvarn_check_config", "kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
     "kvarn_decode_plan",
     "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
-    "kvarn_prefill",
+    "kvarn_prefill", "kvarn_prefill_layers",
     "kvarn_decode_attn", "kvarn_decode_attn_noalloc", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
     "kvarn_dequant_records",
 )
@@ -76,6 +76,7 @@ def lib():
         L.kvarn_append_seal.argtypes = [cp(Config), cp(CacheView), vp, vp, vp]
         L.kvarn_seal_group.argtypes = [cp(Config), cp(CacheView), vp, vp, i32, vp]
         L.kvarn_prefill.argtypes = [cp(Config), cp(CacheView), vp, vp, i64, cp(i32), vp]
+        L.kvarn_prefill_layers.argtypes = [cp(Config), cp(CacheView), i32, cp(vp), cp(vp), i64, cp(i32), vp]
         L.kvarn_decode_attn.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp, sz, vp]
         L.kvarn_decode_attn_noalloc.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp]
         L.kvarn_decode_attn_partial.argtypes = [cp(Config), cp(CacheView), vp, f32, vp, sz, vp]
@@ -253,6 +254,25 @@ class KVarNCache:
         _check(lib().kvarn_decode_attn_combine(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(out),
                                                _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
         return out
+
+
+def prefill_layers(caches: Sequence["KVarNCache"], ks: Sequence[torch.Tensor], vs: Sequence[torch.Tensor],
+                   lengths: Sequence[int], stream=None) -> None:
+    """KVarNCache.prefill for every layer cache at once (kvarn_prefill_layers):
+    caches share config, batch and max_groups; ks[i], vs[i] are layer i's
+    prompt K/V [B][Hkv][src_tokens][D]."""
+    n = len(caches)
+    if not (len(ks) == len(vs) == n) or n == 0:
+        raise ValueError("one K and one V tensor per layer cache")
+    src_tokens = int(ks[0].shape[2])
+    if any(int(t.shape[2]) != src_tokens for t in list(ks) + list(vs)):
+        raise ValueError("every layer's K and V need the same number of tokens")
+    views = (CacheView * n)(*[c.view for c in caches])
+    kp = (ctypes.c_void_p * n)(*[_ptr(t) for t in ks])
+    vp_ = (ctypes.c_void_p * n)(*[_ptr(t) for t in vs])
+    arr = (ctypes.c_int32 * caches[0].batch)(*[int(x) for x in lengths])
+    _check(lib().kvarn_prefill_layers(ctypes.byref(caches[0].cfg), views, n, kp, vp_, src_tokens, arr,
+                                      _stream(stream)))
 
 
 def seal_tiles(src: torch.Tensor, bits: int, kind: str, out: Optional[torch.Tensor] = None,

@@ -125,6 +125,28 @@ def test_prefill_range_checks():
     assert L.kvarn_prefill(r(cfg), r(_view()), FAKE, FAKE, 200, None, None) == K.EINVAL
 
 
+def test_prefill_layers_validates():
+    L = K.lib()
+    cfg = K.make_config(128, 8, 2, 2, 2)
+    r = ctypes.byref
+    views = (K.CacheView * 2)(_view(), _view())
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    lens = (ctypes.c_int32 * 2)(10, 300)
+    assert L.kvarn_prefill_layers(r(cfg), views, 0, ptrs, ptrs, 400, lens, None) == K.OK   # no layer: no launch
+    assert L.kvarn_prefill_layers(r(cfg), views, -1, ptrs, ptrs, 400, lens, None) == K.EINVAL
+    assert L.kvarn_prefill_layers(r(cfg), None, 2, ptrs, ptrs, 400, lens, None) == K.EINVAL
+    assert L.kvarn_prefill_layers(r(cfg), views, 2, None, ptrs, 400, lens, None) == K.EINVAL
+    bad = (K.CacheView * 2)(_view(), _view(batch=3))
+    assert L.kvarn_prefill_layers(r(cfg), bad, 2, ptrs, ptrs, 400, lens, None) == K.EINVAL
+    assert "batch and max_groups" in L.kvarn_last_error().decode()
+    bad = (K.CacheView * 2)(_view(), _view(max_groups=5))
+    assert L.kvarn_prefill_layers(r(cfg), bad, 2, ptrs, ptrs, 400, lens, None) == K.EINVAL
+    nullk = (ctypes.c_void_p * 2)(FAKE, None)
+    assert L.kvarn_prefill_layers(r(cfg), views, 2, nullk, ptrs, 400, lens, None) == K.EINVAL
+    big = (ctypes.c_int32 * 2)(10, 128 + 128 * 4 + 128)
+    assert L.kvarn_prefill_layers(r(cfg), views, 2, ptrs, ptrs, 4096, big, None) == K.ERANGE
+
+
 def test_tile_entry_points_validate():
     L = K.lib()
     assert L.kvarn_seal_tiles(64, 2, 0, 16, FAKE, FAKE, 4608, None, 1, None) == K.EUNSUPPORTED

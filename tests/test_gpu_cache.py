@@ -66,6 +66,45 @@ def test_prefill_ragged(d, kb, vb):
     _check_cache(cache, k, v, lens, kb, vb, d)
 
 
+@pytest.mark.parametrize("d,kb,vb", [(128, 2, 2), (256, 4, 2)])
+def test_prefill_layers_equals_per_layer(d, kb, vb):
+    """kvarn_prefill_layers over 19 layer caches (more than one launch's 16;
+    one paged with a shuffled table) leaves every buffer bit-identical to one
+    kvarn_prefill per layer."""
+    lens = [0, 127, 129, 300, 511]
+    hkv = 2
+    cfg = K.make_config(d, 4, hkv, kb, vb)
+    n_layers = 19
+    ks, vs = [], []
+    for layer in range(n_layers):
+        wl = synth.Workload("ml", 300 + layer, len(lens), 4, hkv, d, 511, 0, kb, vb, 0)
+        k, v = _streams(wl, 511)
+        ks.append(torch.from_numpy(k).cuda())
+        vs.append(torch.from_numpy(v).cuda())
+
+    def make(layer):
+        if layer == 3:
+            c = K.KVarNCache(cfg, len(lens), 3, num_blocks=20)
+            perm = np.random.default_rng(layer).permutation(20)[:len(lens) * 3].astype(np.int32)
+            c.block_table.copy_(torch.from_numpy(perm).view(len(lens), 3))
+            return c
+        return K.KVarNCache(cfg, len(lens), 3)
+
+    multi = [make(layer) for layer in range(n_layers)]
+    single = [make(layer) for layer in range(n_layers)]
+    K.prefill_layers(multi, ks, vs, lens)
+    for layer in range(n_layers):
+        single[layer].prefill(ks[layer], vs[layer], lens)
+    torch.cuda.synchronize()
+    for layer in range(n_layers):
+        for name in ("seq_len", "sink_k", "sink_v", "tail_k", "tail_v", "records"):
+            assert torch.equal(getattr(multi[layer], name), getattr(single[layer], name)), (layer, name)
+    # and the records are the oracle's (spot check: layer 17, request 3, head 1, group 0)
+    k = ks[17].cpu().numpy()
+    rec = multi[17].record(3, 1, 0, "k").cpu().numpy().tobytes()
+    check_sealed_tile(rec, None, O.seal_tile(k[3, 1, 128:256], kb), d, kb, "k")
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_append_seal_stream_and_decode(fused):
     d, hq, hkv, kb, vb = 128, 4, 2, 2, 2
