@@ -277,6 +277,23 @@ kvarn_status kvarn_decode_attn_combine(const kvarn_config *cfg, const kvarn_cach
                                        void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Chunked-prefill attention over the cache [P2 §2.1: attention paths read the
+ * records directly; §7: the format's cost shows in prefill].  The chunk is
+ * the last `chunk` cached positions of every request (append the chunk with
+ * kvarn_prefill / kvarn_append first: every group it completed is sealed).
+ * The query of position p = seq_len[b] - chunk + i (q: device fp16
+ * [batch][chunk][Hq][D], post-RoPE) attends causally over positions 0..p as
+ * the cache holds them: sink and tail exact, sealed groups through their
+ * records, in the rotated frame with the output rotated back once [P2 §1].
+ * Query head h reads KV head floor(h*Hkv/Hq).  out: device fp32
+ * [batch][chunk][Hq][D]; rows whose position would be negative (chunk >
+ * seq_len[b]) are left unwritten.  softmax_scale multiplies q.k.  No
+ * workspace; chunk 0 queues nothing.
+ */
+kvarn_status kvarn_prefill_attn(const kvarn_config *cfg, const kvarn_cache *cache, const void *q,
+                                int32_t chunk, float *out, float softmax_scale, void *stream);
+
+/*
  * Seal n independent tiles (the same kernel as kvarn_seal_group).
  * src: device fp16 [n][128][D].  dst: device; tile i's record is written at
  * dst + i*dst_stride (dst_stride >= kvarn_record_bytes, multiple of 16).

@@ -22,7 +22,7 @@ PROBE_LIB = os.path.join(PKG, "libkvarn_probe.so")
 TRACE_LIB = os.path.join(PKG, "libkvarn_trace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip",
+SOURCES = ["kvarn_api.cpp", "seal.hip", "decode.hip", "cache.hip", "prefill_attn.hip",
            "decode_k2.hip", "decode_k3.hip", "decode_k4.hip", "decode_k5.hip", "decode_k6.hip", "decode_k8.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
 FLAGS = [

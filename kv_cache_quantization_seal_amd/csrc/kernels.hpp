@@ -157,6 +157,17 @@ struct DecodeArgs {
   int groups_per_wave;
 };
 
+struct PrefillAttnArgs {
+  CacheArgs c;
+  const __half* q;  // [B][chunk][Hq][D]
+  float* out;       // [B][chunk][Hq][D]
+  int chunk;        // queries per request: positions seq_len - chunk .. seq_len - 1
+  int hq;
+  float scale;      // softmax scale (applied to q.k)
+  int k_bits;
+  int v_bits;
+};
+
 struct DecodePlan {
   int groups_per_wave;
   int groups_per_split;
@@ -203,6 +214,7 @@ KVARN_DECLARE_SPLIT(5)
 KVARN_DECLARE_SPLIT(6)
 KVARN_DECLARE_SPLIT(8)
 #undef KVARN_DECLARE_SPLIT
+hipError_t launch_prefill_attn(int D, int gq, const PrefillAttnArgs& a, hipStream_t st);
 hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t src_stride, void* dst, int n,
                           hipStream_t st);
 

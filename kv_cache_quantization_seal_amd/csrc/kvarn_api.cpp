@@ -449,6 +449,34 @@ kvarn_status kvarn_decode_attn_combine(const kvarn_config* cfg, const kvarn_cach
                        "kvarn_decode_attn_combine launch");
 }
 
+kvarn_status kvarn_prefill_attn(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, int32_t chunk,
+                                float* out, float softmax_scale, void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (chunk < 0) return fail(KVARN_EINVAL, "chunk must be >= 0 (got %d)", chunk);
+  if (chunk == 0) return ok();
+  if (!q || !out) return fail(KVARN_EINVAL, "q and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVARN_EINVAL, "q and out must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale)) return fail(KVARN_EINVAL, "softmax_scale is NaN");
+  const int64_t cap = (int64_t)KVARN_SINK + (int64_t)KVARN_GROUP * cache->max_groups + KVARN_GROUP - 1;
+  if (chunk > cap) return fail(KVARN_ERANGE, "chunk %d exceeds the cache capacity %lld", chunk, (long long)cap);
+  const int gq = cfg->num_q_heads / cfg->num_kv_heads;
+  if ((int64_t)cache->batch * cfg->num_kv_heads > 65535 || cache->batch > 65535)
+    return fail(KVARN_ERANGE, "batch and KV heads exceed the launch grid");
+  kvarn::PrefillAttnArgs a;
+  a.c = cache_args(cfg, cache);
+  a.q = (const __half*)q;
+  a.out = out;
+  a.chunk = chunk;
+  a.hq = cfg->num_q_heads;
+  a.scale = softmax_scale;
+  a.k_bits = cfg->k_bits;
+  a.v_bits = cfg->v_bits;
+  return hip_status(kvarn::launch_prefill_attn(cfg->head_dim, gq, a, (hipStream_t)stream),
+                    "kvarn_prefill_attn launch");
+}
+
 kvarn_status kvarn_seal_tiles(int32_t head_dim, int32_t bits, int32_t kind, int32_t sinkhorn_iters, const void* src,
                               void* dst, int64_t dst_stride, float* dbg, int32_t n, void* stream) {
   if (!dim_ok(head_dim)) return fail(KVARN_EUNSUPPORTED, "head_dim must be 128 or 256 (got %d)", head_dim);

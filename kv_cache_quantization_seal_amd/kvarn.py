@@ -28,7 +28,7 @@ EXPORTS = (
     "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
     "kvarn_prefill", "kvarn_prefill_layers",
     "kvarn_decode_attn", "kvarn_decode_attn_noalloc", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
-    "kvarn_dequant_records",
+    "kvarn_dequant_records", "kvarn_prefill_attn",
 )
 
 
@@ -83,6 +83,7 @@ def lib():
         L.kvarn_decode_attn_combine.argtypes = [cp(Config), cp(CacheView), vp, vp, sz, vp]
         L.kvarn_seal_tiles.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp, i32, vp]
         L.kvarn_dequant_records.argtypes = [i32, i32, i32, vp, i64, vp, i32, vp]
+        L.kvarn_prefill_attn.argtypes = [cp(Config), cp(CacheView), vp, i32, vp, f32, vp]
         for name in EXPORTS:
             if name not in ("kvarn_record_bytes", "kvarn_group_bytes", "kvarn_decode_workspace_bytes",
                             "kvarn_last_error", "kvarn_status_string"):
@@ -241,6 +242,18 @@ class KVarNCache:
             scale = self.cfg.head_dim ** -0.5
         _check(lib().kvarn_decode_attn_noalloc(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q), _ptr(out),
                                                float(scale), _stream(stream)))
+        return out
+
+    def prefill_attn(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                     stream=None) -> torch.Tensor:
+        """Chunked-prefill attention of the last q.shape[1] cached positions
+        (q fp16 [B][chunk][Hq][D]); returns fp32 [B][chunk][Hq][D]."""
+        if out is None:
+            out = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+        if scale is None:
+            scale = self.cfg.head_dim ** -0.5
+        _check(lib().kvarn_prefill_attn(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q), int(q.shape[1]),
+                                        _ptr(out), float(scale), _stream(stream)))
         return out
 
     def decode_partial(self, q: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:

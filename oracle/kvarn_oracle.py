@@ -411,6 +411,32 @@ def decode_attention(q: np.ndarray, states: List[KVarNState], num_kv_heads: int,
     return out
 
 
+def prefill_attention(q: np.ndarray, states: List[KVarNState], num_kv_heads: int, scale: Optional[float] = None) -> np.ndarray:
+    """Chunked-prefill attention of one request over its cache (reading N1).
+
+    q [C][Hq][D]: the queries of the chunk, i.e. of the last C cached
+    positions n-C .. n-1, taken after the chunk has been appended and every
+    group it completed sealed.  The query at position p attends causally over
+    positions 0..p as the cache holds them: the sink and the tail exact, the
+    sealed groups through their records (P2 §2.1: attention paths read the
+    records; the chunk is appended before its attention, as a decode step
+    appends before it attends).  One plain attention per query position and
+    head; returns [C][Hq][D] float64.
+    """
+    c, hq = q.shape[0], q.shape[1]
+    n = states[0].n
+    if c > n:
+        raise ValueError("the chunk is longer than the cache")
+    mats = [st.materialize() for st in states]
+    out = np.empty(q.shape, dtype=np.float64)
+    for i in range(c):
+        p = n - c + i
+        for h in range(hq):
+            kvh = (h * num_kv_heads) // hq
+            out[i, h] = attention(q[i, h], mats[kvh][0][:p + 1], mats[kvh][1][:p + 1], scale)
+    return out
+
+
 def seal_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int):
     """Records of every complete group of a prefilled fp16 stream [L][D].
 

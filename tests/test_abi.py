@@ -147,6 +147,18 @@ def test_prefill_layers_validates():
     assert L.kvarn_prefill_layers(r(cfg), views, 2, ptrs, ptrs, 4096, big, None) == K.ERANGE
 
 
+def test_prefill_attn_validates():
+    L = K.lib()
+    cfg = K.make_config(128, 8, 2, 2, 2)
+    r = ctypes.byref
+    assert L.kvarn_prefill_attn(r(cfg), r(_view()), FAKE, 0, FAKE, 0.1, None) == K.OK   # empty chunk: no launch
+    assert L.kvarn_prefill_attn(r(cfg), r(_view()), FAKE, -1, FAKE, 0.1, None) == K.EINVAL
+    assert L.kvarn_prefill_attn(r(cfg), r(_view()), None, 4, FAKE, 0.1, None) == K.EINVAL
+    assert L.kvarn_prefill_attn(r(cfg), r(_view()), FAKE, 4, FAKE + 8, 0.1, None) == K.EINVAL
+    assert L.kvarn_prefill_attn(r(cfg), r(_view()), FAKE, 4, FAKE, float("nan"), None) == K.EINVAL
+    assert L.kvarn_prefill_attn(r(cfg), r(_view(max_groups=1)), FAKE, 384, FAKE, 0.1, None) == K.ERANGE
+
+
 def test_tile_entry_points_validate():
     L = K.lib()
     assert L.kvarn_seal_tiles(64, 2, 0, 16, FAKE, FAKE, 4608, None, 1, None) == K.EUNSUPPORTED

@@ -82,3 +82,42 @@ def test_dequant_error_bound(bits):
     assert np.all(err_rot <= bound * (1 + 1e-9) + fp16_slack)
     rel = np.linalg.norm(xhat - x.astype(np.float64)) / np.linalg.norm(x.astype(np.float64))
     assert rel < (0.6 if bits == 2 else 0.15)
+
+
+def test_prefill_attention_all_exact_is_causal_sdpa():
+    """With no sealed group (n <= 255) the chunk's attention is textbook causal
+    attention over the fp16 tokens (a query sees every earlier position and
+    itself); checked against torch's float64 SDPA with an explicit mask."""
+    import torch
+    rng = np.random.default_rng(7)
+    n, c, hq, hkv, d = 200, 37, 4, 2, 128
+    ks = rng.standard_normal((hkv, n, d)).astype(np.float16)
+    vs = rng.standard_normal((hkv, n, d)).astype(np.float16)
+    q = rng.standard_normal((c, hq, d)).astype(np.float16)
+    states = [O.state_from_stream(ks[h], vs[h], 2, 2) for h in range(hkv)]
+    got = O.prefill_attention(q, states, hkv)
+    pos = np.arange(n - c, n)
+    mask = torch.from_numpy(np.arange(n)[None, :] <= pos[:, None])   # [C][n]
+    for h in range(hq):
+        kvh = h * hkv // hq
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h].astype(np.float64))[None],
+            torch.from_numpy(ks[kvh].astype(np.float64))[None],
+            torch.from_numpy(vs[kvh].astype(np.float64))[None], attn_mask=mask[None])[0].numpy()
+        assert np.allclose(got[:, h], ref, atol=1e-12, rtol=1e-12)
+
+
+def test_prefill_attention_last_row_is_decode():
+    """The chunk's last query sees the whole cache: it equals decode attention
+    of the same query over the same (partly sealed) cache."""
+    wl = synth.Workload("pa", 95, 1, 4, 1, 128, 600, 0, 2, 2, 0)
+    k, v = synth.kv_stream(wl, 0, 0, 600)
+    st = O.state_from_stream(k, v, 2, 2)
+    q = np.random.default_rng(8).standard_normal((5, 4, 128)).astype(np.float16)
+    got = O.prefill_attention(q, [st], 1)
+    assert np.allclose(got[-1], O.decode_attention(q[-1], [st], 1), atol=1e-14)
+    # an earlier query does not see later positions: changing them leaves it unchanged
+    st2 = O.state_from_stream(k, v, 2, 2)
+    st2.tail_v[-1] = (st2.tail_v[-1].astype(np.float32) + 3).astype(np.float16)
+    got2 = O.prefill_attention(q, [st2], 1)
+    assert np.array_equal(got[:-1], got2[:-1]) and not np.array_equal(got[-1], got2[-1])
