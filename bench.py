@@ -34,6 +34,7 @@ import time
 import numpy as np
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_F16_PEAK = 2.5e15     # flop/s, dense fp16 MFMA, MI355X
 # fp32 vector peak without packed instructions (disabled in this build):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz.  The 157.3 TFLOP/s
 # vendor figure counts packed FMAs, which no kernel here issues.
@@ -50,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="llama31_8b_32k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seal-groups", type=int, default=48)
+    ap.add_argument("--prefill-chunk", type=int, default=2048,
+                    help="query tokens of the chunked-prefill attention measurement (the last chunk of the prompt)")
     ap.add_argument("--other-workloads", default="qwen3_4b_16k_b16,qwen3_4b_16k_b16_aligned,phi4_14b_32k_b8,longctx_d256_64k_b4,"
                     "llama31_8b_32k_k3v2,llama31_8b_32k_k6v5",
                     help="comma-separated workloads measured after the headline one and reported under "
@@ -645,6 +648,36 @@ def main():
     print(f"[bench] record -> fp16: {dequant['hbm_GBps']:.0f} GB/s ({dequant['hbm_frac'] * 100:.1f}% of HBM)",
           file=sys.stderr, flush=True)
 
+    # ---- chunked-prefill attention over records: the last `chunk` positions
+    # of the prompt attend causally over the cache (cache0 holds the prompt)
+    chunk = min(args.prefill_chunk, min(lens0))
+    qp = torch.from_numpy(np.random.default_rng(5).standard_normal((B, chunk, hq, d)).astype(np.float16)).to(dev)
+    outp = torch.empty(B, chunk, hq, d, dtype=torch.float32, device=dev)
+    gp = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gp, stream=stream):
+        cache0.prefill_attn(qp, out=outp, stream=stream)
+    t_pa = _timed_replays(torch, stream, gp, 20)
+    del gp
+    st_pa = _stats(t_pa)
+    # useful flops: QK and PV over positions 0..p for every query row
+    pa_flops = sum(hq * 4 * d * sum(n - chunk + i + 1 for i in range(chunk)) for n in lens0)
+    prefill_attn = {
+        "chunk": chunk, "us_per_call": st_pa["median"] * 1e6,
+        "us_stats": {k: (v * 1e6 if k != "reps" else v) for k, v in st_pa.items()},
+        "tflops": pa_flops / st_pa["median"] / 1e12,
+        "roofline": {"bound": "mfma", "achieved": pa_flops / st_pa["median"] / 1e12,
+                     "peak": MFMA_F16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": pa_flops / st_pa["median"] / MFMA_F16_PEAK},
+        "query_tokens_per_s": B * chunk / st_pa["median"],
+        "note": (f"kvarn_prefill_attn: the last {chunk} prompt positions attend causally over the {lens0[0]}-token "
+                 "cache (records read directly); flops = 4 D (p+1) per query row and head (QK and PV), against "
+                 "the dense fp16 MFMA peak; median of 20 graph replays"),
+    }
+    del qp, outp
+    print(f"[bench] prefill attention, {chunk}-token chunk over {lens0[0]}: {st_pa['median'] * 1e6:.1f} us, "
+          f"{prefill_attn['tflops']:.1f} TFLOP/s ({prefill_attn['roofline']['frac'] * 100:.1f}% of fp16 MFMA peak)",
+          file=sys.stderr, flush=True)
+
     # ---- layer caches at their phases -------------------------------------
     caches = [cache0]
     for c in range(1, ncopy):
@@ -754,6 +787,9 @@ def main():
         del gk
         return _stats(ts)
 
+    # A/B for folding the append (and seal-if-due) into the decode launches:
+    # the same steps without the append launch bound what a fused step saves.
+    st_noappend = time_graph(lambda r: caches[r % ncopy].decode_attn(q_all[0], out=outs[r % ncopy]))
     st_kernel = time_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]))
     st_combine = time_graph(lambda r: caches[r % ncopy].decode_combine(outs[r % ncopy]))
     t_kernel, t_combine = st_kernel["median"], st_combine["median"]
@@ -882,6 +918,7 @@ def main():
                    "max_groups": max_groups, "seals_in_timed_steps": seals_timed,
                    "step": "append + seal-if-due + decode attention (one layer)"},
         "step_us_stats": us(_stats(t_step_reps)),
+        "step_without_append_us_stats": us(st_noappend),
         "decode_plan": plan,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
@@ -892,6 +929,7 @@ def main():
         "seal_event": seal_event,
         "seal": seal,
         "seal_layers": seal_layers,
+        "prefill_attn": prefill_attn,
         "dequant": dequant,
         "paged": paged_line,
         "workloads": others,
