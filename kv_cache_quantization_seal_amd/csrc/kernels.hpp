@@ -220,8 +220,8 @@ hipError_t launch_dequant(int D, int bits, int kind, const void* src, int64_t sr
 
 #ifdef KVARN_WAVE_TRACE
 // Trace build only: copy (host non-NULL) or clear (host NULL) the per-wave
-// timestamp buffer of the decode split kernel for K width b, or of the seal
-// kernels (see trace.hpp).
+// timestamp buffer of the decode split kernel for K width b, of the seal
+// kernels, or of the chunked-prefill attention kernel (see trace.hpp).
 hipError_t trace_io_decode_k2(void* host, size_t bytes);
 hipError_t trace_io_decode_k3(void* host, size_t bytes);
 hipError_t trace_io_decode_k4(void* host, size_t bytes);
@@ -229,6 +229,7 @@ hipError_t trace_io_decode_k5(void* host, size_t bytes);
 hipError_t trace_io_decode_k6(void* host, size_t bytes);
 hipError_t trace_io_decode_k8(void* host, size_t bytes);
 hipError_t trace_io_seal(void* host, size_t bytes);
+hipError_t trace_io_prefill_attn(void* host, size_t bytes);
 #endif
 
 }  // namespace kvarn

@@ -519,6 +519,7 @@ kvarn_status kvarn_dequant_records(int32_t head_dim, int32_t bits, int32_t kind,
 int kvarn_trace_io(int which, void* host, size_t bytes) {
   switch (which) {
     case 1: return (int)kvarn::trace_io_seal(host, bytes);
+    case 2: return (int)kvarn::trace_io_prefill_attn(host, bytes);
     case 102: return (int)kvarn::trace_io_decode_k2(host, bytes);
     case 103: return (int)kvarn::trace_io_decode_k3(host, bytes);
     case 104: return (int)kvarn::trace_io_decode_k4(host, bytes);

@@ -4,54 +4,94 @@
 // groups read directly from their records -- on fp16 MFMA with fp32
 // accumulation ["KVarN KV Cache: Implementation and Benchmarks"
 // (anbeeld.com), §2.1 "Sink, Body, And Tail": attention paths read the
-// records; §1 "Where KVarN Comes From": attention runs in the rotated frame
-// and the output is rotated back once].
+// records; §1 "Where KVarN Comes From": attention over a record runs in the
+// rotated frame, and the result is rotated back once].
 //
 // Workgroup = 4 waves = 64 query rows of one (request, KV head): row
-// r = position-in-tile * GQ + head, so the GQ query heads of a KV head share
-// every key tile staged in LDS.  Each wave owns 16 rows (the MFMA M).  The
-// workgroup walks the key tiles of its request in position order -- sink,
-// records, tail, each 128 tokens at most, up to its last row's position --
-// with an online softmax per row, all in the rotated frame:
-//   * record tile: the codes minus the mid level, exact in fp16, are staged
-//     as the B operand; the query operand is q~ = q_r * c^K (fp32, split into
-//     fp16 hi + lo, two MFMAs); logit = s^K_t * (q~ . (code - mid));
-//     PV: w = p * s^V_t (hi + lo) against V codes - mid, then times c^V_j;
-//   * exact tile (sink, tail): the fp16 rows are rotated in fp32 and staged
-//     as hi + lo fp16 pairs (three MFMAs: hi*hi, hi*lo, lo*hi), scales 1.
-// Every fp32 operand split into hi + lo is first scaled, per row, by the power
-// of two that puts the row's largest magnitude in [2^11, 2^12): its low parts
-// then stay fp16 normals (a subnormal low part would leave only the 11 bits
-// of the high part); the scale is undone exactly on the fp32 results.
-// One inverse Hadamard per row at the end, across the output accumulators.
+// r = position-in-block * GQ + head, so the GQ query heads of a KV head share
+// every key tile staged in LDS.  Wave w owns rows 16w .. 16w+15; lane l
+// (n = l % 16, G = l / 16) owns row 16w + n.  The products are taken
+// transposed -- S^T = K q^T and O^T = V^T P^T -- so an MFMA result lane
+// holds one query row: logits, softmax state and output stay in registers
+// with no LDS transposition (v_mfma_f32_16x16x32_f16 lane layout, checked on
+// the device: A lane l holds row l%16, k = 8(l/16)..+7; B lane l holds
+// column l%16, same k; C lane l holds column l%16, rows 4(l/16)..+3).
 //
-// MFMA v_mfma_f32_16x16x32_f16 lane layout (checked on the device): A lane l
-// holds row l%16, k = 8(l/16)..+7; B lane l holds column l%16, same k; C lane
-// l holds column l%16, rows 4(l/16)..+3.
+// Tiles, in position order: the sink, the sealed groups, the tail, each 128
+// tokens at most, up to the block's last row.
+//   * record tile (rotated frame): the codes minus the mid level, exact in
+//     fp16, are the A operand; the query operand is q~ = q_r * c^K, an fp32
+//     value split into fp16 hi + lo (two MFMAs), so the logit
+//     s^K_t * (q~ . (code - mid)) keeps fp32 accuracy; PV takes the weights
+//     w = p * s^V_t, split the same way, against the V codes and scales by
+//     c^V_j.
+//   * exact tile (original frame): fp16 q against fp16 K rows, one MFMA
+//     (products of fp16 values are exact in fp32); PV as for a record.
+// The output accumulator is rotated (H / sqrt(D), its own inverse) whenever
+// the frame changes, so it leaves the kernel in the original frame.
+//
+// Pipeline: while a tile is computed, the next record's codes and scales are
+// already loading into registers; its K half is decoded into LDS after the
+// QK step, its V half after the PV step (two barriers per tile).
+//
+// Codes are turned into fp16 two at a time: 2c is placed in the mantissa of
+// 512 (fp16 spacing 1/2 in [512, 1024)) and 512 + mid is subtracted with one
+// packed fp16 add, exact.  For 2/4/8-bit codes a dword of codes yields pairs
+// (i, i + B/2) of each B = 32/bits block, so tile rows hold their codes in
+// that order; the query operand, the scales and the K tile's token rows are
+// permuted to match (exact tiles are staged in the same orders).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "trace.hpp"
 
 namespace kvarn {
 
 namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-constexpr int kPaWaves = 4;
-constexpr int kPaRows = 16;  // rows per wave
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 constexpr float kPaLog2e = 1.4426950408889634f;
 
+// LDS tiles: row pitches of 8 (mod 64) dwords make the MFMA operand reads
+// (lanes 16G + n: row n, 16-byte column G) conflict-free -- a 128-bit read
+// is served for lanes {0-7, 16-23}, {8-15, 24-31}, ... together -- and the
+// 128-bit row writes of the staging are conflict-free when lanes
+// {4j .. 4j+3, 4j+8 .. 4j+11} (served together) write rows that differ mod 8,
+// which write_row() arranges.
 template <int D>
 struct PaSmem {
-  static constexpr int KP = D + 8;    // pitch of a K tile row (token), halves
-  static constexpr int VP = 128 + 8;  // pitch of a V tile row (channel), halves
-  static constexpr int TILE = 128 * KP > D * VP ? 128 * KP : D * VP;
-  alignas(16) _Float16 hi[TILE];
-  alignas(16) _Float16 lo[TILE];      // exact tiles only
-  float sk[128], sv[128];              // token scales of the tile (1 for exact tiles)
-  float ck[D], cv[D];                  // channel scales (1 for exact tiles)
-  alignas(16) _Float16 p[kPaWaves][2][kPaRows][32 + 8];  // w hi / lo of one 32-token step
-  float qscale[kPaWaves][kPaRows];   // per-row inverse scale of the query operand
+  static constexpr int KP = D + 16;    // K tile: 128 token rows, pitch in halves
+  static constexpr int VP = 128 + 16;  // V tile: D channel rows of 128 token positions
+  static constexpr int QP = D + 4;    // staged query rows (fp32), aliasing the K tile
+  static_assert(64 * QP * 4 <= 128 * KP * 2, "staged queries fit the K tile");
+  alignas(16) _Float16 k[128 * KP];
+  alignas(16) _Float16 v[D * VP];
+  alignas(16) float sk[128];   // per K tile row: s^K of its token
+  alignas(16) float sv[128];   // per K tile row: s^V of its token / 2^eV
+  alignas(16) float ck[D];     // per K tile column: c^K of its channel / 2^eK
+  alignas(16) float cv[D];     // per channel: c^V * 2^eV
+  float qinv[64];              // per row: inverse power-of-two scale of the staged query
+  float kscale;                // 2^eK of the staged record tile
+  float vscale;                // 2^eV of the staged record tile
 };
+
+// ---- orders -------------------------------------------------------------
+// Block size B of the pair order of a code width (2 = natural order).
+__device__ __forceinline__ int perm_block(int bits) { return bits == 2 ? 16 : bits == 4 ? 8 : bits == 8 ? 4 : 2; }
+// Position p of a tile row -> index of the code it holds, and back.
+__device__ __forceinline__ int pos_to_code(int p, int B) {
+  return (p & -B) | ((p & (B - 1)) >> 1) | ((p & 1) * (B >> 1));
+}
+__device__ __forceinline__ int code_to_pos(int c, int B) {
+  const int h = B >> 1;
+  return (c & -B) | ((c & (h - 1)) << 1) | ((c & h) ? 1 : 0);
+}
+// K tile row r <-> V tile position p, within 32-token blocks: row bits
+// (i: 2, G: 2, h: 1) are position bits (i: 2, h: 1, G: 2).  A QK result lane
+// then holds, for PV step u, the weights of positions 32u + 8G .. +7: its B
+// operand, with no data movement.
+__device__ __forceinline__ int vpos_to_krow(int p) { return (p & ~31) | (p & 3) | ((p & 4) << 2) | ((p & 24) >> 1); }
+__device__ __forceinline__ int krow_to_vpos(int r) { return (r & ~31) | (r & 3) | ((r & 16) >> 2) | ((r & 12) << 1); }
 
 // Power of two that brings x > 0 into [2^11, 2^12) (1 for x = 0), and its inverse.
 __device__ __forceinline__ float pow2_scale(float x, float& inv) {
@@ -133,396 +173,590 @@ __device__ __forceinline__ void load64h(float (&x)[64], const __half* p, bool va
   }
 }
 
-// Exact tile: `count` fp16 rows [128][D] at src (rows past count are zero),
-// rotated, as hi + lo fp16 into the K layout [token][KP] (TRANSPOSE false) or
-// the V layout [channel][VP] (TRANSPOSE true).  All threads.
-template <int D, bool TRANSPOSE>
-__device__ void stage_exact(PaSmem<D>& sm, const __half* __restrict__ src, int count, int tid) {
-  constexpr int NT = D / 64, TPP = 256 / NT;
-#pragma unroll 1
-  for (int pass = 0; pass < 128 / TPP; ++pass) {
-    const int t = pass * TPP + tid / NT, chunk = tid % NT;
-    float x[64];
-    load64h(x, src + (size_t)t * D + 64 * chunk, t < count);
-    rotate64<D>(x, chunk);
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const _Float16 h = (_Float16)x[i];
-      const _Float16 l = (_Float16)(x[i] - (float)h);
-      const int j = 64 * chunk + i;
-      const int idx = TRANSPOSE ? j * PaSmem<D>::VP + t : t * PaSmem<D>::KP + j;
-      sm.hi[idx] = h;
-      sm.lo[idx] = l;
-    }
-  }
-}
-
-// 64 codes of BITS bits (a little-endian bit stream starting at bit 0 of
-// w[0]) minus the mid level, as fp16 (exact: half-integers below 2^8).
-template <int BITS>
-__device__ __forceinline__ void codes64(const uint8_t* __restrict__ src, _Float16* __restrict__ dst) {
-  constexpr int NW = 2 * BITS;  // 64 * BITS / 32 dwords
-  constexpr float MID = 0.5f * ((1 << BITS) - 1);
-  uint32_t w[NW];
-#pragma unroll
-  for (int k = 0; k < NW; ++k) w[k] = reinterpret_cast<const uint32_t*>(src)[k];
-  v8h out[8];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const int bit = BITS * i, wi = bit >> 5, sh = bit & 31;
-    uint32_t v;
-    if (sh + BITS <= 32)
-      v = (w[wi] >> sh) & ((1u << BITS) - 1);
-    else
-      v = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << BITS) - 1);
-    out[i >> 3][i & 7] = (_Float16)((float)v - MID);
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) reinterpret_cast<v8h*>(dst)[k] = out[k];
-}
-
-// Record tile: the codes of one record (kind K: rows = 128 tokens of D codes,
-// into [token][KP]; kind V: rows = D channels of 128 codes, into
-// [channel][VP]) as fp16 code - mid.  All threads.
-template <int D, bool VKIND>
-__device__ void stage_codes(PaSmem<D>& sm, const uint8_t* __restrict__ rec, int bits, int tid) {
-  constexpr int ROWS = VKIND ? D : 128, CODES = VKIND ? 128 : D, PITCH = VKIND ? PaSmem<D>::VP : PaSmem<D>::KP;
-  constexpr int ITEMS = ROWS * CODES / 64;
-#pragma unroll 1
-  for (int it = tid; it < ITEMS; it += 256) {
-    const int r = it / (CODES / 64), ch = it % (CODES / 64);
-    const uint8_t* src = rec + (size_t)r * (CODES * bits / 8) + ch * 8 * bits;
-    _Float16* dst = sm.hi + r * PITCH + 64 * ch;
-    switch (bits) {
-      case 2: codes64<2>(src, dst); break;
-      case 3: codes64<3>(src, dst); break;
-      case 4: codes64<4>(src, dst); break;
-      case 5: codes64<5>(src, dst); break;
-      case 6: codes64<6>(src, dst); break;
-      default: codes64<8>(src, dst); break;
-    }
-  }
-}
-
 __device__ __forceinline__ v8h ld8(const _Float16* p) { return *reinterpret_cast<const v8h*>(p); }
 
-}  // namespace
+// Tile row written by thread index x in the staging (bits 2 and 3 swapped).
+__device__ __forceinline__ int write_row(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int D, int GQ>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
-  __shared__ PaSmem<D> sm;
-  constexpr int KS = D / 32;   // MFMA k-steps over the channels
-  constexpr int NCT = D / 16;  // output channel tiles
-  constexpr int POS = 64 / GQ; // positions per workgroup
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int G = l >> 4, n = l & 15;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int nseq = a.c.seq_len[b];
-  const int C = a.chunk;
-  const int64_t bh = (int64_t)b * a.c.hkv + kvh;
-  // Position of workgroup row r (or -1 if the row is outside the chunk).
-  auto row_pos = [&](int r) {
-    const int i = blockIdx.x * POS + r / GQ;
-    const int p = nseq - C + i;
-    return (i < C && p >= 0) ? p : -1;
-  };
-  int pmax = -1;
-#pragma unroll 1
-  for (int r = 0; r < 64; ++r) pmax = max(pmax, row_pos(r));
-
-  // ---- queries: rotated and scaled by softmax_scale * log2(e), staged in
-  // LDS (fp32, 64 rows x D) through the K tile space, then read in A order.
-  {
-    float* qs = reinterpret_cast<float*>(sm.hi);   // 64 x D fp32 fits in the tile space
-    constexpr int NT = D / 64;
-#pragma unroll 1
-    for (int it = tid; it < 64 * NT; it += 256) {
-      const int r = it / NT, chunk = it % NT;
-      const int p = row_pos(r);
-      const int hq = kvh * GQ + r % GQ;
-      const int i = blockIdx.x * POS + r / GQ;
-      float x[64];
-      load64h(x, a.q + (((int64_t)b * C + (p >= 0 ? i : 0)) * a.hq + hq) * D + 64 * chunk, p >= 0);
-      // rotate64 needs the NT threads of a row in adjacent lanes: it = r*NT + chunk
-      rotate64<D>(x, chunk);
+// Output rotation by H_D / sqrt(D) over the C-layout channels 16 ct + 4 G + i
+// of one query row: butterflies over i and ct in registers, over G across
+// the lane groups.
+template <int NCT>
+__device__ __forceinline__ void rotate_out(v4f (&o)[NCT], int G) {
 #pragma unroll
-      for (int k = 0; k < 64; ++k) qs[r * D + 64 * chunk + k] = x[k] * a.scale * kPaLog2e;
-    }
+  for (int c = 0; c < NCT; ++c) {
+    const float a0 = o[c][0] + o[c][1], a1 = o[c][0] - o[c][1];
+    const float a2 = o[c][2] + o[c][3], a3 = o[c][2] - o[c][3];
+    o[c] = v4f{a0 + a2, a1 + a3, a0 - a2, a1 - a3};
   }
-  lds_barrier();
-  float qr[KS][8];   // A operand order: row 16w + n', n' = l % 16; channels 32s + 8G + e
-  {
-    const float* qs = reinterpret_cast<const float*>(sm.hi);
-    const int r = 16 * w + n;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qr[s][e] = qs[r * D + 32 * s + 8 * G + e];
-  }
-  // C-layout rows of this lane: 16w + 4G + i.
-  int prow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) prow[i] = row_pos(16 * w + 4 * G + i);
-
-  float m_run[4], l_run[4];
-  v4f o[NCT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
-  const int n_tiles = 1 + n_groups + 1;   // sink, records, tail
-#pragma unroll 1
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    // Tile positions [base, base + count) and its storage.
-    int base, count;
-    const uint8_t* rec = nullptr;
-    const bool exact = tile == 0 || tile == n_tiles - 1;
-    if (tile == 0) {
-      base = 0;
-      count = min(nseq, kSink);
-    } else if (tile == n_tiles - 1) {
-      base = kSink + kGroup * n_groups;
-      count = nseq > base ? nseq - base : 0;
-    } else {
-      base = kSink + kGroup * (tile - 1);
-      count = kGroup;
-      const int64_t off = pair_offset(a.c.map, b, kvh, tile - 1, a.c.hkv, a.c.max_groups, a.c.group_bytes);
-      if (off < 0) continue;   // no storage: the group is absent (uniform over the workgroup)
-      rec = a.c.records + off;
-    }
-    if (count <= 0 || base > pmax) continue;   // uniform over the workgroup
-
-    lds_barrier();   // the previous tile's V operands have been read
-    // ---- stage K and every scale of the tile
-    if (exact) {
-      const __half* src = (tile == 0 ? a.c.sink_k : a.c.tail_k) + bh * kGroup * D;
-      stage_exact<D, false>(sm, src, count, tid);
-      for (int t = tid; t < 128; t += 256) sm.sk[t] = sm.sv[t] = 1.f;
-      for (int j = tid; j < D; j += 256) sm.ck[j] = sm.cv[j] = 1.f;
-    } else {
-      stage_codes<D, false>(sm, rec, a.k_bits, tid);
-      const int kcode = kGroup * D * a.k_bits / 8, vrec = a.c.rec_k_bytes, vcode = kGroup * D * a.v_bits / 8;
-      const uint16_t* sK = reinterpret_cast<const uint16_t*>(rec + kcode);
-      const uint16_t* sV = reinterpret_cast<const uint16_t*>(rec + vrec + vcode);
-      for (int t = tid; t < 128; t += 256) {
-        sm.sk[t] = h2f(sK[t]);
-        sm.sv[t] = h2f(sV[t]);
-      }
-      for (int j = tid; j < D; j += 256) {
-        sm.ck[j] = h2f(sK[kGroup + j]);
-        sm.cv[j] = h2f(sV[kGroup + j]);
-      }
-    }
-    lds_barrier();
-
-    // ---- QK: logits of the wave's 16 rows x 128 tokens (8 token tiles).
-    // q~ of row n, scaled by a power of two per row (its inverse goes to the
-    // C-layout lanes of that row through the wave's LDS area).
-    v8h ahi[KS], alo[KS];
-    {
-      float qt[KS][8];
-      float mx = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qt[s][e] = qr[s][e] * sm.ck[32 * s + 8 * G + e];
-          mx = fmaxf(mx, fabsf(qt[s][e]));
-        }
-      float inv;
-      const float sc = pow2_scale(max_over_groups(mx), inv);
-      if (G == 0) sm.qscale[w][n] = inv;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = qt[s][e] * sc;
-          const _Float16 h = (_Float16)x;
-          ahi[s][e] = h;
-          alo[s][e] = (_Float16)(x - (float)h);
-        }
-    }
-    wave_sync();
-    float qinv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qinv[i] = sm.qscale[w][4 * G + i];
-    float lg[8][4];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const _Float16* krow = sm.hi + (16 * tt + n) * PaSmem<D>::KP + 8 * G;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const v8h bk = ld8(krow + 32 * s);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], bk, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bk, acc, 0, 0, 0);
-      }
-      if (exact) {
-        const _Float16* klo = sm.lo + (16 * tt + n) * PaSmem<D>::KP + 8 * G;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], ld8(klo + 32 * s), acc, 0, 0, 0);
-      }
-      const int tok = 16 * tt + n;
-      const float st = sm.sk[tok];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lg[tt][i] = (tok < count && base + tok <= prow[i]) ? acc[i] * (st * qinv[i]) : -INFINITY;
-    }
-
-    // ---- online softmax per row (row 4G + i of the wave spans the 16 lanes of DPP row G)
-    float alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = lg[0][i];
-#pragma unroll
-      for (int tt = 1; tt < 8; ++tt) mx = fmaxf(mx, lg[tt][i]);
-      mx = row16_max(mx);
-      const float m_new = fmaxf(m_run[i], mx);
-      alpha[i] = (m_new == -INFINITY || m_run[i] == -INFINITY) ? (m_new == -INFINITY ? 1.f : 0.f)
-                                                                 : __builtin_amdgcn_exp2f(m_run[i] - m_new);
-      float ps = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const float p = lg[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[tt][i] - m_new);
-        ps += p;
-        lg[tt][i] = p * sm.sv[16 * tt + n];   // w = p * s^V (1 for exact tiles)
-      }
-      l_run[i] = fmaf(l_run[i], alpha[i], row16_sum(ps));
-      m_run[i] = m_new;
-    }
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[c][i] *= alpha[i];
-
-    // ---- w as the PV A operand (hi + lo), scaled per row by a power of two,
-    // through the wave's LDS area: token step u = token tiles 2u, 2u + 1
-    float winv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) mx = fmaxf(mx, lg[tt][i]);
-      const float sc = pow2_scale(row16_max(mx), winv[i]);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) lg[tt][i] *= sc;
-    }
-    v8h whi[4], wlo[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = lg[2 * u + q][i];
-          const _Float16 h = (_Float16)x;
-          sm.p[w][0][4 * G + i][16 * q + n] = h;
-          sm.p[w][1][4 * G + i][16 * q + n] = (_Float16)(x - (float)h);
-        }
-      }
-      wave_sync();
-      whi[u] = ld8(&sm.p[w][0][n][8 * G]);
-      wlo[u] = ld8(&sm.p[w][1][n][8 * G]);
-      wave_sync();
-    }
-
-    lds_barrier();   // every wave is done with the K tile
-    // ---- stage V
-    if (exact)
-      stage_exact<D, true>(sm, (tile == 0 ? a.c.sink_v : a.c.tail_v) + bh * kGroup * D, count, tid);
-    else
-      stage_codes<D, true>(sm, rec + a.c.rec_k_bytes, a.v_bits, tid);
-    lds_barrier();
-
-    // ---- PV: channel tiles of 16, token steps of 32; records scale by c^V
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const _Float16* vrow = sm.hi + (16 * ct + n) * PaSmem<D>::VP + 8 * G;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v8h bv = ld8(vrow + 32 * u);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(whi[u], bv, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo[u], bv, acc, 0, 0, 0);
-      }
-      if (exact) {
-        const _Float16* vlo = sm.lo + (16 * ct + n) * PaSmem<D>::VP + 8 * G;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(whi[u], ld8(vlo + 32 * u), acc, 0, 0, 0);
-      }
-      const float cvj = sm.cv[16 * ct + n];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[ct][i] = fmaf(cvj * winv[i], acc[i], o[ct][i]);
-    }
-  }
-
-  // ---- normalize, rotate back (H symmetric: channel 16 ct + n; butterflies
-  // over the bits of ct in registers, over the bits of n across the row's
-  // lanes), write the rows of this lane.
 #pragma unroll
   for (int st = 1; st < NCT; st <<= 1) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       if (!(c & st)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float u = o[c][i], v = o[c + st][i];
-          o[c][i] = u + v;
-          o[c + st][i] = u - v;
-        }
+        const v4f u = o[c], v = o[c + st];
+        o[c] = u + v;
+        o[c + st] = u - v;
       }
     }
   }
 #pragma unroll
-  for (int st = 1; st < 16; st <<= 1) {
-    const bool upper = n & st;
+  for (int gb = 1; gb < 4; gb <<= 1) {
+    const bool upper = G & gb;
 #pragma unroll
     for (int c = 0; c < NCT; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = dpp_pair_f(o[c][i], st);
-        o[c][i] = upper ? pv - o[c][i] : o[c][i] + pv;
+        const float x = o[c][i];
+        const float y = __shfl_xor(x, 16 * gb);
+        o[c][i] = upper ? y - x : x + y;
       }
   }
-  const float rs = D == 128 ? 0.08838834764831845f : 0.0625f;
+  const float rs = NCT == 8 ? 0.08838834764831845f : 0.0625f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + 4 * G + i;
-    if (prow[i] < 0) continue;
-    const int pi = blockIdx.x * POS + r / GQ;
-    const int hq = kvh * GQ + r % GQ;
-    const float inv = l_run[i] > 0.f ? rs / l_run[i] : 0.f;
-    float* out = a.out + (((int64_t)b * C + pi) * a.hq + hq) * D;
+  for (int c = 0; c < NCT; ++c) o[c] *= rs;
+}
+
+// ---- code decode -----------------------------------------------------------
+// x holds 2c0 in bits 1.. and 2c1 in bits 17..: (512 + c0, 512 + c1) - (512 + mid).
+__device__ __forceinline__ uint32_t code_pair(uint32_t x, v2h off) {
+  const v2h h = __builtin_bit_cast(v2h, x | 0x60006000u) + off;
+  return __builtin_bit_cast(uint32_t, h);
+}
+// (x & m) | c in one instruction: VOP3 takes no literal operand and one
+// scalar operand on this target, so m sits in a vector and c in a scalar
+// register (the compiler would emit a separate AND and OR with literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "s"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t biased_code_pair(uint32_t x, v2h off) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, x) + off);
+}
+
+// 64 codes of BITS bits (a little-endian bit stream in w) -> 64 fp16
+// (code - mid) at dst, in the width's pair order.
+template <int BITS>
+__device__ __forceinline__ void decode_item(const uint32_t* w, _Float16* dst) {
+  constexpr float MID = 0.5f * ((1 << BITS) - 1);
+  const v2h off = {(_Float16)(-512.f - MID), (_Float16)(-512.f - MID)};
+  uint32_t out[32];
+  if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
+    constexpr int HALF = 16 / BITS;   // output dwords per input dword
+    constexpr uint32_t M = ((1u << BITS) - 1) << 1;
+    constexpr uint32_t MASK = M | (M << 16);
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) out[16 * c + n] = o[c][i] * inv;
+    for (int d = 0; d < 2 * BITS; ++d)
+#pragma unroll
+      for (int m = 0; m < HALF; ++m) {
+        const uint32_t x = m == 0 ? (w[d] << 1) : (w[d] >> (BITS * m - 1));
+        out[HALF * d + m] = biased_code_pair(and_or(x, MASK, 0x60006000u), off);
+      }
+  } else {
+    constexpr uint32_t M = (1u << BITS) - 1;
+#pragma unroll
+    for (int o = 0; o < 32; ++o) {
+      uint32_t c[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int bit = BITS * (2 * o + h), wi = bit >> 5, sh = bit & 31;
+        c[h] = sh + BITS <= 32 ? (w[wi] >> sh) & M : __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & M;
+      }
+      out[o] = code_pair((c[0] << 1) | (c[1] << 17), off);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    reinterpret_cast<uint4*>(dst)[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
+}
+
+template <int MAXB>
+__device__ __forceinline__ void decode_item_rt(const uint32_t (&w)[2 * MAXB], int bits, _Float16* dst) {
+  switch (bits) {
+    case 2: decode_item<2>(w, dst); break;
+    case 3: decode_item<3>(w, dst); break;
+    case 4: decode_item<4>(w, dst); break;
+    default:
+      if constexpr (MAXB >= 8) {
+        if (bits == 5) decode_item<5>(w, dst);
+        else if (bits == 6) decode_item<6>(w, dst);
+        else decode_item<8>(w, dst);
+      }
+      break;
   }
 }
 
-template <int D>
+// The 8 * bits bytes of one 64-code item (8-byte aligned).
+template <int MAXB>
+__device__ __forceinline__ void load_item(uint32_t (&w)[2 * MAXB], const uint8_t* src, int bits) {
+#pragma unroll
+  for (int k = 0; k < MAXB; ++k) {
+    if (k < bits) {
+      const uint2 x = reinterpret_cast<const uint2*>(src)[k];
+      w[2 * k] = x.x;
+      w[2 * k + 1] = x.y;
+    }
+  }
+}
+
+}  // namespace
+
+template <int D, int GQ, int MAXB>
+__global__ __launch_bounds__(256, D == 128 ? 2 : 1) void prefill_attn_kernel(PrefillAttnArgs a) {
+  __shared__ PaSmem<D> sm;
+  constexpr int KS = D / 32;    // MFMA k-steps over the channels
+  constexpr int NCT = D / 16;   // output channel tiles
+  constexpr int POS = 64 / GQ;  // positions per workgroup
+  constexpr int NI = D / 128;   // K (and V) items of 64 codes per thread
+  constexpr int KP = PaSmem<D>::KP, VP = PaSmem<D>::VP, QP = PaSmem<D>::QP;
+  const int w = threadIdx.x >> 6;
+  int tid = threadIdx.x, l = tid & 63;   // re-derived per tile (see the tile loop)
+  const int G = l >> 4, n = l & 15;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int nseq = a.c.seq_len[b];
+  const int C = a.chunk;
+  const int64_t bh = (int64_t)b * a.c.hkv + kvh;
+  const int kb = a.k_bits, vb = a.v_bits;
+  const int Bk = perm_block(kb), Bv = perm_block(vb);
+  const float qk_scale = a.scale * kPaLog2e;
+  auto row_pos = [&](int r) {   // position of workgroup row r, or -1
+    const int i = blockIdx.x * POS + r / GQ;
+    const int p = nseq - C + i;
+    return (i < C && p >= 0) ? p : -1;
+  };
+  auto krow_of_token = [&](int t) { return vpos_to_krow(code_to_pos(t, Bv)); };
+  auto token_of_krow = [&](int r) { return pos_to_code(krow_to_vpos(r), Bv); };
+  int pmax = -1, pmin = 0x7fffffff;
+#pragma unroll 1
+  for (int r = 0; r < 64; ++r) {
+    const int p = row_pos(r);
+    if (p >= 0) {
+      pmax = max(pmax, p);
+      pmin = min(pmin, p);
+    }
+  }
+  if (pmax < 0) return;   // no row of this block is in the chunk (uniform)
+
+  const int r_lane = 16 * w + n;
+  const int prow = row_pos(r_lane);
+  const __half* qrow =
+      a.q + (((int64_t)b * C + blockIdx.x * POS + r_lane / GQ) * a.hq + kvh * GQ + r_lane % GQ) * D;
+
+  // ---- queries: rotated, times softmax_scale * log2(e), times a per-row
+  // power of two that puts the row's largest magnitude in [2^11, 2^12)
+  // (fp32 in LDS over the K tile); then read as the B operand in the K
+  // width's pair order.
+  {
+    float* qs = reinterpret_cast<float*>(sm.k);
+    constexpr int NT = D / 64;
+#pragma unroll 1
+    for (int it = tid; it < 64 * NT; it += 256) {
+      const int r = it / NT, chunk = it % NT;
+      const int p = row_pos(r);
+      float x[64];
+      load64h(x,
+              a.q + (((int64_t)b * C + (p >= 0 ? blockIdx.x * POS + r / GQ : 0)) * a.hq + kvh * GQ + r % GQ) * D +
+                  64 * chunk,
+              p >= 0);
+      rotate64<D>(x, chunk);   // the NT threads of a row are adjacent lanes
+      float mx = 0.f;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) mx = fmaxf(mx, fabsf(x[k]));
+      mx = fmaxf(mx, dpp_pair_f(mx, 1));
+      if (NT == 4) mx = fmaxf(mx, dpp_pair_f(mx, 2));
+      float inv;
+      const float sc = pow2_scale(mx * qk_scale, inv) * qk_scale;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) qs[r * QP + 64 * chunk + k] = x[k] * sc;
+      if (chunk == 0) sm.qinv[r] = inv;
+    }
+  }
+  lds_barrier();
+  float qr[KS][8];
+  {
+    const float* qs = reinterpret_cast<const float*>(sm.k);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qr[s][e] = qs[r_lane * QP + pos_to_code(32 * s + 8 * G + e, Bk)];
+  }
+  const float qinv = sm.qinv[r_lane];
+  lds_barrier();   // the staged queries are read; the K tile is free
+
+  // ---- staging --------------------------------------------------------------
+  // Exact tile: `count` fp16 rows [128][D] at src (rows past count are zero).
+  auto stage_k_exact = [&](const __half* __restrict__ src, int count) {
+#pragma unroll 4
+    for (int idx = tid; idx < 128 * D / 8; idx += 256) {
+      const int r = write_row(idx & 127), c8 = idx >> 7;
+      const int t = token_of_krow(r);
+      const uint4 x = t < count ? *reinterpret_cast<const uint4*>(src + (size_t)t * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sm.k + r * KP + 8 * c8) = x;
+    }
+    for (int t = tid; t < 128; t += 256) {
+      sm.sk[t] = 1.f;
+      sm.sv[t] = 1.f;
+    }
+  };
+  auto stage_v_exact = [&](const __half* __restrict__ src, int count) {
+#pragma unroll 4
+    for (int idx = tid; idx < 128 * D / 8; idx += 256) {
+      const int t = idx % 128, c8 = idx / 128;
+      const uint4 x = t < count ? *reinterpret_cast<const uint4*>(src + (size_t)t * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+      const int p = code_to_pos(t, Bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sm.v[(8 * c8 + e) * VP + p] = __builtin_bit_cast(_Float16, (uint16_t)(xs[e >> 1] >> (16 * (e & 1))));
+    }
+    for (int j = tid; j < D; j += 256) sm.cv[j] = 1.f;
+  };
+
+  // Record tile: registers of the next record (codes of this thread's items,
+  // and the scale dwords of this wave's scale vector: wave 0 s^K, wave 1
+  // c^K, wave 2 s^V, wave 3 c^V).
+  uint32_t rk[NI][2 * MAXB], rv[NI][2 * MAXB], rs[NI];
+  const int kcode = 16 * D * kb, vcode = 16 * D * vb, vrec = a.c.rec_k_bytes;
+  // Tile-invariant item placement of this thread (kept in registers): K item
+  // = tile row write_row(it % 128), holding token token_of_krow(that row),
+  // 64-channel chunk it / 128; V item = channel write_row(it % D), 64-token
+  // chunk it / D.  Byte offsets within the record, element offsets in LDS.
+  int koff[NI], voff[NI], kdst[NI], vdst[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int it = (int)threadIdx.x + 256 * i;
+    const int r = write_row(it & 127), jv = write_row(it & (D - 1));
+    koff[i] = (token_of_krow(r) * (D / 64) + (it >> 7)) * 8 * kb;
+    kdst[i] = r * KP + 64 * (it >> 7);
+    voff[i] = vrec + (2 * jv + it / D) * 8 * vb;
+    vdst[i] = jv * VP + 64 * (it / D);
+  }
+  const int soff = (w < 2 ? kcode : vrec + vcode) + 4 * ((w & 1) ? 64 + l : l);
+  auto issue_record = [&](const uint8_t* __restrict__ rec) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      load_item<MAXB>(rk[i], rec + koff[i], kb);
+      load_item<MAXB>(rv[i], rec + voff[i], vb);
+    }
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(rec + soff);
+    rs[0] = sc[0];
+    if (NI > 1 && (w & 1)) rs[NI - 1] = sc[64];
+  };
+  auto stage_k_record = [&]() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) decode_item_rt<MAXB>(rk[i], kb, sm.k + kdst[i]);
+    if (w == 0) {
+      sm.sk[krow_of_token(2 * l)] = h2f((uint16_t)(rs[0] & 0xFFFFu));
+      sm.sk[krow_of_token(2 * l + 1)] = h2f((uint16_t)(rs[0] >> 16));
+    } else if (w == 1 || w == 2) {
+      // normalize c^K (wave 1) or s^V (wave 2) by the power of two of its
+      // maximum, so that q~ stays below 2^12 and w = p s^V below 1
+      const int nd = w == 1 ? NI : 1;
+      float x[2 * NI];
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        x[2 * i] = h2f((uint16_t)(rs[i] & 0xFFFFu));
+        x[2 * i + 1] = h2f((uint16_t)(rs[i] >> 16));
+        if (i < nd) mx = fmaxf(mx, fmaxf(x[2 * i], x[2 * i + 1]));
+      }
+      mx = wave_max_f(mx);
+      int e;
+      (void)frexpf(mx, &e);
+      const float down = ldexpf(1.f, -e);
+      if (w == 1) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) sm.ck[code_to_pos(2 * (l + 64 * i) + h, Bk)] = x[2 * i + h] * down;
+        if (l == 0) sm.kscale = ldexpf(1.f, e);
+      } else {
+        sm.sv[krow_of_token(2 * l)] = x[0] * down;
+        sm.sv[krow_of_token(2 * l + 1)] = x[1] * down;
+        if (l == 0) sm.vscale = ldexpf(1.f, e);
+      }
+    }
+  };
+  auto stage_v_record = [&]() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) decode_item_rt<MAXB>(rv[i], vb, sm.v + vdst[i]);
+    if (w == 3) {
+      const float up = sm.vscale;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        sm.cv[2 * (l + 64 * i)] = h2f((uint16_t)(rs[i] & 0xFFFFu)) * up;
+        sm.cv[2 * (l + 64 * i) + 1] = h2f((uint16_t)(rs[i] >> 16)) * up;
+      }
+    }
+  };
+
+  // ---- tiles: 0 = sink, 1 .. n_rec = records (group t - 1), then the tail
+  const int n_groups = nseq > kSink ? min((nseq - kSink) / kGroup, a.c.max_groups) : 0;
+  const int n_rec = pmax >= kSink ? min(n_groups, (pmax - kSink) / kGroup + 1) : 0;
+  const int tail_base = kSink + kGroup * n_groups;
+  const bool has_tail = n_rec == n_groups && nseq > tail_base && tail_base <= pmax;
+  const int T = 1 + n_rec + (has_tail ? 1 : 0);
+  const int tail_count = min(nseq - tail_base, kGroup);
+  const int32_t* table = a.c.map.table;
+  int ent = (table && n_rec > 0) ? table[(int64_t)b * a.c.max_groups] : 0;
+
+  stage_k_exact(a.c.sink_k + bh * kGroup * D, min(nseq, kSink));
+  stage_v_exact(a.c.sink_v + bh * kGroup * D, min(nseq, kSink));
+  lds_barrier();
+
+  PhaseClock pc;   // trace build only: cycles per phase, summed over the tiles
+  phase_start(pc);
+  float m_run = -INFINITY, l_run = 0.f;
+  v4f o[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  bool rotated = false;   // frame of o
+  bool present = true;    // tile t has storage
+
+#pragma unroll 1
+  for (int t = 0; t < T; ++t) {
+    // Per-lane index math of the staging and masking (tens of values) is
+    // cheaper to recompute per tile than to keep live across the loop.
+    asm volatile("" : "+v"(tid));
+    l = tid & 63;
+    const bool exact = t == 0 || (has_tail && t == T - 1);
+    const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
+    const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
+
+    // ---- issue the next record's loads (its map entry was read a tile ago)
+    bool next_present = t + 1 < T;
+    if (t + 1 <= n_rec) {
+      const int g = t;
+      int64_t off;
+      if (!table)
+        off = (bh * a.c.max_groups + g) * a.c.group_bytes;
+      else
+        off = (ent >= 0 && ent < a.c.map.num_blocks) ? ((int64_t)ent * a.c.hkv + kvh) * a.c.group_bytes : -1;
+      next_present = off >= 0;
+      if (next_present) issue_record(a.c.records + off);
+      if (table && g + 1 < n_rec) ent = table[(int64_t)b * a.c.max_groups + g + 1];
+    }
+
+    phase_end(pc, 0);   // next record's loads issued
+    // ---- QK^T: logits of the lane's row for K tile rows 16 tt + 4 G + i
+    v8h bhi[KS], blo[KS];
+    float f;   // logit scale to log2 units
+    if (exact) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 x = prow >= 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * G) : make_uint4(0, 0, 0, 0);
+        bhi[s] = __builtin_bit_cast(v8h, x);
+        blo[s] = v8h{};   // one code path for both kinds: the low product adds zero
+      }
+      f = qk_scale;
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v4f c0 = *reinterpret_cast<const v4f*>(sm.ck + 32 * s + 8 * G);
+        const v4f c1 = *reinterpret_cast<const v4f*>(sm.ck + 32 * s + 8 * G + 4);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float x0 = qr[s][e] * (e < 4 ? c0[e] : c1[e - 4]);
+          const float x1 = qr[s][e + 1] * (e < 4 ? c0[e + 1] : c1[e - 3]);
+          const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);   // fp16-exact high part
+          const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+          const auto ph = __builtin_amdgcn_cvt_pkrtz(h0, h1);
+          const auto pl = __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1);
+          bhi[s][e] = ph[0];
+          bhi[s][e + 1] = ph[1];
+          blo[s][e] = pl[0];
+          blo[s][e + 1] = pl[1];
+        }
+      }
+      f = qinv * sm.kscale;
+    }
+    phase_end(pc, 1);   // query operand of the tile
+    float lg[8][4];
+#pragma unroll
+    for (int tp = 0; tp < 8; tp += 2) {   // two token tiles at a time: independent MFMA chains
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      const _Float16* kr0 = sm.k + (16 * tp + n) * KP + 8 * G;
+      const _Float16* kr1 = kr0 + 16 * KP;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v8h a0 = ld8(kr0 + 32 * s), a1 = ld8(kr1 + 32 * s);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bhi[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bhi[s], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, blo[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, blo[s], acc1, 0, 0, 0);
+      }
+      const v4f sk0 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 4 * G);
+      const v4f sk1 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 16 + 4 * G);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lg[tp][i] = acc0[i] * sk0[i];
+        lg[tp + 1][i] = acc1[i] * sk1[i];
+      }
+    }
+
+    phase_end(pc, 2);   // QK products
+    // ---- online softmax of the lane's row (its 128 tokens span the four lane
+    // groups); tiles below every row of the block and complete need no mask
+    const bool full = __builtin_amdgcn_readfirstlane((int)(count == kGroup && base + kGroup - 1 <= pmin)) != 0;
+    float alpha, m_new, ps = 0.f;
+    if (full) {
+      float mx = lg[0][0];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[tt][i]);
+      m_new = fmaxf(m_run, max_over_groups(mx) * f);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lg[tt][i] = __builtin_amdgcn_exp2f(fmaf(lg[tt][i], f, -m_new));
+          ps += lg[tt][i];
+        }
+    } else {
+      // causal and length mask: token of K tile row 16 tt + 4 G + i
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = token_of_krow(16 * tt + 4 * (l >> 4) + i);
+          if (!(tok < count && base + tok <= prow)) lg[tt][i] = -INFINITY;
+        }
+      float mx = lg[0][0];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[tt][i]);
+      m_new = fmaxf(m_run, max_over_groups(mx) * f);
+      alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lg[tt][i] = lg[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(lg[tt][i], f, -m_new));
+          ps += lg[tt][i];
+        }
+    }
+    l_run = fmaf(l_run, alpha, xor32_sum(xor16_sum(ps)));
+    m_run = m_new;
+    v8h bwh[4], bwl[4];   // PV B operands: w = p * s^V (hi + lo) for positions 32 u + 8 G + e
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const v4f sv4 = *reinterpret_cast<const v4f*>(sm.sv + 16 * tt + 4 * G);
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float x0 = lg[tt][i] * sv4[i], x1 = lg[tt][i + 1] * sv4[i + 1];
+        const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);
+        const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+        const auto ph = __builtin_amdgcn_cvt_pkrtz(h0, h1);
+        const auto pl = __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1);
+        const int e = 4 * (tt & 1) + i;
+        bwh[tt >> 1][e] = ph[0];
+        bwh[tt >> 1][e + 1] = ph[1];
+        bwl[tt >> 1][e] = pl[0];
+        bwl[tt >> 1][e + 1] = pl[1];
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) o[c] *= alpha;
+    }
+
+    phase_end(pc, 3);   // softmax and the PV operands
+    // ---- the next tile's K half, once every wave is done with this K tile
+    if (t + 1 < T) {
+      lds_barrier();
+      phase_end(pc, 4);   // barrier A
+      if (t + 1 == T - 1 && has_tail)
+        stage_k_exact(a.c.tail_k + bh * kGroup * D, tail_count);
+      else if (next_present)
+        stage_k_record();
+    }
+
+    phase_end(pc, 5);   // K staging
+    // ---- PV: O^T += V^T w^T, channel tiles of 16, token steps of 32
+    if (rotated == exact) {   // frame change
+      rotate_out<NCT>(o, G);
+      rotated = !exact;
+    }
+#pragma unroll
+    for (int cp = 0; cp < NCT; cp += 2) {   // two channel tiles at a time
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      const _Float16* vr0 = sm.v + (16 * cp + n) * VP + 8 * G;
+      const _Float16* vr1 = vr0 + 16 * VP;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v8h a0 = ld8(vr0 + 32 * u), a1 = ld8(vr1 + 32 * u);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bwh[u], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bwh[u], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bwl[u], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bwl[u], acc1, 0, 0, 0);
+      }
+      const v4f cv0 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 4 * G);
+      const v4f cv1 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 16 + 4 * G);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[cp][i] = fmaf(acc0[i], cv0[i], o[cp][i]);
+        o[cp + 1][i] = fmaf(acc1[i], cv1[i], o[cp + 1][i]);
+      }
+    }
+
+    phase_end(pc, 6);   // PV products
+    // ---- the next tile's V half, once every wave is done with this V tile
+    if (t + 1 < T) {
+      lds_barrier();
+      phase_end(pc, 7);   // barrier B
+      if (t + 1 == T - 1 && has_tail)
+        stage_v_exact(a.c.tail_v + bh * kGroup * D, tail_count);
+      else if (next_present)
+        stage_v_record();
+    }
+    present = next_present;
+    phase_end(pc, 8);   // V staging
+  }
+  phase_store(((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 4 + w, pc);
+
+  if (rotated) rotate_out<NCT>(o, G);
+  if (prow >= 0) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* out = a.out + (((int64_t)b * C + blockIdx.x * POS + r_lane / GQ) * a.hq + kvh * GQ + r_lane % GQ) * D;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) *reinterpret_cast<v4f*>(out + 16 * c + 4 * G) = o[c] * inv;
+  }
+}
+
+#ifdef KVARN_WAVE_TRACE
+hipError_t trace_io_prefill_attn(void* host, size_t bytes) { return trace_io_local(host, bytes); }
+#endif
+
+template <int D, int MAXB>
 static void launch_pa_d(int gq, const PrefillAttnArgs& a, hipStream_t st) {
   const int pos = 64 / gq;
   const dim3 grid((a.chunk + pos - 1) / pos, a.c.hkv, a.c.batch);
   if (gq == 1)
-    hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<D, 1, MAXB>), grid, dim3(256), 0, st, a);
   else if (gq == 2)
-    hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<D, 2, MAXB>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<D, 4, MAXB>), grid, dim3(256), 0, st, a);
 }
 
 hipError_t launch_prefill_attn(int D, int gq, const PrefillAttnArgs& a, hipStream_t st) {
   if (a.chunk <= 0) return hipSuccess;
-  if (D == 128)
-    launch_pa_d<128>(gq, a, st);
-  else
-    launch_pa_d<256>(gq, a, st);
+  const bool wide = a.k_bits > 4 || a.v_bits > 4;
+  if (D == 128) {
+    if (wide)
+      launch_pa_d<128, 8>(gq, a, st);
+    else
+      launch_pa_d<128, 4>(gq, a, st);
+  } else {
+    if (wide)
+      launch_pa_d<256, 8>(gq, a, st);
+    else
+      launch_pa_d<256, 4>(gq, a, st);
+  }
   return hipGetLastError();
 }
 

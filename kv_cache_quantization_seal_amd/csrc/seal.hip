@@ -646,6 +646,10 @@ hipError_t launch_append_seal(int D, const AppendSealArgs& a, int nbh, hipStream
   return hipGetLastError();
 }
 
+#ifdef KVARN_WAVE_TRACE
+hipError_t trace_io_seal(void* host, size_t bytes) { return trace_io_local(host, bytes); }
+#endif
+
 hipError_t launch_seal_stream(int D, const SealStreamArgs& a, int nbh, hipStream_t st) {
   if (nbh <= 0) return hipSuccess;
   if (D == 128)

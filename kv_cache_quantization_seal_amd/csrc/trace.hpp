@@ -68,9 +68,48 @@ __device__ __forceinline__ void trace_mark(int slot, int phase) {
   }
   __builtin_amdgcn_sched_barrier(0);
 }
+
+// Loop kernels: core-clock cycles per phase, summed over the iterations of a
+// wave, in place of the phase timestamps: record [2 + p] = cycles spent in
+// phase p (p < kTracePhases), [1] / [kTraceWords-1] = the core-clock counter
+// at the first / last mark.  phase_end(c, p) closes phase p at this point.
+struct PhaseClock {
+  uint64_t first, last;
+  uint32_t acc[kTracePhases];
+};
+__device__ __forceinline__ void phase_start(PhaseClock& c) {
+  __builtin_amdgcn_sched_barrier(0);
+  c.first = c.last = __builtin_amdgcn_s_memtime();
+#pragma unroll
+  for (int p = 0; p < kTracePhases; ++p) c.acc[p] = 0;
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void phase_end(PhaseClock& c, int p) {
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t now = __builtin_amdgcn_s_memtime();
+  c.acc[p] += (uint32_t)(now - c.last);
+  c.last = now;
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void phase_store(int slot, const PhaseClock& c) {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));   // HW_ID
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11));  // XCC_ID
+  if ((threadIdx.x & 63) == 0 && slot >= 0 && slot < kTraceSlots) {
+    uint64_t* r = g_trace + (size_t)slot * kTraceWords;
+    r[0] = ((uint64_t)xcc << 32) | hw;
+    r[1] = c.first;
+#pragma unroll
+    for (int p = 0; p < kTracePhases; ++p) r[2 + p] = c.acc[p];
+    r[kTraceWords - 1] = c.last;
+  }
+}
 #else
 __device__ __forceinline__ void trace_begin(int) {}
 __device__ __forceinline__ void trace_mark(int, int) {}
+struct PhaseClock {};
+__device__ __forceinline__ void phase_start(PhaseClock&) {}
+__device__ __forceinline__ void phase_end(PhaseClock&, int) {}
+__device__ __forceinline__ void phase_store(int, const PhaseClock&) {}
 #endif
 
 }  // namespace kvarn
