@@ -287,16 +287,30 @@ __device__ __forceinline__ void decode_item_rt(const uint32_t (&w)[2 * MAXB], in
   }
 }
 
-// The 8 * bits bytes of one 64-code item (8-byte aligned).
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) int32_t ConstI32;   // read-only: scalar loads
+
+// Buffer resource over one record (`bytes` bytes at a wave-uniform address):
+// loads past its end return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int bytes) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(rec);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 8 * MAXB bytes from byte offset `off` of a record: the 8 * bits bytes of a
+// 64-code item (8-byte aligned) and whatever follows it.  A fixed number of
+// loads with no width test: loads under a width test get moved down to
+// their use, which would undo the prefetch.
 template <int MAXB>
-__device__ __forceinline__ void load_item(uint32_t (&w)[2 * MAXB], const uint8_t* src, int bits) {
+__device__ __forceinline__ void load_item(uint32_t (&w)[2 * MAXB], __amdgpu_buffer_rsrc_t r, int off) {
 #pragma unroll
   for (int k = 0; k < MAXB; ++k) {
-    if (k < bits) {
-      const uint2 x = reinterpret_cast<const uint2*>(src)[k];
-      w[2 * k] = x.x;
-      w[2 * k + 1] = x.y;
-    }
+    const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8 * k, 0, 0);
+    w[2 * k] = x[0];
+    w[2 * k + 1] = x[1];
   }
 }
 
@@ -434,14 +448,14 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void prefill_attn_kernel(Pre
   }
   const int soff = (w < 2 ? kcode : vrec + vcode) + 4 * ((w & 1) ? 64 + l : l);
   auto issue_record = [&](const uint8_t* __restrict__ rec) {
+    const __amdgpu_buffer_rsrc_t r = record_rsrc(rec, (int)a.c.group_bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      load_item<MAXB>(rk[i], rec + koff[i], kb);
-      load_item<MAXB>(rv[i], rec + voff[i], vb);
+      load_item<MAXB>(rk[i], r, koff[i]);
+      load_item<MAXB>(rv[i], r, voff[i]);
     }
-    const uint32_t* sc = reinterpret_cast<const uint32_t*>(rec + soff);
-    rs[0] = sc[0];
-    if (NI > 1 && (w & 1)) rs[NI - 1] = sc[64];
+    rs[0] = __builtin_amdgcn_raw_buffer_load_b32(r, soff, 0, 0);
+    if (NI > 1) rs[NI - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, soff + 256, 0, 0);   // c^K / c^V waves
   };
   auto stage_k_record = [&]() {
 #pragma unroll
@@ -499,7 +513,8 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void prefill_attn_kernel(Pre
   const int T = 1 + n_rec + (has_tail ? 1 : 0);
   const int tail_count = min(nseq - tail_base, kGroup);
   const int32_t* table = a.c.map.table;
-  int ent = (table && n_rec > 0) ? table[(int64_t)b * a.c.max_groups] : 0;
+  // Block-table entry of the next record (scalar loads, a tile ahead).
+  int ent = (table && n_rec > 0) ? *(ConstI32*)(table + (int64_t)b * a.c.max_groups) : 0;
 
   stage_k_exact(a.c.sink_k + bh * kGroup * D, min(nseq, kSink));
   stage_v_exact(a.c.sink_v + bh * kGroup * D, min(nseq, kSink));
@@ -524,31 +539,44 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void prefill_attn_kernel(Pre
     const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
     const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
 
-    // ---- issue the next record's loads (its map entry was read a tile ago)
+    // ---- exact tile: the fp16 query rows as the B operand.  Loaded and
+    // waited for before the next record's loads are issued: the load counter
+    // completes in order, so a wait for them issued later would also wait for
+    // that whole prefetch.
+    v8h bhi[KS], blo[KS];
+    if (exact) {
+      uint4 x[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        x[s] = prow >= 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * G) : make_uint4(0, 0, 0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        asm volatile("" : "+v"(x[s].x), "+v"(x[s].y), "+v"(x[s].z), "+v"(x[s].w));   // ready here
+        bhi[s] = __builtin_bit_cast(v8h, x[s]);
+        blo[s] = v8h{};   // one code path for both kinds: the low product adds zero
+      }
+    }
+
+    // ---- issue the next record's loads
     bool next_present = t + 1 < T;
     if (t + 1 <= n_rec) {
       const int g = t;
       int64_t off;
-      if (!table)
+      if (!table) {
         off = (bh * a.c.max_groups + g) * a.c.group_bytes;
-      else
+      } else {
         off = (ent >= 0 && ent < a.c.map.num_blocks) ? ((int64_t)ent * a.c.hkv + kvh) * a.c.group_bytes : -1;
+        if (g + 1 < n_rec) ent = *(ConstI32*)(table + (int64_t)b * a.c.max_groups + g + 1);
+      }
       next_present = off >= 0;
       if (next_present) issue_record(a.c.records + off);
-      if (table && g + 1 < n_rec) ent = table[(int64_t)b * a.c.max_groups + g + 1];
     }
 
     phase_end(pc, 0);   // next record's loads issued
     // ---- QK^T: logits of the lane's row for K tile rows 16 tt + 4 G + i
-    v8h bhi[KS], blo[KS];
     float f;   // logit scale to log2 units
     if (exact) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const uint4 x = prow >= 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * G) : make_uint4(0, 0, 0, 0);
-        bhi[s] = __builtin_bit_cast(v8h, x);
-        blo[s] = v8h{};   // one code path for both kinds: the low product adds zero
-      }
       f = qk_scale;
     } else {
 #pragma unroll

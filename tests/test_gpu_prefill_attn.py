@@ -105,3 +105,52 @@ def test_prefill_attn_full_size_sampled():
                 worst = max(worst, float(np.abs(out[0, i, h * gq + hh] - ref).max()))
     print(f"llama 32k chunk 512: sampled max abs err {worst:.3e}")
     assert worst <= ATTN_ATOL
+
+
+def test_prefill_attn_paged_with_absent_group():
+    """Block-table cache (shuffled blocks of a shared pool) with one table
+    entry outside the pool: that group has no storage and every query skips
+    its 128 positions; the other positions keep their places (the reference
+    attends over the oracle's full materialization minus that group)."""
+    d, hq, hkv, kb, vb = 128, 8, 2, 2, 4
+    lens, chunk, mg = [700, 460], 300, 5
+    B = len(lens)
+    states = _states(d, hkv, kb, vb, lens, 470)
+    cfg = K.make_config(d, hq, hkv, kb, vb)
+    nblk = B * mg + 3
+    cache = K.KVarNCache(cfg, B, mg, num_blocks=nblk)
+    table = np.random.default_rng(5).permutation(nblk)[:B * mg].astype(np.int32).reshape(B, mg)
+    absent = (0, 2)   # request 0, group 2: positions 384 .. 511
+    table[absent] = -1
+    cache.block_table.copy_(torch.from_numpy(table))
+    dev = cache.sink_k.device
+    for b, row in enumerate(states):
+        for h, st in enumerate(row):
+            cache.sink_k[b, h, :len(st.sink_k)] = torch.from_numpy(np.stack(st.sink_k)).to(dev)
+            cache.sink_v[b, h, :len(st.sink_v)] = torch.from_numpy(np.stack(st.sink_v)).to(dev)
+            if st.tail_k:
+                cache.tail_k[b, h, :st.tail_len] = torch.from_numpy(np.stack(st.tail_k)).to(dev)
+                cache.tail_v[b, h, :st.tail_len] = torch.from_numpy(np.stack(st.tail_v)).to(dev)
+            for g, (rk, rv) in enumerate(zip(st.rec_k, st.rec_v)):
+                if (b, g) != absent:
+                    cache.record(b, h, g, "k").copy_(torch.frombuffer(bytearray(rk), dtype=torch.uint8).to(dev))
+                    cache.record(b, h, g, "v").copy_(torch.frombuffer(bytearray(rv), dtype=torch.uint8).to(dev))
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32, device=dev))
+    q = np.random.default_rng(8).standard_normal((B, chunk, hq, d)).astype(np.float16)
+    out = cache.prefill_attn(torch.from_numpy(q).to(dev)).cpu().numpy()
+    gq = hq // hkv
+    worst = 0.0
+    for b, n in enumerate(lens):
+        mats = [st.materialize() for st in states[b]]
+        keep = np.ones(n, dtype=bool)
+        if b == absent[0]:
+            keep[128 + 128 * absent[1]:256 + 128 * absent[1]] = False
+        for i in range(0, chunk, 7):
+            p = n - chunk + i
+            sel = np.flatnonzero(keep[:p + 1])
+            for h in range(hq):
+                kall, vall = mats[h // gq]
+                ref = O.attention(q[b, i, h], kall[sel], vall[sel])
+                worst = max(worst, float(np.abs(out[b, i, h] - ref).max()))
+    print(f"paged, absent group: max abs err {worst:.3e}")
+    assert worst <= ATTN_ATOL
