@@ -63,15 +63,19 @@ def parse():
     ap.add_argument("--profile-seal", type=int, default=0, metavar="N",
                     help="if > 0: run N bulk seals (kvarn_prefill of the workload's prompt, K and V) only "
                          "(for rocprofv3) and exit")
+    ap.add_argument("--profile-prefill", type=int, default=0, metavar="N",
+                    help="if > 0: build the workload's cache, then run N chunked-prefill attention calls "
+                         "(--prefill-chunk query tokens) only (for rocprofv3) and exit")
     ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
                     help="print, per kernel whose name contains --kernel, the median over dispatches of every "
                          "counter found in the rocprofv3 --pmc output directories DIR..., and exit")
     ap.add_argument("--kernel", default="seal_prefill_kernel", help="kernel name filter for --counter-summary")
     ap.add_argument("--trace-max-groups", type=int, default=0,
                     help="with --trace: cache capacity in groups (default: the workload's own)")
-    ap.add_argument("--trace", choices=["decode", "seal"],
-                    help="load the trace build (libkvarn_trace.so), run the decode split kernel or the bulk seal "
-                         "of the workload cold a few times, print per-wave phase timestamps as JSON, and exit")
+    ap.add_argument("--trace", choices=["decode", "seal", "prefill"],
+                    help="load the trace build (libkvarn_trace.so), run the decode split kernel, the bulk seal or "
+                         "the chunked-prefill attention of the workload cold a few times, print per-wave phase "
+                         "timestamps (prefill: cycles per phase summed over the tiles) as JSON, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 8 device-to-device copies of MIB MiB (a plain copy kernel of known "
                          "size, the reference for the HBM counters) and exit")
@@ -226,6 +230,9 @@ def trace_run(args, reps=8):
     torch.cuda.synchronize()
     summaries = []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.trace == "prefill":
+        print(json.dumps(prefill_trace(args, wl, caches, e0, e1, flush_buf, sink)))
+        return
     for r in range(reps):
         probe.read(flush_buf, sink)
         torch.cuda.synchronize()
@@ -254,6 +261,42 @@ def trace_run(args, reps=8):
         summ["event_us"] = us
         summaries.append(summ)
     print(json.dumps({"workload": wl.name, "trace": args.trace, "plan": plan, "reps": summaries}))
+
+
+PREFILL_PHASES = ["issue_next_record", "query_operand", "qk_mfma", "softmax_and_pv_operands", "barrier_a",
+                  "stage_k", "pv_mfma", "barrier_b", "stage_v"]
+
+
+def prefill_trace(args, wl, caches, e0, e1, flush_buf, sink):
+    """Trace build, chunked-prefill attention: core-clock cycles per phase of
+    every wave, summed over its tiles; median over waves, per tile."""
+    import torch
+    from kv_cache_quantization_seal_amd import probe, wavetrace
+    dev = caches[0].sink_k.device
+    chunk = args.prefill_chunk
+    q = torch.from_numpy(np.random.default_rng(7).standard_normal(
+        (wl.batch, chunk, wl.num_q_heads, wl.head_dim)).astype(np.float16)).to(dev)
+    gq = wl.num_q_heads // wl.num_kv_heads
+    n_waves = -(-chunk * gq // 64) * wl.num_kv_heads * wl.batch * 4
+    reps = []
+    for c in caches[:3]:
+        probe.read(flush_buf, sink)
+        torch.cuda.synchronize()
+        wavetrace.clear(wavetrace.PREFILL_ATTN)
+        e0.record()
+        c.prefill_attn(q)
+        e1.record()
+        torch.cuda.synchronize()
+        rec = wavetrace.read(wavetrace.PREFILL_ATTN, n_waves).astype(np.int64)
+        ran = rec[:, 15] > rec[:, 1]
+        tiles = 1 + (wl.context - 128) // 128 + 1
+        cyc = rec[ran][:, 2:2 + len(PREFILL_PHASES)].astype(np.float64)
+        life = (rec[ran][:, 15] - rec[ran][:, 1]).astype(np.float64)
+        reps.append({"event_us": e0.elapsed_time(e1) * 1e3, "waves": int(ran.sum()), "tiles_per_wave": tiles,
+                     "wave_cycles_per_tile": float(np.median(life) / tiles),
+                     "phase_cycles_per_tile": {n: float(np.median(cyc[:, i]) / tiles)
+                                               for i, n in enumerate(PREFILL_PHASES)}})
+    return {"workload": wl.name, "trace": "prefill", "chunk": chunk, "reps": reps}
 
 
 def _cpu_model():
@@ -510,6 +553,26 @@ def main():
             cache.prefill(kd, vd, lens)
         torch.cuda.synchronize()
         print(f"[bench] seal profile run: {args.profile_seal} bulk seals of {wl.name}", file=sys.stderr, flush=True)
+        return
+
+    if args.profile_prefill > 0:
+        # Chunked-prefill attention only (after one bulk seal that builds the
+        # cache): its dispatches for a profiler.
+        wl = synth.WORKLOADS[args.workload]
+        lens = [wl.start_len(b) for b in range(wl.batch)]
+        dev = torch.device("cuda:0")
+        kd, vd = synth.kv_streams_device(wl, max(lens), dev)
+        cfg = K.make_config(wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.k_bits, wl.v_bits)
+        cache = K.KVarNCache(cfg, wl.batch, wl.max_groups(), device=dev)
+        cache.prefill(kd, vd, lens)
+        q = torch.from_numpy(np.random.default_rng(7).standard_normal(
+            (wl.batch, args.prefill_chunk, wl.num_q_heads, wl.head_dim)).astype(np.float16)).to(dev)
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        for _ in range(args.profile_prefill):
+            cache.prefill_attn(q, out=out)
+        torch.cuda.synchronize()
+        print(f"[bench] prefill attention profile run: {args.profile_prefill} calls, {args.prefill_chunk}-token "
+              f"chunk of {wl.name}", file=sys.stderr, flush=True)
         return
 
     if args.copy_calibration > 0:

@@ -5,7 +5,9 @@ trace code.
 
 Each wave slot holds (see csrc/trace.hpp): hardware ids, the core-clock
 counter at its start and at its last mark, and the 100 MHz real-time counter
-at phase marks 0..11 (0 = start; 0 where a wave did not reach a mark)."""
+at phase marks 0..11 (0 = start; 0 where a wave did not reach a mark); for
+the chunked-prefill attention kernel (a loop over tiles) the slots hold
+instead the core-clock cycles of each phase summed over the wave's tiles."""
 from __future__ import annotations
 
 import ctypes
@@ -16,6 +18,7 @@ WORDS = 16
 SLOTS = 32768
 REALTIME_HZ = 100e6
 SEAL = 1
+PREFILL_ATTN = 2   # loop kernel: record [2 + p] = core-clock cycles of phase p, summed over its tiles
 
 
 def decode(k_bits: int) -> int:
