@@ -38,8 +38,8 @@
 //             -> A_col[16][2] in VGPRs.
 //   A half-step reads 16 factors from LDS (four 128-bit reads of a skewed
 //   vector) for 32 register FMAs; the partial sums of a token pair (channel
-//   pair) sit in RL (8) adjacent lanes and meet through DPP; the first lane
-//   publishes the two new factors.  One barrier per half-step.  About 110
+//   pair) sit in RL (8) adjacent lanes and meet through DPP; the first two
+//   lanes publish the two new factors.  One barrier per half-step.  About 110
 //   VGPRs per lane and 70 KB (D 128) of LDS give two workgroups, four waves
 //   per SIMD, on a CU.
 #include "common.hpp"
@@ -181,7 +181,7 @@ __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& 
         make_float4((float)(x[4 * k] * rs), (float)(x[4 * k + 1] * rs), (float)(x[4 * k + 2] * rs),
                     (float)(x[4 * k + 3] * rs));
   if (tid < D) {
-    sm.u[sk(tid)] = 1.0f;
+    sm.u[sk(tid)] = 1.0f / D;
     sm.c2[tid] = 1.0f;
   }
   lds_barrier();
@@ -208,17 +208,36 @@ struct SealRoles {
 // Sinkhorn iterations on the tile that seal_rotate left in LDS: A = X_r^2 in
 // both roles' register blocks, then `iters` token and channel steps.  Leaves
 // c_j^2 in sm.c2; ends with a barrier.
+//
+// Scaling: sm.u holds u_j = 1 / (D c_j^2), so the token step's plain sum
+// sum_j A_tj u_j is r_t^2 itself, and the column role holds (D / T) A, so the
+// channel step's sum sum_t (D / T) A_tj v_t is D c_j^2, whose reciprocal is
+// the next u_j (powers of two only: exact).
+//
+// The lanes of a token pair (channel pair) with odd cb (tb) hold the pair in
+// swapped order, so one DPP add gives every lane the sum of its own first
+// token over itself and its neighbour: that folds both tokens into one value
+// per lane, and the remaining steps of the reduction (same parity throughout)
+// take one add each.  Lanes cb (tb) = 0 and 1 then hold the totals of the
+// pair's first and second token (channel) and publish them together.
+//
+// Publishing: a new factor is 1 / total, kept finite with a min so that an
+// all-zero row or column (total 0) has a factor that multiplies only zeros in
+// the next step; its A entries are all zero, so the other steps do not change
+// (the same as keeping its factor).  c_j^2 itself is stored in the last
+// iteration only, 1 for an all-zero column (its factor stays 1).
 template <int D>
 __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid) {
   constexpr int RL = SealRoles<D>::RL;
   const SealRoles<D> ro(tid);
   const int tp = ro.tp, cb = ro.cb, cp = ro.cp, tb = ro.tb;
+  const int rsw = cb & 1, csw = tb & 1;
   float ar[2][16], ac[16][2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(xg(sm, 2 * tp + r, 4 * cb + k));
+      const float4 a = *reinterpret_cast<const float4*>(xg(sm, 2 * tp + (r ^ rsw), 4 * cb + k));
       ar[r][4 * k] = a.x * a.x;
       ar[r][4 * k + 1] = a.y * a.y;
       ar[r][4 * k + 2] = a.z * a.z;
@@ -227,10 +246,12 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float2 a = *reinterpret_cast<const float2*>(xg(sm, 16 * tb + i, cp >> 1) + 2 * (cp & 1));
-    ac[i][0] = a.x * a.x;
-    ac[i][1] = a.y * a.y;
+    const float* a = xg(sm, 16 * tb + i, cp >> 1) + 2 * (cp & 1);
+    const float x0 = a[csw], x1 = a[csw ^ 1];
+    ac[i][0] = x0 * x0 * (float)(D / kGroup);
+    ac[i][1] = x1 * x1 * (float)(D / kGroup);
   }
+  constexpr float kBig = 3.40282347e38f;
 
   for (int it = 0; it < iters; ++it) {
     // Token step: r_t^2 = mean_j A_tj u_j.
@@ -244,23 +265,17 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
         uv[4 * k + 2] = q.z;
         uv[4 * k + 3] = q.w;
       }
-      float tot[2];
+      float pa = 0.f, pb = 0.f;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < 16; c += 2) {
-          p0 = fmaf(ar[r][c], uv[c], p0);
-          p1 = fmaf(ar[r][c + 1], uv[c + 1], p1);
-        }
-        tot[r] = sum_rl<RL>(p0 + p1);
+      for (int c = 0; c < 16; ++c) {
+        pa = fmaf(ar[0][c], uv[c], pa);
+        pb = fmaf(ar[1][c], uv[c], pb);
       }
-      if (cb == 0) {
-        float2 vv;
-        vv.x = tot[0] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[0]) : 0.f;
-        vv.y = tot[1] > 0.f ? (float)D * __builtin_amdgcn_rcpf(tot[1]) : 0.f;
-        *reinterpret_cast<float2*>(sm.v + sk(2 * tp)) = vv;
-      }
+      float tot = pa + dpp_f<0xB1>(pb);  // quad_perm [1,0,3,2]
+      tot += dpp_f<0x4E>(tot);           // quad_perm [2,3,0,1]
+      tot += dpp_f<0x104>(tot);          // row_shl:4 (lanes 0, 1 of each eight read 4, 5)
+      if constexpr (RL == 16) tot += dpp_f<0x108>(tot);  // row_shl:8
+      if (cb < 2) sm.v[sk(2 * tp + cb)] = fminf(__builtin_amdgcn_rcpf(tot), kBig);
     }
     lds_barrier();
     // Channel step: c_j^2 = mean_t A_tj v_t.
@@ -274,31 +289,32 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
         vt[4 * k + 2] = q.z;
         vt[4 * k + 3] = q.w;
       }
-      float tot[2];
+      float qa = 0.f, qb = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float q0 = 0.f, q1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          q0 = fmaf(ac[i][c], vt[i], q0);
-          q1 = fmaf(ac[i + 1][c], vt[i + 1], q1);
-        }
-        tot[c] = sum8(q0 + q1);
+      for (int i = 0; i < 16; ++i) {
+        qa = fmaf(ac[i][0], vt[i], qa);
+        qb = fmaf(ac[i][1], vt[i], qb);
       }
-      if (tb == 0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          if (tot[c] > 0.f) {
-            sm.c2[2 * cp + c] = tot[c] * (1.0f / kGroup);
-            sm.u[sk(2 * cp + c)] = (float)kGroup * __builtin_amdgcn_rcpf(tot[c]);
-          } else {
-            sm.u[sk(2 * cp + c)] = 0.f;
-          }
-        }
+      float tot = qa + dpp_f<0xB1>(qb);
+      tot += dpp_f<0x4E>(tot);
+      tot += dpp_f<0x104>(tot);
+      if (tb < 2) {
+        sm.u[sk(2 * cp + tb)] = fminf(__builtin_amdgcn_rcpf(tot), kBig);
+        if (it == iters - 1) sm.c2[2 * cp + tb] = tot > 0.f ? tot * (1.0f / D) : 1.f;
       }
     }
     lds_barrier();
   }
+}
+
+// Code of a value y = x / step + mid that lies in [0, 2^BITS - 1] up to a few
+// fp32 rounding errors (|x| / step <= (2^BITS - 1) / 2 by the choice of the
+// step): adding 2^23 rounds y to an integer, half to even, as rintf does, and
+// leaves that integer in the low mantissa bits; a y a little below 0 (above
+// 2^BITS - 1) rounds to 0 (2^BITS - 1), so no clamp is needed.
+template <int BITS>
+__device__ __forceinline__ uint32_t rtn_code(float y) {
+  return __float_as_uint(y + 8388608.0f) & ((1u << BITS) - 1u);
 }
 
 // Sixteen codes of one record row as a little-endian bit stream: code e
@@ -398,7 +414,7 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
       uint32_t code[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        code[e] = (uint32_t)fminf(fmaxf(rintf(fmaf(zr[r][e], inv[r], MID)), 0.f), (float)LEVELS);
+        code[e] = rtn_code<BITS>(fmaf(zr[r][e], inv[r], MID));
       pack16<BITS>(code, out[r]);
     }
   } else {
@@ -424,7 +440,7 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
       uint32_t code[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        code[i] = (uint32_t)fminf(fmaxf(rintf(fmaf(zc[i][c], iv[i], MID)), 0.f), (float)LEVELS);
+        code[i] = rtn_code<BITS>(fmaf(zc[i][c], iv[i], MID));
       pack16<BITS>(code, out[c]);
     }
   }
