@@ -135,16 +135,19 @@ __device__ __forceinline__ void block_stage(double (&x)[32], bool upper) {
   }
 }
 
-// Rotation X_r = X H_D / sqrt(D) of the tile in `raw` into the LDS tile, then
-// the factor vectors reset.  The sums run in float64, where they are exact
-// (a sum of at most 256 fp16 values needs at most 48 significant bits), and
-// are rounded to fp32 once: in fp32, channels whose rotated value nearly
-// cancels would keep rounding noise of the size of the value itself.
-// Butterflies over the five low channel-index bits run in registers, those
-// over the block bits across neighbouring lanes.  A lane whose block index
-// has an odd number of set bits ends with its values negated by those lane
-// stages (each stage negates the lanes with its bit set, and the negations
-// commute with the later stages), which the final scale undoes.  Ends with a
+// Rotation of the tile in `raw` into the LDS tile, then the factor vectors
+// reset.  The LDS tile holds sigma_j X H_D (channel j): the rotation without
+// its 1/sqrt(D) and with a sign sigma_j = chan_sign(j) per channel, both
+// undone where they matter (see seal_finish; the Sinkhorn factors c_j do not
+// depend on a common scale of the tile or on the signs).  The sums run in
+// float64, where they are exact (a sum of at most 256 fp16 values needs at
+// most 48 significant bits), and are rounded to fp32 once: in fp32, channels
+// whose rotated value nearly cancels would keep rounding noise of the size
+// of the value itself.  Butterflies over the five low channel-index bits run
+// in registers, those over the block bits across neighbouring lanes.  Each
+// lane stage leaves the lanes with its bit set negated, and the negations
+// commute with the later stages, so a lane whose block index has an odd
+// number of set bits ends negated: sigma_j = (-1)^popc(j / 32).  Ends with a
 // barrier.
 template <int D>
 __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& sm, int tid) {
@@ -174,18 +177,19 @@ __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& 
   block_stage<1>(x, bl & 1);
   block_stage<2>(x, bl & 2);
   if constexpr (NB == 8) block_stage<4>(x, bl & 4);
-  const double rs = ((D == 128) ? 0.088388347648318440550 : 0.0625) * ((__popc(bl) & 1) ? -1.0 : 1.0);
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     *reinterpret_cast<float4*>(xg(sm, tl, 8 * bl + k)) =
-        make_float4((float)(x[4 * k] * rs), (float)(x[4 * k + 1] * rs), (float)(x[4 * k + 2] * rs),
-                    (float)(x[4 * k + 3] * rs));
+        make_float4((float)x[4 * k], (float)x[4 * k + 1], (float)x[4 * k + 2], (float)x[4 * k + 3]);
   if (tid < D) {
     sm.u[sk(tid)] = 1.0f / D;
     sm.c2[tid] = 1.0f;
   }
   lds_barrier();
 }
+
+// Sign sigma_j that seal_rotate leaves on channel j of the LDS tile.
+__device__ __forceinline__ bool chan_negated(int j) { return __popc(j >> 5) & 1; }
 
 // Lane roles after the rotation.  Row role: tokens 2tp, 2tp+1 and channels
 // 16cb .. 16cb+15, the RL = D/16 lanes of a token pair adjacent.  Column
@@ -275,6 +279,7 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
       tot += dpp_f<0x4E>(tot);           // quad_perm [2,3,0,1]
       tot += dpp_f<0x104>(tot);          // row_shl:4 (lanes 0, 1 of each eight read 4, 5)
       if constexpr (RL == 16) tot += dpp_f<0x108>(tot);  // row_shl:8
+      asm volatile("" : "+v"(tot));  // the last add stays outside the branch, merged with its DPP move
       if (cb < 2) sm.v[sk(2 * tp + cb)] = fminf(__builtin_amdgcn_rcpf(tot), kBig);
     }
     lds_barrier();
@@ -298,6 +303,7 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
       float tot = qa + dpp_f<0xB1>(qb);
       tot += dpp_f<0x4E>(tot);
       tot += dpp_f<0x104>(tot);
+      asm volatile("" : "+v"(tot));
       if (tb < 2) {
         sm.u[sk(2 * cp + tb)] = fminf(__builtin_amdgcn_rcpf(tot), kBig);
         if (it == iters - 1) sm.c2[2 * cp + tb] = tot > 0.f ? tot * (1.0f / D) : 1.f;
@@ -312,23 +318,43 @@ __device__ __forceinline__ void seal_iterate(int iters, SealSmem<D>& sm, int tid
 // step): adding 2^23 rounds y to an integer, half to even, as rintf does, and
 // leaves that integer in the low mantissa bits; a y a little below 0 (above
 // 2^BITS - 1) rounds to 0 (2^BITS - 1), so no clamp is needed.
+// The bit pattern is 0x4B000000 + code; pack16 removes the constant part.
+constexpr uint32_t kRtnMagicBits = 0x4B000000u;
 template <int BITS>
 __device__ __forceinline__ uint32_t rtn_code(float y) {
-  return __float_as_uint(y + 8388608.0f) & ((1u << BITS) - 1u);
+  return __float_as_uint(y + 8388608.0f);
 }
 
 // Sixteen codes of one record row as a little-endian bit stream: code e
 // occupies bits [BITS e, BITS e + BITS) of the words (the whole-row layout
-// restricted to one 16-code block, which starts on a byte boundary).
+// restricted to one 16-code block, which starts on a byte boundary).  The
+// inputs are rtn_code patterns, kRtnMagicBits + code: the words are built
+// with adds (the code fields do not overlap, so an add is an or for them),
+// and the shifted copies of the constant, the same for every call, are
+// subtracted at the end.
+template <int BITS>
+struct PackBias {
+  uint32_t w[(16 * BITS + 31) / 32];
+  constexpr PackBias() : w{} {
+    for (int e = 0; e < 16; ++e) {
+      const int bit = BITS * e;
+      w[bit / 32] += kRtnMagicBits << (bit % 32);
+      if (bit % 32 + BITS > 32) w[bit / 32 + 1] += kRtnMagicBits >> (32 - bit % 32);
+    }
+  }
+};
+
 template <int BITS>
 __device__ __forceinline__ void pack16(const uint32_t (&code)[16], uint32_t (&w)[(16 * BITS + 31) / 32]) {
+  constexpr PackBias<BITS> bias;
+  constexpr int NW = (16 * BITS + 31) / 32;
 #pragma unroll
-  for (int k = 0; k < (16 * BITS + 31) / 32; ++k) w[k] = 0;
+  for (int k = 0; k < NW; ++k) w[k] = 0u - bias.w[k];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int bit = BITS * e;
-    w[bit / 32] |= code[e] << (bit % 32);
-    if (bit % 32 + BITS > 32) w[bit / 32 + 1] |= code[e] >> (32 - bit % 32);
+    w[bit / 32] += code[e] << (bit % 32);
+    if (bit % 32 + BITS > 32) w[bit / 32 + 1] += code[e] >> (32 - bit % 32);
   }
 }
 
@@ -352,6 +378,10 @@ __device__ __forceinline__ void store16(uint8_t* dst, const uint32_t (&w)[(16 * 
 // source registers may not be reused before it completes, and waiting for a
 // store also waits for every global load issued before it (one in-order
 // counter), which would expose the next tile's prefetch.
+// 1/sqrt(D), the rotation's normalization (float).
+template <int D>
+constexpr float kRotScale = D == 128 ? 0.0883883476483184405f : 0.0625f;
+
 template <int D, int BITS, bool TOKEN_MAJOR>
 __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __restrict__ dbg, SealSmem<D>& sm,
                                             int tid) {
@@ -364,10 +394,13 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
   const int tp = ro.tp, cb = ro.cb, cp = ro.cp, tb = ro.tb;
 
   // ---- channel scales ----------------------------------------------------
+  // cinv carries sigma_j, so X_r / c_j below is (sigma_j X H_D)_tj * cinv_j
+  // up to the common factor sqrt(D), which cancels in the codes and is
+  // applied to the token scales.
   float cj = 0.f;
   if (tid < D) {
     cj = sqrtf(sm.c2[tid]);
-    sm.cinv[sk(tid)] = 1.0f / cj;
+    sm.cinv[sk(tid)] = (chan_negated(tid) ? -1.0f : 1.0f) / cj;
   }
   lds_barrier();
 
@@ -399,7 +432,7 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
       for (int c = 0; c < 16; ++c) mx = fmaxf(mx, fabsf(zr[r][c]));
       mx = max_rl<RL>(mx);
       inv[r] = mx > 0.f ? (float)LEVELS / (2.0f * mx) : 0.f;
-      sc[r] = mx * (2.0f / LEVELS);
+      sc[r] = mx * (2.0f / LEVELS * kRotScale<D>);
     }
     if (cb == 0) *reinterpret_cast<float2*>(sm.inv + sk(2 * tp)) = make_float2(inv[0], inv[1]);
   }
