@@ -96,21 +96,40 @@ __device__ __forceinline__ float max_rl(float v) {
   return RL == 8 ? max8(v) : row16_max(v);
 }
 
-// The 128 x D fp16 tile as thread (token tid / NB, 32-channel block tid % NB)
-// holds it, NB = D / 32: 64 bytes in four 16-byte pieces.
+// Rotation layout.  Thread (token tid / NB, block bl = tid % NB), NB = D / 32,
+// loads channels 32 bl .. 32 bl + 31 of its token; block bit m of bl is paired
+// with register bit q_m = 4 - m (value i of the block sits in register slot
+// i ^ relabel(bl), relabel(bl) = sum over set bits m of 2^q_m), so that the
+// lane stages below can exchange half of the values each.
+template <int D>
+__device__ __forceinline__ int rot_relabel(int bl) {
+  return ((bl & 1) << 4) | ((bl & 2) << 2) | (D == 256 ? (bl & 4) : 0);
+}
+
+// The thread's 64 bytes of the fp16 tile in register-slot order: slots
+// 8k .. 8k+7 in raw[k].
 template <int D>
 __device__ __forceinline__ void load_tile(uint4 (&raw)[4], const __half* __restrict__ src, int tid) {
   constexpr int NB = D / 32;
-  const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)(tid / NB) * D + 32 * (tid % NB));
+  const int bl = tid % NB;
+  const __half* base = src + (size_t)(tid / NB) * D + 32 * bl;
+  const int pk = rot_relabel<D>(bl) >> 3;  // 16-byte piece swap (slot bits 3, 4)
+  if constexpr (NB == 4) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) raw[k] = p[k];
+    for (int k = 0; k < 4; ++k) raw[k] = reinterpret_cast<const uint4*>(base)[k ^ pk];
+  } else {
+    const int hb = (bl >> 2) & 1;  // 8-byte half swap within a piece (slot bit 2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint2* p = reinterpret_cast<const uint2*>(base) + 2 * (k ^ pk);
+      const uint2 lo = p[hb], hi = p[hb ^ 1];
+      raw[k] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
 }
 
-// One Hadamard stage across the lanes whose block indices differ in bit M of
-// a 4-lane quad (M = 1, 2) or of an 8-lane group (M = 4): the lane with the
-// bit clear keeps x + x', the other x - x' negated, i.e. computed as x + s x'
-// with s = -1; the negations are undone by the caller.  Values are float64
-// (two 32-bit halves move through DPP).
+// The value of the lane whose block index differs in bit M (M = 1, 2 within
+// a quad, M = 4 within an eight-lane group), one 32-bit half through DPP.
 template <int M>
 __device__ __forceinline__ int dpp_pair(int v) {
   if constexpr (M == 1) {
@@ -124,31 +143,46 @@ __device__ __forceinline__ int dpp_pair(int v) {
     return __builtin_amdgcn_update_dpp(o, v, 0x114, 0xF, 0xA, false);
   }
 }
-template <int M>
-__device__ __forceinline__ void block_stage(double (&x)[32], bool upper) {
-  const double s = upper ? -1.0 : 1.0;
+
+// Hadamard stage over block bit M (lane partner bl ^ M) paired with register
+// bit Q.  The pair (lower lane, upper lane) holds, at each slot i with bit Q
+// clear, a = lower's value and c = upper's value of the same channel offset
+// (the upper lane's slots are relabeled, so slot i | Q of each lane holds
+// what its partner needs): one exchange of slot i | Q gives each lane the
+// other's value, and each lane then keeps both outputs a + c (slot i) and
+// a - c (slot i | Q) for its half of the offsets.  Afterwards block bit M
+// stands for channel bit log2 Q and register bit Q for the block bit; the
+// upper lane's a - c comes out negated.
+template <int M, int Q>
+__device__ __forceinline__ void lane_stage(double (&x)[32]) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int lo = dpp_pair<M>(__double2loint(x[i]));
-    const int hi = dpp_pair<M>(__double2hiint(x[i]));
-    x[i] = fma(s, __hiloint2double(hi, lo), x[i]);
+  for (int r = 0; r < 32; ++r) {
+    if (r & Q) {
+      const int lo = dpp_pair<M>(__double2loint(x[r]));
+      const int hi = dpp_pair<M>(__double2hiint(x[r]));
+      const double recv = __hiloint2double(hi, lo), own = x[r ^ Q];
+      x[r ^ Q] = own + recv;
+      x[r] = own - recv;
+    }
   }
 }
 
 // Rotation of the tile in `raw` into the LDS tile, then the factor vectors
-// reset.  The LDS tile holds sigma_j X H_D (channel j): the rotation without
-// its 1/sqrt(D) and with a sign sigma_j = chan_sign(j) per channel, both
-// undone where they matter (see seal_finish; the Sinkhorn factors c_j do not
-// depend on a common scale of the tile or on the signs).  The sums run in
-// float64, where they are exact (a sum of at most 256 fp16 values needs at
-// most 48 significant bits), and are rounded to fp32 once: in fp32, channels
-// whose rotated value nearly cancels would keep rounding noise of the size
-// of the value itself.  Butterflies over the five low channel-index bits run
-// in registers, those over the block bits across neighbouring lanes.  Each
-// lane stage leaves the lanes with its bit set negated, and the negations
-// commute with the later stages, so a lane whose block index has an odd
-// number of set bits ends negated: sigma_j = (-1)^popc(j / 32).  Ends with a
-// barrier.
+// reset.  The LDS tile holds sigma_j (X H_D)_tj: the rotation without its
+// 1/sqrt(D) and with a sign sigma_j = chan_negated(j) ? -1 : 1 per channel,
+// both undone where they matter (see seal_finish; the Sinkhorn factors c_j
+// do not depend on a common scale of the tile or on the signs).  The sums
+// run in float64, where they are exact (a sum of at most 256 fp16 values
+// needs at most 48 significant bits), and are rounded to fp32 once: in fp32,
+// channels whose rotated value nearly cancels would keep rounding noise of
+// the size of the value itself.
+//
+// Butterflies over the five in-register bits run first; over a relabeled
+// slot bit the upper lane's pair is stored swapped, which a lane sign s
+// absorbs (new low = s a + b, new high = a - s b).  Then one lane_stage per
+// block bit.  Channel of slot r in lane bl afterwards (D 128):
+// r[0..2] | bl1 << 3 | bl0 << 4 | r4 << 5 | r3 << 6; at D 256 slot bits 0, 1,
+// bl2, bl1, bl0, r4, r3, r2.  Ends with a barrier.
 template <int D>
 __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& sm, int tid) {
   constexpr int NB = D / 32;
@@ -163,24 +197,37 @@ __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& 
       x[8 * k + 2 * e + 1] = (double)h2f((uint16_t)(ws[e] >> 16));
     }
   }
+  const int rl = rot_relabel<D>(bl);
 #pragma unroll
   for (int st = 1; st < 32; st <<= 1) {
+    const double s = (rl & st) ? -1.0 : 1.0;
+    const bool relabeled = st == 16 || st == 8 || (NB == 8 && st == 4);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (!(i & st)) {
-        const double a0 = x[i], a1 = x[i + st];
-        x[i] = a0 + a1;
-        x[i + st] = a0 - a1;
+        const double a = x[i], b = x[i + st];
+        if (relabeled) {
+          x[i] = fma(s, a, b);
+          x[i + st] = fma(-s, b, a);
+        } else {
+          x[i] = a + b;
+          x[i + st] = a - b;
+        }
       }
     }
   }
-  block_stage<1>(x, bl & 1);
-  block_stage<2>(x, bl & 2);
-  if constexpr (NB == 8) block_stage<4>(x, bl & 4);
+  lane_stage<1, 16>(x);
+  lane_stage<2, 8>(x);
+  if constexpr (NB == 8) lane_stage<4, 4>(x);
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    *reinterpret_cast<float4*>(xg(sm, tl, 8 * bl + k)) =
-        make_float4((float)x[4 * k], (float)x[4 * k + 1], (float)x[4 * k + 2], (float)x[4 * k + 3]);
+  for (int p = 0; p < 8; ++p) {
+    const int r2 = p & 1, r3 = (p >> 1) & 1, r4 = p >> 2;
+    const int g = NB == 4 ? (r2 | ((bl >> 1) << 1) | ((bl & 1) << 2) | (r4 << 3) | (r3 << 4))
+                          : (((bl >> 2) & 1) | (((bl >> 1) & 1) << 1) | ((bl & 1) << 2) | (r4 << 3) | (r3 << 4) |
+                             (r2 << 5));
+    *reinterpret_cast<float4*>(xg(sm, tl, g)) =
+        make_float4((float)x[4 * p], (float)x[4 * p + 1], (float)x[4 * p + 2], (float)x[4 * p + 3]);
+  }
   if (tid < D) {
     sm.u[sk(tid)] = 1.0f / D;
     sm.c2[tid] = 1.0f;
@@ -188,8 +235,16 @@ __device__ __forceinline__ void seal_rotate(const uint4 (&raw)[4], SealSmem<D>& 
   lds_barrier();
 }
 
-// Sign sigma_j that seal_rotate leaves on channel j of the LDS tile.
-__device__ __forceinline__ bool chan_negated(int j) { return __popc(j >> 5) & 1; }
+// Sign that seal_rotate leaves on channel j of the LDS tile: each lane stage
+// negates the channels whose block bit and paired channel bit are both set
+// (channel bits 4 and 5, 3 and 6, and at D 256 2 and 7).
+template <int D>
+__device__ __forceinline__ bool chan_negated(int j) {
+  const int m = (j >> 4) & (j >> 5) & 1;
+  const int n = (j >> 3) & (j >> 6) & 1;
+  const int o = D == 256 ? (j >> 2) & (j >> 7) & 1 : 0;
+  return (m ^ n ^ o) != 0;
+}
 
 // Lane roles after the rotation.  Row role: tokens 2tp, 2tp+1 and channels
 // 16cb .. 16cb+15, the RL = D/16 lanes of a token pair adjacent.  Column
@@ -400,7 +455,7 @@ __device__ __forceinline__ void seal_finish(uint8_t* __restrict__ rec, float* __
   float cj = 0.f;
   if (tid < D) {
     cj = sqrtf(sm.c2[tid]);
-    sm.cinv[sk(tid)] = (chan_negated(tid) ? -1.0f : 1.0f) / cj;
+    sm.cinv[sk(tid)] = (chan_negated<D>(tid) ? -1.0f : 1.0f) / cj;
   }
   lds_barrier();
 
