@@ -469,8 +469,9 @@ def measure_workload(torch, K, probe, synth, dev, name, steps, hbm_target_bytes=
         c = caches[s % ncopy]
         t = s // ncopy
         if decoding:
-            c.append_seal(new_k[t], new_v[t])
-        c.decode_attn(q_all[t], out=outs[s % ncopy])
+            c.decode_step(new_k[t], new_v[t], q_all[t], lengths=[n + t for n in lens0], out=outs[s % ncopy])
+        else:
+            c.decode_attn(q_all[t], out=outs[s % ncopy])
 
     st_step = timed_graph(step, tokens * ncopy, 20)
     st_split = timed_graph(lambda r: caches[r % ncopy].decode_partial(q_all[0]), 8 * ncopy, 50)
@@ -785,10 +786,12 @@ def main():
             c.seq_len.copy_(s0)
 
     def step(s):
+        # kvarn_decode_step with the lengths the host keeps: the append rides
+        # in the decode launches unless the token completes a group.
         c = s % ncopy
         tok = s // ncopy
-        caches[c].append_seal(new_k[c, tok], new_v[c, tok])
-        caches[c].decode_attn(q_all[tok], out=outs[c])
+        caches[c].decode_step(new_k[c, tok], new_v[c, tok], q_all[tok], lengths=[n + tok for n in lens_c[c]],
+                              out=outs[c])
 
     if args.profile_steps > 0:
         for s in range(args.profile_steps):
@@ -979,9 +982,18 @@ def main():
                    "context": lens0[0], "k_bits": wl.k_bits, "v_bits": wl.v_bits, "layer_caches": ncopy,
                    "tail_phase": f"layer c starts 127 - floor(128 c / {ncopy}) tokens into its tail",
                    "max_groups": max_groups, "seals_in_timed_steps": seals_timed,
-                   "step": "append + seal-if-due + decode attention (one layer)"},
+                   "step": "kvarn_decode_step: append + seal-if-due + decode attention (one layer); the "
+                           "append rides in the decode launches unless the token completes a group"},
         "step_us_stats": us(_stats(t_step_reps)),
         "step_without_append_us_stats": us(st_noappend),
+        "seal_cadence": {
+            "us_step_no_seal": float(np.median(t_step_reps)) * 1e6,
+            "us_step_with_seal": seal_event["us_seal_event"] + us(st_noappend)["median"],
+            "us_per_step_one_seal_per_128": (127 * float(np.median(t_step_reps)) * 1e6
+                                             + seal_event["us_seal_event"] + us(st_noappend)["median"]) / 128,
+            "note": "a step that completes a group is the append+seal launch (seal_event) followed by the decode "
+                    "launches (step_without_append); every request seals once per 128 steps",
+        },
         "decode_plan": plan,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,

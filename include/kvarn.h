@@ -245,6 +245,28 @@ kvarn_status kvarn_decode_attn(const kvarn_config *cfg, const kvarn_cache *cache
                                void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * One decode step: kvarn_append_seal of (k_new, v_new) followed by
+ * kvarn_decode_attn of q, with the same results and the same cache state
+ * afterwards [P2 §2.1: a group is sealed when its last token arrives, before
+ * anything attends over it; P2 §1: attention over the sealed groups and the
+ * exact sink and tail].  k_new, v_new: device fp16 [batch][Hkv][D]; q, out,
+ * softmax_scale, workspace, ws_bytes: as for kvarn_decode_attn.  len_host:
+ * host int32 [batch] holding every request's seq_len before this step (the
+ * caller's own count), or NULL.  When len_host shows that no request's token
+ * completes a group and no request is at capacity, the append rides in the
+ * decode launches (the split kernel reads the new token from k_new and
+ * stores it in its sink or tail slot, the combine kernel advances seq_len):
+ * two launches instead of three.  Otherwise (or with NULL) the step is the
+ * three launches.  len_host values that differ from the cache's seq_len give
+ * undefined results; a negative value returns KVARN_EINVAL before anything
+ * is queued.
+ */
+kvarn_status kvarn_decode_step(const kvarn_config *cfg, const kvarn_cache *cache,
+                               const void *k_new, const void *v_new, const void *q, float *out,
+                               float softmax_scale, const int32_t *len_host,
+                               void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * kvarn_decode_attn without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  Same

@@ -624,15 +624,23 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
   }
   __builtin_amdgcn_sched_barrier(0);
   uint4 kr[kExactRounds][QD / 8], vr[kExactRounds][QD / 8];
-  bool valid[kExactRounds];
+  bool valid[kExactRounds], dst_tail[kExactRounds];
+  int64_t dst[kExactRounds];  // element offset of the appended token's quarter row, or -1
 #pragma unroll
   for (int round = 0; round < kExactRounds; ++round) {
     const int e = kExactPerSplit * es + kExactTok * (kExactRounds * w + round) + tl;
     valid[round] = e < n_exact;
     const bool in_tail = valid[round] && e >= n_sink;
     const int64_t row = bh * kGroup + (valid[round] ? (in_tail ? e - n_sink : e) : 0);
-    const uint4* kp = reinterpret_cast<const uint4*>((in_tail ? a.c.tail_k : a.c.sink_k) + row * D + quarter * QD);
-    const uint4* vp = reinterpret_cast<const uint4*>((in_tail ? a.c.tail_v : a.c.sink_v) + row * D + quarter * QD);
+    // With the append folded in, the newest position (the last exact token)
+    // comes from the step's input; its slot is written below.
+    const bool fresh = a.k_new && valid[round] && e == n_exact - 1;
+    const __half* ks = fresh ? a.k_new + bh * D : (in_tail ? a.c.tail_k : a.c.sink_k) + row * D;
+    const __half* vs = fresh ? a.v_new + bh * D : (in_tail ? a.c.tail_v : a.c.sink_v) + row * D;
+    dst[round] = fresh ? row * D + quarter * QD : -1;
+    dst_tail[round] = in_tail;
+    const uint4* kp = reinterpret_cast<const uint4*>(ks + quarter * QD);
+    const uint4* vp = reinterpret_cast<const uint4*>(vs + quarter * QD);
 #pragma unroll
     for (int c = 0; c < QD / 8; ++c) {
       kr[round][c] = kp[c];
@@ -648,6 +656,20 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
   __syncthreads();
   const int tslot = (int)blockIdx.x * kWaves + w;  // trace build only
   trace_mark(tslot, 1);  // query staged
+  if (a.k_new) {
+#pragma unroll
+    for (int round = 0; round < kExactRounds; ++round) {
+      if (dst[round] >= 0) {
+        uint4* kd = reinterpret_cast<uint4*>((dst_tail[round] ? a.c.tail_k : a.c.sink_k) + dst[round]);
+        uint4* vd = reinterpret_cast<uint4*>((dst_tail[round] ? a.c.tail_v : a.c.sink_v) + dst[round]);
+#pragma unroll
+        for (int c = 0; c < QD / 8; ++c) {
+          kd[c] = kr[round][c];
+          vd[c] = vr[round][c];
+        }
+      }
+    }
+  }
 
   float m_run[GQ], l_run[GQ], o[GQ][CPLX];
 #pragma unroll
@@ -782,18 +804,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int nex = a.nsplit - a.n_rec_splits;
   const int npair = a.c.batch * a.c.hkv;
   const int bx = blockIdx.x;
+  const int fold = a.k_new ? 1 : 0;  // the step's own token counts (append folded in)
   if (bx < nex * npair) {
     const int pair = bx / nex, es = bx - pair * nex;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
     if (nex == 4)
-      exact_split<D, GQ, 1>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b]);
+      exact_split<D, GQ, 1>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b] + fold);
     else
-      exact_split<D, GQ, 2>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b]);
+      exact_split<D, GQ, 2>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b] + fold);
   } else {
     const int r = bx - nex * npair;
     const int pair = r / a.n_rec_splits, split = r - pair * a.n_rec_splits;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
-    record_split<D, KB, VB, GQ, PAGED>(sm.rec, a, b, kvh, split, a.c.seq_len[b]);
+    record_split<D, KB, VB, GQ, PAGED>(sm.rec, a, b, kvh, split, a.c.seq_len[b] + fold);
   }
 }
 
@@ -813,6 +836,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int ns = a.nsplit, nrec = a.n_rec_splits;
+  // Append folded into the step: the split kernel has attended over the new
+  // token and stored it; the length moves on here, once per request (no
+  // kernel of this launch reads it).
+  if (a.k_new && hq == 0 && tid == 0) a.c.seq_len[b] = a.c.seq_len[b] + 1;
   const int64_t base = ((int64_t)b * a.hq + hq) * ns;
   const float* ml = a.ws_ml + 2 * base;
   const float* ob = a.ws_o + base * D + P * l;

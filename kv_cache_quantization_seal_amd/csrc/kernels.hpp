@@ -155,6 +155,13 @@ struct DecodeArgs {
   int n_rec_splits;
   int groups_per_split;
   int groups_per_wave;
+  // Append folded into the step (both NULL: the cache already holds the
+  // step's token): fp16 [B][Hkv][D], the token at position seq_len[b].  The
+  // exact split that covers that position reads it from here and writes it
+  // to its sink or tail slot; the combine kernel then sets seq_len[b] + 1.
+  // Only for steps where no request completes a group or is at capacity.
+  const __half* k_new;
+  const __half* v_new;
 };
 
 struct PrefillAttnArgs {

@@ -348,7 +348,7 @@ kvarn_status kvarn_prefill(const kvarn_config* cfg, const kvarn_cache* cache, co
 
 static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,
                                   float softmax_scale, void* workspace, size_t ws_bytes, int phases, void* stream,
-                                  const char* what) {
+                                  const char* what, const void* k_new = nullptr, const void* v_new = nullptr) {
   kvarn_status s = check_cfg(cfg);
   if (s != KVARN_OK) return s;
   if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
@@ -378,6 +378,8 @@ static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* ca
   a.n_rec_splits = p.n_rec_splits;
   a.groups_per_split = p.groups_per_split;
   a.groups_per_wave = p.groups_per_wave;
+  a.k_new = (const __half*)k_new;
+  a.v_new = (const __half*)v_new;
   return hip_status(kvarn::launch_decode(cfg->head_dim, cfg->k_bits, cfg->v_bits,
                                          cfg->num_q_heads / cfg->num_kv_heads, a, phases, (hipStream_t)stream),
                     what);
@@ -435,6 +437,36 @@ kvarn_status kvarn_decode_attn_noalloc(const kvarn_config* cfg, const kvarn_cach
 kvarn_status kvarn_decode_attn(const kvarn_config* cfg, const kvarn_cache* cache, const void* q, float* out,
                                float softmax_scale, void* workspace, size_t ws_bytes, void* stream) {
   return decode_common(cfg, cache, q, out, softmax_scale, workspace, ws_bytes, 3, stream, "kvarn_decode_attn launch");
+}
+
+kvarn_status kvarn_decode_step(const kvarn_config* cfg, const kvarn_cache* cache, const void* k_new,
+                               const void* v_new, const void* q, float* out, float softmax_scale,
+                               const int32_t* len_host, void* workspace, size_t ws_bytes, void* stream) {
+  kvarn_status s = check_cfg(cfg);
+  if (s != KVARN_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVARN_OK) return s;
+  if (!k_new || !v_new) return fail(KVARN_EINVAL, "k_new and v_new must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVARN_EINVAL, "k_new and v_new must be 16-byte aligned");
+  // The append rides in the decode launches only if no request's token
+  // completes a group (that group's seal must come before the attention)
+  // and no request is at capacity (its append is skipped).
+  bool fold = len_host != nullptr;
+  if (fold) {
+    const int64_t cap = (int64_t)KVARN_SINK + (int64_t)KVARN_GROUP * cache->max_groups + KVARN_GROUP - 1;
+    for (int32_t b = 0; b < cache->batch; ++b) {
+      const int64_t n = len_host[b];
+      if (n < 0) return fail(KVARN_EINVAL, "len_host[%d] = %lld is negative", b, (long long)n);
+      const int64_t n1 = n + 1;
+      if (n >= cap || (n1 >= KVARN_SINK + KVARN_GROUP && (n1 - KVARN_SINK) % KVARN_GROUP == 0)) fold = false;
+    }
+  }
+  if (!fold) {
+    if ((s = kvarn_append_seal(cfg, cache, k_new, v_new, stream)) != KVARN_OK) return s;
+    return decode_common(cfg, cache, q, out, softmax_scale, workspace, ws_bytes, 3, stream,
+                         "kvarn_decode_step launch");
+  }
+  return decode_common(cfg, cache, q, out, softmax_scale, workspace, ws_bytes, 3, stream,
+                       "kvarn_decode_step launch", k_new, v_new);
 }
 
 kvarn_status kvarn_decode_attn_partial(const kvarn_config* cfg, const kvarn_cache* cache, const void* q,

@@ -27,7 +27,8 @@ EXPORTS = (
     "kvarn_decode_plan",
     "kvarn_last_error", "kvarn_status_string", "kvarn_append", "kvarn_append_seal", "kvarn_seal_group",
     "kvarn_prefill", "kvarn_prefill_layers",
-    "kvarn_decode_attn", "kvarn_decode_attn_noalloc", "kvarn_decode_attn_partial", "kvarn_decode_attn_combine", "kvarn_seal_tiles",
+    "kvarn_decode_attn", "kvarn_decode_attn_noalloc", "kvarn_decode_step", "kvarn_decode_attn_partial",
+    "kvarn_decode_attn_combine", "kvarn_seal_tiles",
     "kvarn_dequant_records", "kvarn_prefill_attn",
 )
 
@@ -79,6 +80,7 @@ def lib():
         L.kvarn_prefill_layers.argtypes = [cp(Config), cp(CacheView), i32, cp(vp), cp(vp), i64, cp(i32), vp]
         L.kvarn_decode_attn.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp, sz, vp]
         L.kvarn_decode_attn_noalloc.argtypes = [cp(Config), cp(CacheView), vp, vp, f32, vp]
+        L.kvarn_decode_step.argtypes = [cp(Config), cp(CacheView), vp, vp, vp, vp, f32, cp(i32), vp, sz, vp]
         L.kvarn_decode_attn_partial.argtypes = [cp(Config), cp(CacheView), vp, f32, vp, sz, vp]
         L.kvarn_decode_attn_combine.argtypes = [cp(Config), cp(CacheView), vp, vp, sz, vp]
         L.kvarn_seal_tiles.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp, i32, vp]
@@ -232,6 +234,23 @@ class KVarNCache:
         _check(lib().kvarn_decode_attn(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(q), _ptr(out),
                                        float(scale), _ptr(self.workspace), self.workspace.numel(),
                                        _stream(stream)))
+        return out
+
+    def decode_step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                    lengths: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, stream=None) -> torch.Tensor:
+        """append_seal(k_new, v_new) then decode_attn(q) through
+        kvarn_decode_step; ``lengths`` (each request's length before the
+        step, as the caller counts it) lets the library fold the append into
+        the decode launches when no group completes."""
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if scale is None:
+            scale = self.cfg.head_dim ** -0.5
+        lens = None if lengths is None else (ctypes.c_int32 * self.batch)(*[int(x) for x in lengths])
+        _check(lib().kvarn_decode_step(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k_new), _ptr(v_new),
+                                       _ptr(q), _ptr(out), float(scale), lens, _ptr(self.workspace),
+                                       self.workspace.numel(), _stream(stream)))
         return out
 
     def decode_attn_noalloc(self, q: torch.Tensor, out: torch.Tensor, scale: Optional[float] = None,

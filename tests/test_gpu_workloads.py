@@ -2,7 +2,10 @@
 the launch configuration the benchmark times: the cache capacity is the
 workload's own (``Workload.max_groups``, which bench.py also uses, so both
 launch the same decode plan, printed here) and every decode step of the
-workload runs as one fused append-and-seal launch.
+workload runs as the benchmark's step, kvarn_decode_step with the host's
+lengths: the append folded into the decode launches, or on the steps that
+complete a group the append-and-seal launch first.  Each step's output must
+equal, bit for bit, a plain decode of the cache the step left behind.
 
 The whole cache is built on the GPU (bulk prefill seal of every pair); the
 oracle then checks sampled (request, KV head) pairs end to end from the same
@@ -54,14 +57,16 @@ def test_full_size_sampled(name):
     print(f"{name}: decode plan {K.decode_plan(cfg, B, max_groups)}")
     cache = K.KVarNCache(cfg, B, max_groups, device=dev)
     cache.prefill(Kd, Vd, lens0)
+    q = np.stack([synth.queries(wl, b, 1)[0] for b in range(B)])
+    qd = torch.from_numpy(q).to(dev)
     for s in range(steps):
         idx = torch.tensor([n + s for n in lens0], device=dev)
         knew = Kd[torch.arange(B, device=dev), :, idx].contiguous()   # [B][Hkv][D]
         vnew = Vd[torch.arange(B, device=dev), :, idx].contiguous()
-        cache.append_seal(knew, vnew)   # the step's launch as the benchmark times it
+        # the step as the benchmark times it
+        out_s = cache.decode_step(knew, vnew, qd, lengths=[n + s for n in lens0])
+        assert torch.equal(out_s, cache.decode_attn(qd)), f"step {s}"
     lens = [n + steps for n in lens0]
-    q = np.stack([synth.queries(wl, b, 1)[0] for b in range(B)])
-    qd = torch.from_numpy(q).to(dev)
     out = cache.decode_attn(qd).cpu().numpy()
     # Decoding is a pure function of the cache: a second call gives the same
     # bits (no state is carried from one launch to the next).
