@@ -101,7 +101,8 @@ def decode_source_sha():
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.hpp", "kernels.hpp"):
+    for f in ("decode.hip", "decode_impl.hpp", "decode_k2.hip", "decode_k3.hip", "decode_k4.hip", "decode_k5.hip",
+              "decode_k6.hip", "decode_k8.hip", "common.hpp", "kernels.hpp"):
         with open(os.path.join(here, "kv_cache_quantization_seal_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
