@@ -320,10 +320,11 @@ def _blas_threads():
 
 
 def _oracle_unit(task):
-    """One independent (request, KV head) unit of the oracle: seal `n_seal`
-    groups of its stream, then (state built untimed) one decode step of its
-    query heads.  Returns (seal seconds, decode seconds)."""
-    name, b, h, n_seal = task
+    """One independent unit of the oracle: part `part` of `parts` of a
+    (request, KV head): seal groups [g0, g0 + n_seal) of its stream, then
+    (state built untimed) one decode step of its share of the query heads.
+    Returns (seal seconds, decode seconds)."""
+    name, b, h, n_seal, part, parts = task
     from kv_cache_quantization_seal_amd import synth
     from oracle import kvarn_oracle as O
     wl = synth.WORKLOADS[name]
@@ -331,7 +332,7 @@ def _oracle_unit(task):
     k, v = synth.kv_stream(wl, b, h, n0)
     q = synth.queries(wl, b, 1)[0]
     t0 = time.perf_counter()
-    for g in range(n_seal):
+    for g in range(part * n_seal, (part + 1) * n_seal):
         lo = 128 + 128 * g
         O.encode_record(**_enc(O.seal_tile(k[lo:lo + 128], wl.k_bits), wl.k_bits, "k"))
         O.encode_record(**_enc(O.seal_tile(v[lo:lo + 128], wl.v_bits), wl.v_bits, "v"))
@@ -339,7 +340,7 @@ def _oracle_unit(task):
     st = O.state_from_stream(k, v, wl.k_bits, wl.v_bits)
     gq = wl.num_q_heads // wl.num_kv_heads
     t1 = time.perf_counter()
-    for hh in range(gq):
+    for hh in range(gq * part // parts, gq * (part + 1) // parts):
         st.attend(q[h * gq + hh])
     return t_seal, time.perf_counter() - t1
 
@@ -351,28 +352,34 @@ def cpu_baseline(wl, n_seal_groups):
 
     * One process (NumPy with its BLAS threads): unit 0 alone, its decode step
       scaled by the number of KV heads, ``n_seal_groups`` seal groups.
-    * A pool of P = min(16, affinity, KV heads) worker processes with one BLAS
-      thread each, every unit at once: the decode step takes the slowest
-      unit's time; seal throughput is all units' groups over the slowest
-      unit's seal time.
+    * A pool of P worker processes with one BLAS thread each, P = the CPU
+      affinity (at most 16, the host share of one GPU): each KV head is split
+      into S = P // KV heads parts (at most its query heads), a part sealing
+      its share of the groups and attending its share of the query heads;
+      every unit at once.  The decode step takes the slowest unit's time;
+      seal throughput is all units' groups over the slowest unit's seal time.
 
     Runs before the GPU is initialized (the pool's workers are spawned).
     """
     import multiprocessing as mp
     t_start = time.perf_counter()
     blas = _blas_threads()
-    t_seal1, t_dec1 = _oracle_unit((wl.name, 0, 0, n_seal_groups))
+    t_seal1, t_dec1 = _oracle_unit((wl.name, 0, 0, n_seal_groups, 0, 1))
     single = {"value": wl.batch / (t_dec1 * wl.num_kv_heads), "seal_groups_per_s": n_seal_groups / t_seal1,
               "threads": int(blas)}
-    units = wl.num_kv_heads
-    P = max(1, min(16, len(os.sched_getaffinity(0)), units))
+    gq = wl.num_q_heads // wl.num_kv_heads
+    aff = max(1, min(16, len(os.sched_getaffinity(0))))
+    parts = max(1, min(gq, aff // wl.num_kv_heads))
+    units = wl.num_kv_heads * parts
+    P = max(1, min(aff, units))
     per_unit = max(1, n_seal_groups // units)
     env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in env:
         os.environ[k] = "1"
     try:
         with mp.get_context("spawn").Pool(P) as pool:
-            res = pool.map(_oracle_unit, [(wl.name, 0, h, per_unit) for h in range(units)])
+            res = pool.map(_oracle_unit, [(wl.name, 0, h, per_unit, p, parts)
+                                          for h in range(wl.num_kv_heads) for p in range(parts)])
     finally:
         for k, val in env.items():
             if val is None:
@@ -381,14 +388,13 @@ def cpu_baseline(wl, n_seal_groups):
                 os.environ[k] = val
     t_seal_p = max(r[0] for r in res)
     t_dec_p = max(r[1] for r in res)
-    gq = wl.num_q_heads // wl.num_kv_heads
     n0 = wl.start_len(0)
     return {
         "value": wl.batch / t_dec_p, "unit": "tokens/s", "cores": int(P), "kind": "oracle",
         "seal_groups_per_s": units * per_unit / t_seal_p,
-        "sample": (f"one decode step of request 0 over {n0} tokens ({units} KV heads x {gq} query heads) and "
-                   f"{units * per_unit} seal groups (K+V tiles), as {units} KV-head units on {P} worker "
-                   f"processes with one BLAS thread each; float64 NumPy oracle"),
+        "sample": (f"one decode step of request 0 over {n0} tokens ({wl.num_kv_heads} KV heads x {gq} query "
+                   f"heads) and {units * per_unit} seal groups (K+V tiles), as {units} units ({parts} per KV "
+                   f"head) on {P} worker processes with one BLAS thread each; float64 NumPy oracle"),
         "single_process": dict(single, sample=(f"KV head 0 only ({gq} query heads, step scaled x{units}), "
                                                f"{n_seal_groups} seal groups")),
         "cpu_model": _cpu_model(),
