@@ -278,7 +278,13 @@ def prefill_trace(args, wl, caches, e0, e1, flush_buf, sink):
     q = torch.from_numpy(np.random.default_rng(7).standard_normal(
         (wl.batch, chunk, wl.num_q_heads, wl.head_dim)).astype(np.float16)).to(dev)
     gq = wl.num_q_heads // wl.num_kv_heads
-    n_waves = -(-chunk * gq // 64) * wl.num_kv_heads * wl.batch * 4
+    # Workgroups of 8 waves (128 query rows) at D 128 when that grid has one
+    # per CU, else of 4 waves (64 rows): the launch's own rule.
+    wgs8 = -(-chunk * gq // 128) * wl.num_kv_heads * wl.batch
+    if wl.head_dim == 128 and wgs8 >= torch.cuda.get_device_properties(0).multi_processor_count:
+        n_waves = wgs8 * 8
+    else:
+        n_waves = -(-chunk * gq // 64) * wl.num_kv_heads * wl.batch * 4
     reps = []
     for c in caches[:3]:
         probe.read(flush_buf, sink)

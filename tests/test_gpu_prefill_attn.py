@@ -78,13 +78,13 @@ def test_prefill_attn_last_row_equals_decode():
 
 
 def test_prefill_attn_full_size_sampled():
-    """Llama-3.1-8B shape (32 q / 8 KV heads, D 128, 2-bit): a 512-token chunk
-    at the end of a 32k context, built on the GPU by the bulk seal; sampled
-    rows of two KV heads checked against the oracle (its own seal of the
-    sampled heads' streams)."""
+    """Llama-3.1-8B shape (32 q / 8 KV heads, D 128, 2-bit): the benchmark's
+    2,048-token chunk at the end of a 32k context (eight-wave workgroups),
+    built on the GPU by the bulk seal; sampled rows of two KV heads checked
+    against the oracle (its own seal of the sampled heads' streams)."""
     wl = synth.WORKLOADS["llama31_8b_32k"]
     dev = torch.device("cuda:0")
-    n, chunk = wl.context, 512
+    n, chunk = wl.context, 2048
     pairs = [(0, 0), (0, 5)]
     Kd, Vd = synth.kv_streams_device(wl, n, dev, pairs_from_host=pairs)
     cfg = K.make_config(wl.head_dim, wl.num_q_heads, wl.num_kv_heads, wl.k_bits, wl.v_bits)
@@ -98,12 +98,12 @@ def test_prefill_attn_full_size_sampled():
         k, v = synth.kv_stream(wl, b, h, n)
         st = O.state_from_stream(k, v, wl.k_bits, wl.v_bits)
         kall, vall = st.materialize()
-        for i in (0, 1, 255, 256, 383, 511):
+        for i in (0, 1, 255, 256, 1023, 1024, 2046, 2047):
             p = n - chunk + i
             for hh in range(gq):
                 ref = O.attention(q[0, i, h * gq + hh], kall[:p + 1], vall[:p + 1])
                 worst = max(worst, float(np.abs(out[0, i, h * gq + hh] - ref).max()))
-    print(f"llama 32k chunk 512: sampled max abs err {worst:.3e}")
+    print(f"llama 32k chunk 2048: sampled max abs err {worst:.3e}")
     assert worst <= ATTN_ATOL
 
 
@@ -153,4 +153,40 @@ def test_prefill_attn_paged_with_absent_group():
                 ref = O.attention(q[b, i, h], kall[sel], vall[sel])
                 worst = max(worst, float(np.abs(out[b, i, h] - ref).max()))
     print(f"paged, absent group: max abs err {worst:.3e}")
+    assert worst <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("kb,vb,lens", [
+    (2, 4, [2100, 1900]),   # two requests, tails of 52 and 108 tokens
+    (6, 5, [2200, 700]),    # wide codes; the second request's chunk starts before its cache
+])
+def test_prefill_attn_eight_wave_grid(kb, vb, lens):
+    """A grid large enough for eight-wave workgroups (at least one per CU):
+    8 KV heads x GQ 4, a 2,048-token chunk; every 41st row of every head
+    against the oracle, and rows before a request's first position left
+    untouched."""
+    d, hq, hkv, chunk = 128, 32, 8, 2048
+    states = _states(d, hkv, kb, vb, lens, 900 + kb + vb)
+    cfg = K.make_config(d, hq, hkv, kb, vb)
+    mg = max((n - 128) // 128 for n in lens) + 1
+    cache = K.KVarNCache(cfg, len(lens), mg)
+    upload_states(cache, states)
+    q = np.random.default_rng(kb * 10 + vb).standard_normal((len(lens), chunk, hq, d)).astype(np.float16)
+    sentinel = 12345.0
+    out = torch.full(q.shape, sentinel, dtype=torch.float32, device="cuda")
+    cache.prefill_attn(torch.from_numpy(q).cuda(), out=out)
+    got = out.cpu().numpy()
+    gq = hq // hkv
+    worst = 0.0
+    for b, n in enumerate(lens):
+        c = min(chunk, n)
+        assert np.all(got[b, :chunk - c] == sentinel)
+        mats = [st.materialize() for st in states[b]]
+        for i in range(chunk - c, chunk, 41):
+            p = n - chunk + i
+            for h in range(hq):
+                kall, vall = mats[h // gq]
+                ref = O.attention(q[b, i, h], kall[:p + 1], vall[:p + 1])
+                worst = max(worst, float(np.abs(got[b, i, h] - ref).max()))
+    print(f"eight-wave grid k{kb} v{vb} lens={lens}: sampled max abs err {worst:.3e}")
     assert worst <= ATTN_ATOL
