@@ -96,3 +96,46 @@ def test_decode_step_rejects_negative_length():
         c.decode_step(z, z, q, lengths=[0, -1])
     torch.cuda.synchronize()
     assert c.seq_len.cpu().tolist() == [0, 0]
+
+
+def test_decode_step_graph_replays():
+    """Steps captured in a HIP graph (as the benchmark runs them), replayed
+    three times with the lengths reset and eager work in between: every
+    replay gives the eager steps' outputs and cache bit for bit (the folded
+    append writes the cache from inside the split kernel; nothing in the
+    step is a memset node)."""
+    cfg = K.make_config(128, 8, 2, 2, 2)
+    lens = [250, 383]   # the sixth step completes a group of request 0 (three launches)
+    eager, graphed = _pair(cfg, 2, 4, lens, 21)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    steps = 6
+    kn = torch.randn((steps, 2, 2, 128), generator=g, device="cuda").half()
+    vn = torch.randn((steps, 2, 2, 128), generator=g, device="cuda").half()
+    q = torch.randn((steps, 2, 8, 128), generator=g, device="cuda").half()
+    ref = [eager.decode_step(kn[s], vn[s], q[s], lengths=[n + s for n in lens]) for s in range(steps)]
+    torch.cuda.synchronize()
+    seq0 = graphed.seq_len.clone()
+    tail0 = (graphed.tail_k.clone(), graphed.tail_v.clone(), graphed.records.clone())
+    outs = [torch.empty((2, 8, 128), dtype=torch.float32, device="cuda") for _ in range(steps)]
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=st):
+            for s in range(steps):
+                graphed.decode_step(kn[s], vn[s], q[s], lengths=[n + s for n in lens], out=outs[s], stream=st)
+    for rep in range(3):
+        graphed.seq_len.copy_(seq0)
+        graphed.tail_k.copy_(tail0[0])
+        graphed.tail_v.copy_(tail0[1])
+        graphed.records.copy_(tail0[2])
+        for o in outs:
+            o.fill_(float("nan"))
+        _ = (torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")).sum().item()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            gr.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs[s], ref[s]), f"replay {rep}, step {s}"
+        for a, b in zip(_state(graphed), _state(eager)):
+            assert torch.equal(a, b), f"replay {rep}: cache state"
