@@ -41,10 +41,14 @@ struct RecordMap {
 };
 
 // Byte offset of the record pair of (b, h, g), or -1 if it has no storage.
+// (b, g) are uniform over the calling workgroup: the table entry is a scalar
+// load (its own counter, so waiting for it never waits for vector loads or
+// stores in flight).
 __device__ __forceinline__ int64_t pair_offset(const RecordMap& m, int b, int h, int g, int hkv, int max_groups,
                                                int64_t group_bytes) {
   if (!m.table) return (((int64_t)b * hkv + h) * max_groups + g) * group_bytes;
-  const int blk = m.table[(int64_t)b * max_groups + g];
+  typedef const __attribute__((address_space(4))) int32_t ConstTableEntry;
+  const int blk = *(ConstTableEntry*)(m.table + (int64_t)b * max_groups + g);
   if (blk < 0 || blk >= m.num_blocks) return -1;
   return ((int64_t)blk * hkv + h) * group_bytes;
 }

@@ -42,6 +42,9 @@
 //   lanes publish the two new factors.  One barrier per half-step.  About 110
 //   VGPRs per lane and 70 KB (D 128) of LDS give two workgroups, four waves
 //   per SIMD, on a CU.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "trace.hpp"
@@ -581,9 +584,28 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_tiles_kernel(const 
   seal_finish<D, BITS, KIND == 0>(dst + i * dst_stride, dbg ? dbg + i * (kGroup + D) : nullptr, sm, threadIdx.x);
 }
 
-// Bulk sealing: one workgroup per tile (group g, request-head bh, K|V,
-// layer), tile index g + G (bh + NBH (kind + 2 layer)); groups a request does
-// not have return at once.
+// Tile idx of a bulk seal (group g, request-head bh, K|V, layer; tile index
+// g + G (bh + NBH (kind + 2 layer))): its fp16 source and record, or false
+// if the request has no such group or the group has no storage.  len(b) is
+// request b's prompt length.
+template <int D, typename Len>
+__device__ __forceinline__ bool prefill_tile(const SealPrefillArgs& a, int idx, Len len, const __half*& src,
+                                             uint8_t*& rec, int& kind) {
+  const int g = idx % a.gmax, r = idx / a.gmax;
+  const int bhl = r % a.nbh, r2 = r / a.nbh;
+  const int layer = r2 >> 1;
+  kind = r2 & 1;
+  if (kSink + kGroup * (g + 1) > len(bhl / a.hkv)) return false;
+  const PrefillLayer& L = a.layer[layer];
+  const int64_t bh = (int64_t)a.b0 * a.hkv + bhl;
+  const int64_t off = pair_offset(L.map, (int)(bh / a.hkv), (int)(bh % a.hkv), g, a.hkv, a.max_groups, a.group_bytes);
+  if (off < 0) return false;
+  src = (kind ? L.v : L.k) + (bh * a.src_tokens + kSink + (int64_t)kGroup * g) * D;
+  rec = L.records + off + (kind ? a.rec_k_bytes : 0);
+  return true;
+}
+
+// Bulk sealing at D 128: one workgroup per tile, two resident per CU.
 // One tile per workgroup lets the dispatcher refill a CU as soon as either of
 // its two workgroups finishes.  (A persistent grid that prefetched its next
 // tile during the iterations measured slower: the older workgroup of a CU
@@ -595,16 +617,10 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
   const int idx = blockIdx.x;
   const int tslot = idx * (kSealThreadsPerD * D / 64) + (int)(threadIdx.x >> 6);  // trace build only
   trace_begin(tslot);
-  const int g = idx % a.gmax, r = idx / a.gmax;
-  const int bhl = r % a.nbh, r2 = r / a.nbh;
-  const int kind = r2 & 1, layer = r2 >> 1;
-  if (kSink + kGroup * (g + 1) > a.lens.len[bhl / a.hkv]) return;
-  const PrefillLayer& L = a.layer[layer];
-  const int64_t bh = (int64_t)a.b0 * a.hkv + bhl;
-  const int64_t off = pair_offset(L.map, (int)(bh / a.hkv), (int)(bh % a.hkv), g, a.hkv, a.max_groups, a.group_bytes);
-  if (off < 0) return;
-  const __half* src = (kind ? L.v : L.k) + (bh * a.src_tokens + kSink + (int64_t)kGroup * g) * D;
-  uint8_t* rec = L.records + off + (kind ? a.rec_k_bytes : 0);
+  const __half* src;
+  uint8_t* rec;
+  int kind;
+  if (!prefill_tile<D>(a, idx, [&](int b) { return a.lens.len[b]; }, src, rec, kind)) return;
   uint4 raw[4];
   load_tile<D>(raw, src, threadIdx.x);
   seal_rotate<D>(raw, sm, threadIdx.x);
@@ -616,6 +632,56 @@ __global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_kernel(Seal
   else
     seal_finish_bits<D, false>(a.v_bits, rec, sm, threadIdx.x);
   trace_mark(tslot, 3);  // record stores issued
+}
+
+// Bulk sealing at D 256, where one workgroup (136 KB of LDS) fills a CU: a
+// resident grid whose workgroups take tiles blockIdx.x, + gridDim.x, ... and
+// load the next tile into registers before finishing the current one, so
+// the load does not leave the CU idle at each tile's start.
+template <int D>
+__global__ __launch_bounds__(kSealThreadsPerD * D) void seal_prefill_persistent_kernel(SealPrefillArgs a) {
+  __shared__ SealSmem<D> sm;
+  __shared__ int32_t s_len[kMaxPrefillBatch];   // prompt lengths: LDS reads in the loop wait for nothing else
+  constexpr int kWavesPerTile = kSealThreadsPerD * D / 64;
+  int tid = threadIdx.x;
+  for (int b = tid; b < kMaxPrefillBatch; b += kSealThreadsPerD * D) s_len[b] = a.lens.len[b];
+  __syncthreads();
+  auto len = [&](int b) { return s_len[b]; };
+  int idx = blockIdx.x;
+  const __half* src;
+  uint8_t* rec;
+  int kind;
+  while (idx < a.n_tiles && !prefill_tile<D>(a, idx, len, src, rec, kind)) idx += gridDim.x;
+  if (idx >= a.n_tiles) return;
+  uint4 raw[4];
+  load_tile<D>(raw, src, tid);
+  for (;;) {
+    // The per-lane index math of the phases is recomputed per tile rather
+    // than kept live across the loop (it would not fit the registers).
+    asm volatile("" : "+v"(tid));
+    const int tslot = idx * kWavesPerTile + (tid >> 6);  // trace build only
+    trace_begin(tslot);
+    seal_rotate<D>(raw, sm, tid);
+    trace_mark(tslot, 1);  // tile loaded and rotated
+    int nidx = idx + (int)gridDim.x;
+    const __half* nsrc = nullptr;
+    uint8_t* nrec = nullptr;
+    int nkind = 0;
+    while (nidx < a.n_tiles && !prefill_tile<D>(a, nidx, len, nsrc, nrec, nkind)) nidx += gridDim.x;
+    if (nidx < a.n_tiles) load_tile<D>(raw, nsrc, tid);   // lands during the iterations
+    seal_iterate<D>(a.iters, sm, tid);
+    trace_mark(tslot, 2);  // iterations done
+    if (kind == 0)
+      seal_finish_bits<D, true>(a.k_bits, rec, sm, tid);
+    else
+      seal_finish_bits<D, false>(a.v_bits, rec, sm, tid);
+    trace_mark(tslot, 3);  // record stores issued
+    if (nidx >= a.n_tiles) break;
+    idx = nidx;
+    rec = nrec;
+    kind = nkind;
+    lds_barrier();   // every wave is done with this tile's LDS before the next rotation writes it
+  }
 }
 
 // Seal on arrival.  Workgroup (entry, KV head, K|V): in the predicate form
@@ -728,16 +794,39 @@ static void launch_prefill_t(const SealPrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((seal_prefill_kernel<D>), dim3(a.n_tiles), dim3(kSealThreadsPerD * D), 0, st, a);
 }
 
+// Resident workgroups of the persistent D 256 seal on the current device
+// (0 if the query fails), looked up once per device.
+static int persistent_seal_wgs() {
+  static std::atomic<int> cache[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int v = dev < 16 ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (v > 0) return v;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, seal_prefill_persistent_kernel<256>,
+                                                   kSealThreadsPerD * 256, 0) != hipSuccess)
+    return 0;
+  v = per_cu * decode_cu_count();
+  if (dev < 16 && v > 0) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 hipError_t launch_seal_prefill(int D, const SealPrefillArgs& args, int max_groups_in_batch, int nbh, hipStream_t st) {
   if (max_groups_in_batch <= 0 || nbh <= 0) return hipSuccess;
   SealPrefillArgs a = args;
   a.gmax = max_groups_in_batch;
   a.nbh = nbh;
   a.n_tiles = 2 * a.n_layers * nbh * max_groups_in_batch;
-  if (D == 128)
+  if (D == 128) {
     launch_prefill_t<128>(a, st);
-  else
-    launch_prefill_t<256>(a, st);
+  } else {
+    const int wgs = persistent_seal_wgs();
+    if (wgs > 0)
+      hipLaunchKernelGGL((seal_prefill_persistent_kernel<256>), dim3(std::min(wgs, a.n_tiles)),
+                         dim3(kSealThreadsPerD * 256), 0, st, a);
+    else
+      launch_prefill_t<256>(a, st);
+  }
   return hipGetLastError();
 }
 
