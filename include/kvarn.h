@@ -257,9 +257,11 @@ kvarn_status kvarn_decode_attn(const kvarn_config *cfg, const kvarn_cache *cache
  * decode launches (the split kernel reads the new token from k_new and
  * stores it in its sink or tail slot, the combine kernel advances seq_len):
  * two launches instead of three.  Otherwise (or with NULL) the step is the
- * three launches.  len_host values that differ from the cache's seq_len give
- * undefined results; a negative value returns KVARN_EINVAL before anything
- * is queued.
+ * three launches.  len_host must equal the cache's seq_len: with other
+ * values the outputs are unspecified, and a request whose token would in
+ * fact complete a group or find its cache full is left unchanged (its token
+ * is not appended) rather than written to a wrong slot.  A negative value
+ * returns KVARN_EINVAL before anything is queued.
  */
 kvarn_status kvarn_decode_step(const kvarn_config *cfg, const kvarn_cache *cache,
                                const void *k_new, const void *v_new, const void *q, float *out,

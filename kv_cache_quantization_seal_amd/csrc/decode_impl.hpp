@@ -600,8 +600,20 @@ __device__ void record_split(RecSmem<D, KB, VB, GQ>& sm, const DecodeArgs& a, in
 // lane (token, quarter) holds a quarter of a K row and of a V row.  QK: fp32
 // FMAs against the LDS query; PV: V rows staged in LDS.
 // ---------------------------------------------------------------------------
+// With the append folded into the step, whether request b's token may ride
+// in the decode launches by its device length n: it completes no group and
+// the cache is not full (the caller's host lengths promised this; a request
+// for which they were wrong is left without its token instead of having it
+// written to a wrong slot).
+__device__ __forceinline__ bool fold_ok(const DecodeArgs& a, int n) {
+  const int cap = kSink + kGroup * a.c.max_groups + kGroup - 1;
+  const int n1 = n + 1;
+  return a.k_new && n < cap && !(n1 >= kSink + kGroup && (n1 - kSink) % kGroup == 0);
+}
+
 template <int D, int GQ, int kExactRounds>
-__device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int split, int n) {
+__device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, int kvh, int es, int split, int n,
+                            bool fold) {
   constexpr int kExactPerSplit = kWaves * kExactTok * kExactRounds;  // exact tokens of this split
   constexpr int QD = D / 4;     // channels per lane (quarter row)
   constexpr int CPLX = D / 64;  // channels per lane in the PV part
@@ -634,7 +646,7 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
     const int64_t row = bh * kGroup + (valid[round] ? (in_tail ? e - n_sink : e) : 0);
     // With the append folded in, the newest position (the last exact token)
     // comes from the step's input; its slot is written below.
-    const bool fresh = a.k_new && valid[round] && e == n_exact - 1;
+    const bool fresh = fold && valid[round] && e == n_exact - 1;
     const __half* ks = fresh ? a.k_new + bh * D : (in_tail ? a.c.tail_k : a.c.sink_k) + row * D;
     const __half* vs = fresh ? a.v_new + bh * D : (in_tail ? a.c.tail_v : a.c.sink_v) + row * D;
     dst[round] = fresh ? row * D + quarter * QD : -1;
@@ -656,7 +668,7 @@ __device__ void exact_split(ExactSmem<D, GQ>& sm, const DecodeArgs& a, int b, in
   __syncthreads();
   const int tslot = (int)blockIdx.x * kWaves + w;  // trace build only
   trace_mark(tslot, 1);  // query staged
-  if (a.k_new) {
+  if (fold) {
 #pragma unroll
     for (int round = 0; round < kExactRounds; ++round) {
       if (dst[round] >= 0) {
@@ -804,19 +816,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int nex = a.nsplit - a.n_rec_splits;
   const int npair = a.c.batch * a.c.hkv;
   const int bx = blockIdx.x;
-  const int fold = a.k_new ? 1 : 0;  // the step's own token counts (append folded in)
   if (bx < nex * npair) {
     const int pair = bx / nex, es = bx - pair * nex;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
+    const int n = a.c.seq_len[b];
+    const bool fold = fold_ok(a, n);   // the step's own token counts (append folded in)
     if (nex == 4)
-      exact_split<D, GQ, 1>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b] + fold);
+      exact_split<D, GQ, 1>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, n + fold, fold);
     else
-      exact_split<D, GQ, 2>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, a.c.seq_len[b] + fold);
+      exact_split<D, GQ, 2>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, n + fold, fold);
   } else {
     const int r = bx - nex * npair;
     const int pair = r / a.n_rec_splits, split = r - pair * a.n_rec_splits;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
-    record_split<D, KB, VB, GQ, PAGED>(sm.rec, a, b, kvh, split, a.c.seq_len[b] + fold);
+    const int n = a.c.seq_len[b];
+    record_split<D, KB, VB, GQ, PAGED>(sm.rec, a, b, kvh, split, n + fold_ok(a, n));
   }
 }
 
@@ -839,7 +853,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   // Append folded into the step: the split kernel has attended over the new
   // token and stored it; the length moves on here, once per request (no
   // kernel of this launch reads it).
-  if (a.k_new && hq == 0 && tid == 0) a.c.seq_len[b] = a.c.seq_len[b] + 1;
+  if (a.k_new && hq == 0 && tid == 0) {
+    const int n = a.c.seq_len[b];
+    if (fold_ok(a, n)) a.c.seq_len[b] = n + 1;
+  }
   const int64_t base = ((int64_t)b * a.hq + hq) * ns;
   const float* ml = a.ws_ml + 2 * base;
   const float* ob = a.ws_o + base * D + P * l;

@@ -139,3 +139,25 @@ def test_decode_step_graph_replays():
             assert torch.equal(outs[s], ref[s]), f"replay {rep}, step {s}"
         for a, b in zip(_state(graphed), _state(eager)):
             assert torch.equal(a, b), f"replay {rep}: cache state"
+
+
+def test_decode_step_wrong_host_length_leaves_request_unchanged():
+    """Host lengths that claim no group completes when, by the cache's own
+    length, request 0's token does: request 0 is left as it was (no token
+    written, length unchanged) instead of having the token written into a
+    sink row; request 1 appends as usual."""
+    cfg = K.make_config(128, 4, 2, 2, 2)
+    c, _ = _pair(cfg, 2, 2, [255, 100], 31)
+    before = [t.clone() for t in _state(c)]
+    g = torch.Generator(device="cuda").manual_seed(2)
+    kn = torch.randn((2, 2, 128), generator=g, device="cuda").half()
+    vn = torch.randn((2, 2, 128), generator=g, device="cuda").half()
+    q = torch.randn((2, 4, 128), generator=g, device="cuda").half()
+    c.decode_step(kn, vn, q, lengths=[254, 100])   # wrong for request 0 (its cache holds 255)
+    torch.cuda.synchronize()
+    assert c.seq_len.cpu().tolist() == [255, 101]
+    for name, t0 in zip(("sink_k", "sink_v", "tail_k", "tail_v"), before[:4]):
+        t = getattr(c, name)
+        assert torch.equal(t[0], t0[0]), name
+    assert torch.equal(c.sink_k[1, :, 100], kn[1]) and torch.equal(c.sink_v[1, :, 100], vn[1])
+    assert torch.equal(c.records, before[4])
