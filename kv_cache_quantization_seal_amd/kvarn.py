@@ -247,6 +247,8 @@ class KVarNCache:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         if scale is None:
             scale = self.cfg.head_dim ** -0.5
+        if lengths is not None and len(lengths) != self.batch:
+            raise ValueError(f"lengths has {len(lengths)} entries for a batch of {self.batch}")
         lens = None if lengths is None else (ctypes.c_int32 * self.batch)(*[int(x) for x in lengths])
         _check(lib().kvarn_decode_step(ctypes.byref(self.cfg), ctypes.byref(self.view), _ptr(k_new), _ptr(v_new),
                                        _ptr(q), _ptr(out), float(scale), lens, _ptr(self.workspace),
