@@ -43,6 +43,9 @@ def _state(c):
     (128, 4, 4, 3, 5, [127, 400], 2, 160, False),                  # reaches capacity (mg 2: 511 tokens)
     (256, 8, 4, 4, 2, [500, 130], 4, 100, False),                  # head dim 256
     (128, 8, 2, 4, 4, [300, 900, 20], 8, 130, True),               # paged records
+    (256, 4, 4, 8, 8, [330, 140], 4, 60, False),                   # head dim 256, GQ 1, 8-bit codes
+    (128, 16, 4, 6, 5, [129, 1500], 12, 80, False),                # wide codes, a long request
+    (256, 8, 2, 2, 2, [0, 700], 6, 70, True),                      # paged, head dim 256, an empty request
 ])
 def test_decode_step_equals_append_then_decode(d, hq, hkv, kb, vb, lens, mg, steps, paged):
     cfg = K.make_config(d, hq, hkv, kb, vb)
