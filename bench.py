@@ -264,6 +264,9 @@ def trace_run(args, reps=8):
     print(json.dumps({"workload": wl.name, "trace": args.trace, "plan": plan, "reps": summaries}))
 
 
+# Phases of the chunked-prefill trace build (per tile).  In eight-wave
+# workgroups waves 0-3 stage only K halves and waves 4-7 only V halves, so
+# the two kinds are summarized apart.
 PREFILL_PHASES = ["issue_next_record", "query_operand", "qk_mfma", "softmax_and_pv_operands", "barrier_a",
                   "stage_k", "pv_mfma", "barrier_b", "stage_v"]
 
@@ -281,10 +284,8 @@ def prefill_trace(args, wl, caches, e0, e1, flush_buf, sink):
     # Workgroups of 8 waves (128 query rows) at D 128 when that grid has one
     # per CU, else of 4 waves (64 rows): the launch's own rule.
     wgs8 = -(-chunk * gq // 128) * wl.num_kv_heads * wl.batch
-    if wl.head_dim == 128 and wgs8 >= torch.cuda.get_device_properties(0).multi_processor_count:
-        n_waves = wgs8 * 8
-    else:
-        n_waves = -(-chunk * gq // 64) * wl.num_kv_heads * wl.batch * 4
+    eight = wl.head_dim == 128 and wgs8 >= torch.cuda.get_device_properties(0).multi_processor_count
+    n_waves = wgs8 * 8 if eight else -(-chunk * gq // 64) * wl.num_kv_heads * wl.batch * 4
     reps = []
     for c in caches[:3]:
         probe.read(flush_buf, sink)
@@ -297,12 +298,18 @@ def prefill_trace(args, wl, caches, e0, e1, flush_buf, sink):
         rec = wavetrace.read(wavetrace.PREFILL_ATTN, n_waves).astype(np.int64)
         ran = rec[:, 15] > rec[:, 1]
         tiles = 1 + (wl.context - 128) // 128 + 1
-        cyc = rec[ran][:, 2:2 + len(PREFILL_PHASES)].astype(np.float64)
         life = (rec[ran][:, 15] - rec[ran][:, 1]).astype(np.float64)
+        # the slot of a wave is its workgroup's index times the waves per workgroup plus the wave
+        wave = np.arange(n_waves) % (8 if eight else 4)
+        kinds = ({"k_staging_waves": wave < 4, "v_staging_waves": wave >= 4} if eight else {"all_waves": wave >= 0})
+        phases = {}
+        for kind, sel in kinds.items():
+            cyc = rec[ran & sel][:, 2:2 + len(PREFILL_PHASES)].astype(np.float64)
+            phases[kind] = {n: float(np.median(cyc[:, i]) / tiles) for i, n in enumerate(PREFILL_PHASES)}
         reps.append({"event_us": e0.elapsed_time(e1) * 1e3, "waves": int(ran.sum()), "tiles_per_wave": tiles,
+                     "waves_per_workgroup": 8 if eight else 4,
                      "wave_cycles_per_tile": float(np.median(life) / tiles),
-                     "phase_cycles_per_tile": {n: float(np.median(cyc[:, i]) / tiles)
-                                               for i, n in enumerate(PREFILL_PHASES)}})
+                     "phase_cycles_per_tile": phases})
     return {"workload": wl.name, "trace": "prefill", "chunk": chunk, "reps": reps}
 
 

@@ -63,12 +63,18 @@ constexpr float kPaLog2e = 1.4426950408889634f;
 // 128-bit row writes of the staging are conflict-free when lanes
 // {4j .. 4j+3, 4j+8 .. 4j+11} (served together) write rows that differ mod 8,
 // which write_row() arranges.
-template <int D>
+// Staged query rows (fp32, pitch QP = 8 mod 64 dwords) hold the value of
+// K-tile column position p = 32 s + 8 G + 4 h + e at 32 s + 16 h + 4 G + e,
+// so that lane 16 G + n reads its 8 values of step s as two conflict-free
+// 128-bit reads.  Four-wave workgroups stage them over the K and V tiles
+// and keep them in registers; eight-wave ones keep them in LDS (KEEPQ).
+template <int D, bool KEEPQ>
 struct PaSmem {
   static constexpr int KP = D + 16;    // K tile: 128 token rows, pitch in halves
   static constexpr int VP = 128 + 16;  // V tile: D channel rows of 128 token positions
-  static constexpr int QP = D + 4;    // staged query rows (fp32), aliasing the K and V tiles
+  static constexpr int QP = D + 8;     // staged query rows (fp32)
   static_assert(128 * QP * 4 <= 128 * KP * 2 + D * VP * 2, "staged queries fit the K and V tiles");
+  alignas(16) float q[KEEPQ ? 128 * QP : 4];   // kept query rows
   alignas(16) _Float16 k[128 * KP];
   alignas(16) _Float16 v[D * VP];
   alignas(16) float sk[128];   // per K tile row: s^K of its token
@@ -91,6 +97,8 @@ __device__ __forceinline__ int code_to_pos(int c, int B) {
   const int h = B >> 1;
   return (c & -B) | ((c & (h - 1)) << 1) | ((c & h) ? 1 : 0);
 }
+// Slot of K-tile column position p in a staged query row (see PaSmem).
+__device__ __forceinline__ int q_slot(int p) { return (p & ~31) | ((p & 4) << 2) | ((p & 24) >> 1) | (p & 3); }
 // K tile row r <-> V tile position p, within 32-token blocks: row bits
 // (i: 2, G: 2, h: 1) are position bits (i: 2, h: 1, G: 2).  A QK result lane
 // then holds, for PV step u, the weights of positions 32u + 8G .. +7: its B
@@ -323,16 +331,18 @@ __device__ __forceinline__ void load_item(uint32_t (&w)[2 * MAXB], __amdgpu_buff
 
 template <int D, int GQ, int MAXB, int NW>
 __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefill_attn_kernel(PrefillAttnArgs a) {
-  __shared__ PaSmem<D> sm;
   static_assert(NW == 4 || (NW == 8 && D == 128), "four waves, or eight at head dimension 128");
-  constexpr int SPLIT = NW == 8;  // K and V staging split between the wave halves
+  constexpr bool SPLIT = NW == 8;  // K and V staging split between the wave halves
+  __shared__ PaSmem<D, SPLIT> sm;
   constexpr int ROWS = 16 * NW;   // query rows
   constexpr int KS = D / 32;      // MFMA k-steps over the channels
   constexpr int NCT = D / 16;     // output channel tiles
   constexpr int POS = ROWS / GQ;  // positions per workgroup
   constexpr int NI = D / 128;     // K or V items of 64 codes per thread
-  constexpr int KP = PaSmem<D>::KP, VP = PaSmem<D>::VP, QP = PaSmem<D>::QP;
-  const int w = threadIdx.x >> 6;
+  constexpr int KP = PaSmem<D, SPLIT>::KP, VP = PaSmem<D, SPLIT>::VP, QP = PaSmem<D, SPLIT>::QP;
+  // Eight-wave workgroups branch on the wave half: a scalar wave index keeps
+  // those branches (and the loads inside them) uniform.
+  const int w = SPLIT ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
   const bool vrole = SPLIT && w >= NW / 2;   // stages V items only (else K items); wave-uniform
   int tid = threadIdx.x, l = tid & 63;   // re-derived per tile (see the tile loop)
   const int G = l >> 4, n = l & 15;
@@ -368,10 +378,10 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
 
   // ---- queries: rotated, times softmax_scale * log2(e), times a per-row
   // power of two that puts the row's largest magnitude in [2^11, 2^12)
-  // (fp32 in LDS over the K tile); then read as the B operand in the K
-  // width's pair order.
+  // (fp32 in LDS, each channel at the slot of its K-tile column position in
+  // the K width's pair order); read as the B operand.
+  float* const qs = SPLIT ? sm.q : reinterpret_cast<float*>(sm.k);
   {
-    float* qs = reinterpret_cast<float*>(sm.k);
     constexpr int NT = D / 64;
 #pragma unroll 1
     for (int it = tid; it < ROWS * NT; it += 64 * NW) {
@@ -391,21 +401,25 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
       float inv;
       const float sc = pow2_scale(mx * qk_scale, inv) * qk_scale;
 #pragma unroll
-      for (int k = 0; k < 64; ++k) qs[r * QP + 64 * chunk + k] = x[k] * sc;
+      for (int k = 0; k < 64; ++k) qs[r * QP + q_slot(code_to_pos(64 * chunk + k, Bk))] = x[k] * sc;
       if (chunk == 0) sm.qinv[r] = inv;
     }
   }
   lds_barrier();
-  float qr[KS][8];
-  {
-    const float* qs = reinterpret_cast<const float*>(sm.k);
+  float qr[KS][8];   // the lane's query row, in registers for a tile's use
+  auto read_query = [&]() {
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qr[s][e] = qs[r_lane * QP + pos_to_code(32 * s + 8 * G + e, Bk)];
-  }
+      for (int h = 0; h < 2; ++h) {
+        const v4f x = *reinterpret_cast<const v4f*>(qs + r_lane * QP + 32 * s + 16 * h + 4 * G);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qr[s][4 * h + e] = x[e];
+      }
+  };
+  if (!SPLIT) read_query();
   const float qinv = sm.qinv[r_lane];
-  lds_barrier();   // the staged queries are read; the K and V tiles are free
+  if (!SPLIT) lds_barrier();   // the staged queries are read; the K and V tiles are free
 
   // ---- staging --------------------------------------------------------------
   // Exact tile: `count` fp16 rows [128][D] at src (rows past count are zero),
@@ -550,39 +564,34 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
 #pragma unroll
   for (int c = 0; c < NCT; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
   bool rotated = false;   // frame of o
-  bool present = true;    // tile t has storage
 
-#pragma unroll 1
-  for (int t = 0; t < T; ++t) {
-    // Per-lane index math of the staging and masking (tens of values) is
-    // cheaper to recompute per tile than to keep live across the loop.
-    asm volatile("" : "+v"(tid));
-    l = tid & 63;
-    const bool exact = t == 0 || (has_tail && t == T - 1);
-    const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
-    const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
+  // ---- the phases of a tile, for one wave --------------------------------
+  v8h bhi[KS], blo[KS];   // QK B operand: the query (hi + lo)
+  float lg[8][4];         // QK results, then the softmax weights
+  float f;                // logit scale to log2 units
+  v8h bwh[4], bwl[4];     // PV B operands: w = p * s^V (hi + lo) for positions 32 u + 8 G + e
 
-    // ---- exact tile: the fp16 query rows as the B operand.  Loaded and
-    // waited for before the next record's loads are issued: the load counter
-    // completes in order, so a wait for them issued later would also wait for
-    // that whole prefetch.
-    v8h bhi[KS], blo[KS];
-    if (exact) {
-      uint4 x[KS];
+  // Exact tile: the fp16 query rows as the B operand.  Loaded and waited for
+  // before the next record's loads are issued: the load counter completes in
+  // order, so a wait for them issued later would also wait for that whole
+  // prefetch.
+  auto load_exact_query = [&]() {
+    uint4 x[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        x[s] = prow >= 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * G) : make_uint4(0, 0, 0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int s = 0; s < KS; ++s)
+      x[s] = prow >= 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * G) : make_uint4(0, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        asm volatile("" : "+v"(x[s].x), "+v"(x[s].y), "+v"(x[s].z), "+v"(x[s].w));   // ready here
-        bhi[s] = __builtin_bit_cast(v8h, x[s]);
-        blo[s] = v8h{};   // one code path for both kinds: the low product adds zero
-      }
+    for (int s = 0; s < KS; ++s) {
+      asm volatile("" : "+v"(x[s].x), "+v"(x[s].y), "+v"(x[s].z), "+v"(x[s].w));   // ready here
+      bhi[s] = __builtin_bit_cast(v8h, x[s]);
+      blo[s] = v8h{};   // one code path for both kinds: the low product adds zero
     }
-
-    // ---- issue the next record's loads
-    bool next_present = t + 1 < T;
+  };
+  // Issues this thread's loads of tile t + 1 when it is a record; returns
+  // whether tile t + 1 has storage.
+  auto issue_next = [&](int t) {
+    bool np = t + 1 < T;
     if (t + 1 <= n_rec) {
       const int g = t;
       int64_t off;
@@ -592,16 +601,18 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
         off = (ent >= 0 && ent < a.c.map.num_blocks) ? ((int64_t)ent * a.c.hkv + kvh) * a.c.group_bytes : -1;
         if (g + 1 < n_rec) ent = *(ConstI32*)(table + (int64_t)b * a.c.max_groups + g + 1);
       }
-      next_present = off >= 0;
-      if (next_present) issue_record(a.c.records + off);
+      np = off >= 0;
+      if (np) issue_record(a.c.records + off);
     }
-
-    phase_end(pc, 0);   // next record's loads issued
-    // ---- QK^T: logits of the lane's row for K tile rows 16 tt + 4 G + i
-    float f;   // logit scale to log2 units
+    return np;
+  };
+  // QK^T: logits of the lane's row for K tile rows 16 tt + 4 G + i (record
+  // tiles first form the query operand q~ = q_r c^K, split into fp16 hi + lo).
+  auto qk = [&](bool exact) {
     if (exact) {
       f = qk_scale;
     } else {
+      if (SPLIT) read_query();   // kept in LDS: 32 registers fewer across the steps
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const v4f c0 = *reinterpret_cast<const v4f*>(sm.ck + 32 * s + 8 * G);
@@ -622,33 +633,78 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
       }
       f = qinv * sm.kscale;
     }
-    phase_end(pc, 1);   // query operand of the tile
-    float lg[8][4];
+    phase_end(pc, 1);
+    if constexpr (SPLIT) {
+      // Two token tiles at a time (independent MFMA chains), in groups of two
+      // k-steps: the next group's A operands are read from LDS before this
+      // group's eight products are issued, so a wave covers its own LDS
+      // latency (in an eight-wave workgroup, half the waves stage meanwhile;
+      // a four-wave one has no registers to spare for it).
+      constexpr int NG = 4 * KS / 2;   // groups: 4 token-tile pairs x KS / 2
+      v8h A[2][4];
+      auto load_a = [&](v8h* dst, int gi) {
+        const int tp = 2 * (gi / (KS / 2)), s0 = 2 * (gi % (KS / 2));
+        const _Float16* kr0 = sm.k + (16 * tp + n) * KP + 8 * G;
+        dst[0] = ld8(kr0 + 32 * s0);
+        dst[1] = ld8(kr0 + 16 * KP + 32 * s0);
+        dst[2] = ld8(kr0 + 32 * s0 + 32);
+        dst[3] = ld8(kr0 + 16 * KP + 32 * s0 + 32);
+      };
+      load_a(A[0], 0);
+      v4f acc0, acc1;
 #pragma unroll
-    for (int tp = 0; tp < 8; tp += 2) {   // two token tiles at a time: independent MFMA chains
-      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      const _Float16* kr0 = sm.k + (16 * tp + n) * KP + 8 * G;
-      const _Float16* kr1 = kr0 + 16 * KP;
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 1 < NG) load_a(A[(gi + 1) & 1], gi + 1);
+        __builtin_amdgcn_sched_barrier(0);   // the next group's reads stay ahead of this group's products
+        const int tp = 2 * (gi / (KS / 2)), s0 = 2 * (gi % (KS / 2));
+        if (s0 == 0) acc0 = acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+        const v8h* a = A[gi & 1];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const v8h a0 = ld8(kr0 + 32 * s), a1 = ld8(kr1 + 32 * s);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bhi[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bhi[s], acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, blo[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, blo[s], acc1, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h], bhi[s0 + h], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h + 1], bhi[s0 + h], acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h], blo[s0 + h], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h + 1], blo[s0 + h], acc1, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s0 + 2 == KS) {
+          const v4f sk0 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 4 * G);
+          const v4f sk1 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 16 + 4 * G);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            lg[tp][i] = acc0[i] * sk0[i];
+            lg[tp + 1][i] = acc1[i] * sk1[i];
+          }
+        }
       }
-      const v4f sk0 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 4 * G);
-      const v4f sk1 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 16 + 4 * G);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lg[tp][i] = acc0[i] * sk0[i];
-        lg[tp + 1][i] = acc1[i] * sk1[i];
+      for (int tp = 0; tp < 8; tp += 2) {   // two token tiles at a time: independent MFMA chains
+        v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const _Float16* kr0 = sm.k + (16 * tp + n) * KP + 8 * G;
+        const _Float16* kr1 = kr0 + 16 * KP;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const v8h a0 = ld8(kr0 + 32 * s), a1 = ld8(kr1 + 32 * s);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bhi[s], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bhi[s], acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, blo[s], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, blo[s], acc1, 0, 0, 0);
+        }
+        const v4f sk0 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 4 * G);
+        const v4f sk1 = *reinterpret_cast<const v4f*>(sm.sk + 16 * tp + 16 + 4 * G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lg[tp][i] = acc0[i] * sk0[i];
+          lg[tp + 1][i] = acc1[i] * sk1[i];
+        }
       }
     }
-
-    phase_end(pc, 2);   // QK products
-    // ---- online softmax of the lane's row (its 128 tokens span the four lane
-    // groups); tiles below every row of the block and complete need no mask
+  };
+  // Online softmax of the lane's row (its 128 tokens span the four lane
+  // groups) and the PV operands; tiles below every row of the block and
+  // complete need no mask.
+  auto softmax = [&](int base, int count) {
     const bool full = __builtin_amdgcn_readfirstlane((int)(count == kGroup && base + kGroup - 1 <= pmin)) != 0;
     float alpha, m_new, ps = 0.f;
     if (full) {
@@ -692,7 +748,6 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
     }
     l_run = fmaf(l_run, alpha, xor32_sum(xor16_sum(ps)));
     m_run = m_new;
-    v8h bwh[4], bwl[4];   // PV B operands: w = p * s^V (hi + lo) for positions 32 u + 8 G + e
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const v4f sv4 = *reinterpret_cast<const v4f*>(sm.sv + 16 * tt + 4 * G);
@@ -714,62 +769,126 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
 #pragma unroll
       for (int c = 0; c < NCT; ++c) o[c] *= alpha;
     }
-
-    phase_end(pc, 3);   // softmax and the PV operands
-    // ---- the next tile's K half, once every wave is done with this K tile
-    if (t + 1 < T) {
-      lds_barrier();
-      phase_end(pc, 4);   // barrier A
-      if (!vrole) {
-        if (t + 1 == T - 1 && has_tail)
-          stage_k_exact(a.c.tail_k + bh * kGroup * D, tail_count, 0, SPLIT ? 32 * NW : 64 * NW);
-        else if (next_present)
-          stage_k_record();
-      }
-    }
-
-    phase_end(pc, 5);   // K staging
-    // ---- PV: O^T += V^T w^T, channel tiles of 16, token steps of 32
+  };
+  // PV: O^T += V^T w^T, channel tiles of 16, token steps of 32.
+  auto pv = [&](bool exact) {
     if (rotated == exact) {   // frame change
       rotate_out<NCT>(o, G);
       rotated = !exact;
     }
+    if constexpr (SPLIT) {
+      // Two channel tiles at a time, in groups of two token steps, the next
+      // group's A operands read ahead as in QK.
+      constexpr int NG = NCT / 2 * 2;   // groups: NCT / 2 channel-tile pairs x 2
+      v8h A[2][4];
+      auto load_a = [&](v8h* dst, int gi) {
+        const int cp = 2 * (gi / 2), u0 = 2 * (gi % 2);
+        const _Float16* vr0 = sm.v + (16 * cp + n) * VP + 8 * G;
+        dst[0] = ld8(vr0 + 32 * u0);
+        dst[1] = ld8(vr0 + 16 * VP + 32 * u0);
+        dst[2] = ld8(vr0 + 32 * u0 + 32);
+        dst[3] = ld8(vr0 + 16 * VP + 32 * u0 + 32);
+      };
+      load_a(A[0], 0);
+      v4f acc0, acc1;
 #pragma unroll
-    for (int cp = 0; cp < NCT; cp += 2) {   // two channel tiles at a time
-      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      const _Float16* vr0 = sm.v + (16 * cp + n) * VP + 8 * G;
-      const _Float16* vr1 = vr0 + 16 * VP;
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 1 < NG) load_a(A[(gi + 1) & 1], gi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int cp = 2 * (gi / 2), u0 = 2 * (gi % 2);
+        if (u0 == 0) acc0 = acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+        const v8h* a = A[gi & 1];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v8h a0 = ld8(vr0 + 32 * u), a1 = ld8(vr1 + 32 * u);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bwh[u], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bwh[u], acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bwl[u], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bwl[u], acc1, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h], bwh[u0 + h], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h + 1], bwh[u0 + h], acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h], bwl[u0 + h], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2 * h + 1], bwl[u0 + h], acc1, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u0 == 2) {
+          const v4f cv0 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 4 * G);
+          const v4f cv1 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 16 + 4 * G);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[cp][i] = fmaf(acc0[i], cv0[i], o[cp][i]);
+            o[cp + 1][i] = fmaf(acc1[i], cv1[i], o[cp + 1][i]);
+          }
+        }
       }
-      const v4f cv0 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 4 * G);
-      const v4f cv1 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 16 + 4 * G);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[cp][i] = fmaf(acc0[i], cv0[i], o[cp][i]);
-        o[cp + 1][i] = fmaf(acc1[i], cv1[i], o[cp + 1][i]);
+      for (int cp = 0; cp < NCT; cp += 2) {   // two channel tiles at a time
+        v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const _Float16* vr0 = sm.v + (16 * cp + n) * VP + 8 * G;
+        const _Float16* vr1 = vr0 + 16 * VP;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const v8h a0 = ld8(vr0 + 32 * u), a1 = ld8(vr1 + 32 * u);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bwh[u], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bwh[u], acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bwl[u], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bwl[u], acc1, 0, 0, 0);
+        }
+        const v4f cv0 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 4 * G);
+        const v4f cv1 = *reinterpret_cast<const v4f*>(sm.cv + 16 * cp + 16 + 4 * G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[cp][i] = fmaf(acc0[i], cv0[i], o[cp][i]);
+          o[cp + 1][i] = fmaf(acc1[i], cv1[i], o[cp + 1][i]);
+        }
       }
     }
+  };
+  // Staging of tile u >= 1 (the tail, or a record whose loads were issued a
+  // tile ahead): K half by the K-staging threads, V half by the V-staging ones.
+  auto stage_k_tile = [&](int u, bool pres) {
+    if (has_tail && u == T - 1)
+      stage_k_exact(a.c.tail_k + bh * kGroup * D, tail_count, 0, SPLIT ? 32 * NW : 64 * NW);
+    else if (pres)
+      stage_k_record();
+  };
+  auto stage_v_tile = [&](int u, bool pres) {
+    if (has_tail && u == T - 1)
+      stage_v_exact(a.c.tail_v + bh * kGroup * D, tail_count, SPLIT ? 32 * NW : 0, SPLIT ? 32 * NW : 64 * NW);
+    else if (pres)
+      stage_v_record();
+  };
 
-    phase_end(pc, 6);   // PV products
-    // ---- the next tile's V half, once every wave is done with this V tile
+  bool present = true;   // tile t has storage
+#pragma unroll 1
+  for (int t = 0; t < T; ++t) {
+    // Per-lane index math of the staging and masking (tens of values) is
+    // cheaper to recompute per tile than to keep live across the loop.
+    asm volatile("" : "+v"(tid));
+    l = tid & 63;
+    const bool exact = t == 0 || (has_tail && t == T - 1);
+    const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
+    const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
+    if (exact) load_exact_query();
+    const bool np = issue_next(t);
+    phase_end(pc, 0);   // next record's loads issued
+    qk(exact);          // phase 1 (query operand) and phase 2 (products)
+    phase_end(pc, 2);
+    softmax(base, count);
+    phase_end(pc, 3);
+    // the next tile's K half, once every wave is done with this K tile
     if (t + 1 < T) {
       lds_barrier();
-      phase_end(pc, 7);   // barrier B
-      if (vrole || !SPLIT) {
-        if (t + 1 == T - 1 && has_tail)
-          stage_v_exact(a.c.tail_v + bh * kGroup * D, tail_count, SPLIT ? 32 * NW : 0, SPLIT ? 32 * NW : 64 * NW);
-        else if (next_present)
-          stage_v_record();
-      }
+      phase_end(pc, 4);
+      if (!vrole) stage_k_tile(t + 1, np);
     }
-    present = next_present;
-    phase_end(pc, 8);   // V staging
+    phase_end(pc, 5);
+    pv(exact);
+    phase_end(pc, 6);
+    // the next tile's V half, once every wave is done with this V tile
+    if (t + 1 < T) {
+      lds_barrier();
+      phase_end(pc, 7);
+      if (vrole || !SPLIT) stage_v_tile(t + 1, np);
+    }
+    phase_end(pc, 8);
+    present = np;
   }
   phase_store(((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * NW + w, pc);
 
