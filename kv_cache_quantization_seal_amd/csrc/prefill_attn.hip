@@ -79,10 +79,10 @@ struct PaSmem {
   alignas(16) _Float16 v[D * VP];
   alignas(16) float sk[128];   // per K tile row: s^K of its token
   alignas(16) float sv[128];   // per K tile row: s^V of its token / 2^eV
-  alignas(16) float ck[D];     // per K tile column: c^K of its channel / 2^eK
+  alignas(16) float ck[2 * D]; // per K tile column: c^K of its channel / 2^eK (two tiles' worth)
   alignas(16) float cv[D];     // per channel: c^V * 2^eV
   float qinv[128];             // per row: inverse power-of-two scale of the staged query
-  float kscale;                // 2^eK of the staged record tile
+  float kscale[2];             // 2^eK of the record tiles in the two c^K buffers
   float vscale;                // 2^eV of the staged record tile
 };
 
@@ -494,39 +494,46 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
       if (NI > 1) rs[NI - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, soff + 256, 0, 0);   // c^K / c^V waves
     }
   };
+  // Role 1: c^K of the record in rs, normalized by the power of two of its
+  // maximum so that q~ stays below 2^12, into c^K buffer buf.
+  auto stage_ck = [&](int buf) {
+    float x[2 * NI];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      x[2 * i] = h2f((uint16_t)(rs[i] & 0xFFFFu));
+      x[2 * i + 1] = h2f((uint16_t)(rs[i] >> 16));
+      mx = fmaxf(mx, fmaxf(x[2 * i], x[2 * i + 1]));
+    }
+    mx = wave_max_f(mx);
+    int e;
+    (void)frexpf(mx, &e);
+    const float down = ldexpf(1.f, -e);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sm.ck[buf * D + code_to_pos(2 * (l + 64 * i) + h, Bk)] = x[2 * i + h] * down;
+    if (l == 0) sm.kscale[buf] = ldexpf(1.f, e);
+  };
   auto stage_k_record = [&]() {   // K-staging waves
 #pragma unroll
     for (int i = 0; i < NI; ++i) decode_item_rt<MAXB>(rc[0][i], kb, sm.k + cdst[0][i]);
     if (role == 0) {
       sm.sk[krow_of_token(2 * l)] = h2f((uint16_t)(rs[0] & 0xFFFFu));
       sm.sk[krow_of_token(2 * l + 1)] = h2f((uint16_t)(rs[0] >> 16));
-    } else if (role == 1 || role == 2) {
-      // normalize c^K (role 1) or s^V (role 2) by the power of two of its
-      // maximum, so that q~ stays below 2^12 and w = p s^V below 1
-      const int nd = role == 1 ? NI : 1;
-      float x[2 * NI];
-      float mx = 0.f;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        x[2 * i] = h2f((uint16_t)(rs[i] & 0xFFFFu));
-        x[2 * i + 1] = h2f((uint16_t)(rs[i] >> 16));
-        if (i < nd) mx = fmaxf(mx, fmaxf(x[2 * i], x[2 * i + 1]));
-      }
-      mx = wave_max_f(mx);
+    } else if (role == 1) {
+      if (!SPLIT) stage_ck(0);   // eight-wave workgroups stage c^K a window earlier
+    } else if (role == 2) {
+      // s^V, normalized by the power of two of its maximum so that
+      // w = p s^V stays below 1
+      const float x0 = h2f((uint16_t)(rs[0] & 0xFFFFu)), x1 = h2f((uint16_t)(rs[0] >> 16));
+      const float mx = wave_max_f(fmaxf(x0, x1));
       int e;
       (void)frexpf(mx, &e);
       const float down = ldexpf(1.f, -e);
-      if (role == 1) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) sm.ck[code_to_pos(2 * (l + 64 * i) + h, Bk)] = x[2 * i + h] * down;
-        if (l == 0) sm.kscale = ldexpf(1.f, e);
-      } else {
-        sm.sv[krow_of_token(2 * l)] = x[0] * down;
-        sm.sv[krow_of_token(2 * l + 1)] = x[1] * down;
-        if (l == 0) sm.vscale = ldexpf(1.f, e);
-      }
+      sm.sv[krow_of_token(2 * l)] = x0 * down;
+      sm.sv[krow_of_token(2 * l + 1)] = x1 * down;
+      if (l == 0) sm.vscale = ldexpf(1.f, e);
     }
   };
   auto stage_v_record = [&]() {   // V-staging waves
@@ -606,34 +613,33 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
     }
     return np;
   };
-  // QK^T: logits of the lane's row for K tile rows 16 tt + 4 G + i (record
-  // tiles first form the query operand q~ = q_r c^K, split into fp16 hi + lo).
-  auto qk = [&](bool exact) {
-    if (exact) {
-      f = qk_scale;
-    } else {
-      if (SPLIT) read_query();   // kept in LDS: 32 registers fewer across the steps
+  // Record tile: the query operand q~ = q_r c^K (c^K from buffer buf),
+  // split into fp16 hi + lo; returns the logit scale to log2 units.
+  auto record_operand = [&](int buf) {
+    if (SPLIT) read_query();   // kept in LDS: 32 registers fewer across the steps
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const v4f c0 = *reinterpret_cast<const v4f*>(sm.ck + 32 * s + 8 * G);
-        const v4f c1 = *reinterpret_cast<const v4f*>(sm.ck + 32 * s + 8 * G + 4);
+    for (int s = 0; s < KS; ++s) {
+      const v4f c0 = *reinterpret_cast<const v4f*>(sm.ck + buf * D + 32 * s + 8 * G);
+      const v4f c1 = *reinterpret_cast<const v4f*>(sm.ck + buf * D + 32 * s + 8 * G + 4);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float x0 = qr[s][e] * (e < 4 ? c0[e] : c1[e - 4]);
-          const float x1 = qr[s][e + 1] * (e < 4 ? c0[e + 1] : c1[e - 3]);
-          const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);   // fp16-exact high part
-          const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
-          const auto ph = __builtin_amdgcn_cvt_pkrtz(h0, h1);
-          const auto pl = __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1);
-          bhi[s][e] = ph[0];
-          bhi[s][e + 1] = ph[1];
-          blo[s][e] = pl[0];
-          blo[s][e + 1] = pl[1];
-        }
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = qr[s][e] * (e < 4 ? c0[e] : c1[e - 4]);
+        const float x1 = qr[s][e + 1] * (e < 4 ? c0[e + 1] : c1[e - 3]);
+        const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFFE000u);   // fp16-exact high part
+        const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFFE000u);
+        const auto ph = __builtin_amdgcn_cvt_pkrtz(h0, h1);
+        const auto pl = __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1);
+        bhi[s][e] = ph[0];
+        bhi[s][e + 1] = ph[1];
+        blo[s][e] = pl[0];
+        blo[s][e + 1] = pl[1];
       }
-      f = qinv * sm.kscale;
     }
-    phase_end(pc, 1);
+    return qinv * sm.kscale[buf];
+  };
+  // QK^T with the query operand in bhi / blo: logits of the lane's row for K
+  // tile rows 16 tt + 4 G + i.
+  auto qk_products = [&]() {
     if constexpr (SPLIT) {
       // Two token tiles at a time (independent MFMA chains), in groups of two
       // k-steps: the next group's A operands are read from LDS before this
@@ -856,39 +862,126 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
   };
 
   bool present = true;   // tile t has storage
+  if constexpr (SPLIT) {
+    // Eight-wave workgroups, one loop per wave half (so that the query
+    // operand the V-staging waves hold across their V staging is not kept
+    // live through the K-staging waves' steps).  Per tile, between barrier B
+    // and barrier A the V-staging waves stage the tile's V half, so they
+    // form the next tile's query operand after their PV instead, where they
+    // would otherwise wait for the K staging; that needs the next record's
+    // c^K in LDS before barrier A, so wave 1 stages it at the end of its
+    // softmax, into the other of the two c^K buffers.
+    if (!vrole) {
 #pragma unroll 1
-  for (int t = 0; t < T; ++t) {
-    // Per-lane index math of the staging and masking (tens of values) is
-    // cheaper to recompute per tile than to keep live across the loop.
-    asm volatile("" : "+v"(tid));
-    l = tid & 63;
-    const bool exact = t == 0 || (has_tail && t == T - 1);
-    const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
-    const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
-    if (exact) load_exact_query();
-    const bool np = issue_next(t);
-    phase_end(pc, 0);   // next record's loads issued
-    qk(exact);          // phase 1 (query operand) and phase 2 (products)
-    phase_end(pc, 2);
-    softmax(base, count);
-    phase_end(pc, 3);
-    // the next tile's K half, once every wave is done with this K tile
-    if (t + 1 < T) {
-      lds_barrier();
-      phase_end(pc, 4);
-      if (!vrole) stage_k_tile(t + 1, np);
+      for (int t = 0; t < T; ++t) {
+        // Per-lane index math of the staging and masking (tens of values) is
+        // cheaper to recompute per tile than to keep live across the loop.
+        asm volatile("" : "+v"(tid));
+        l = tid & 63;
+        const bool exact = t == 0 || (has_tail && t == T - 1);
+        const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
+        const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
+        if (exact) {
+          load_exact_query();
+          f = qk_scale;
+        }
+        const bool np = issue_next(t);
+        phase_end(pc, 0);   // next record's loads issued
+        if (!exact) f = record_operand(t & 1);
+        phase_end(pc, 1);
+        qk_products();
+        phase_end(pc, 2);
+        softmax(base, count);
+        if (role == 1 && np && t + 1 <= n_rec) stage_ck((t + 1) & 1);
+        phase_end(pc, 3);
+        if (t + 1 < T) {
+          lds_barrier();   // every wave is done with this K tile
+          phase_end(pc, 4);
+          stage_k_tile(t + 1, np);
+        }
+        phase_end(pc, 5);
+        pv(exact);
+        phase_end(pc, 6);
+        if (t + 1 < T) lds_barrier();   // every wave is done with this V tile
+        phase_end(pc, 7);
+        present = np;
+      }
+    } else {
+      load_exact_query();   // tile 0, the sink
+      f = qk_scale;
+#pragma unroll 1
+      for (int t = 0; t < T; ++t) {
+        asm volatile("" : "+v"(tid));   // as above
+        l = tid & 63;
+        const bool exact = t == 0 || (has_tail && t == T - 1);
+        const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
+        const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
+        const bool np = issue_next(t);
+        phase_end(pc, 0);
+        qk_products();   // operand formed in the previous tile's last window
+        phase_end(pc, 2);
+        softmax(base, count);
+        phase_end(pc, 3);
+        if (t + 1 < T) lds_barrier();
+        phase_end(pc, 4);
+        pv(exact);
+        phase_end(pc, 6);
+        if (t + 1 < T) {
+          // the next tile's query operand (its c^K was staged before barrier A;
+          // no record loads are in flight for a next tile that is the tail)
+          if (has_tail && t + 1 == T - 1) {
+            load_exact_query();
+            f = qk_scale;
+          } else {
+            f = record_operand((t + 1) & 1);
+          }
+          phase_end(pc, 1);
+          lds_barrier();
+          phase_end(pc, 7);
+          stage_v_tile(t + 1, np);
+        }
+        phase_end(pc, 8);
+        present = np;
+      }
     }
-    phase_end(pc, 5);
-    pv(exact);
-    phase_end(pc, 6);
-    // the next tile's V half, once every wave is done with this V tile
-    if (t + 1 < T) {
-      lds_barrier();
-      phase_end(pc, 7);
-      if (vrole || !SPLIT) stage_v_tile(t + 1, np);
+  } else {
+#pragma unroll 1
+    for (int t = 0; t < T; ++t) {
+      asm volatile("" : "+v"(tid));   // as above
+      l = tid & 63;
+      const bool exact = t == 0 || (has_tail && t == T - 1);
+      const int base = t == 0 ? 0 : exact ? tail_base : kSink + kGroup * (t - 1);
+      const int count = !present ? 0 : t == 0 ? min(nseq, kSink) : exact ? tail_count : kGroup;
+      if (exact) {
+        load_exact_query();
+        f = qk_scale;
+      }
+      const bool np = issue_next(t);
+      phase_end(pc, 0);   // next record's loads issued
+      if (!exact) f = record_operand(0);
+      phase_end(pc, 1);
+      qk_products();
+      phase_end(pc, 2);
+      softmax(base, count);
+      phase_end(pc, 3);
+      // the next tile's K half, once every wave is done with this K tile
+      if (t + 1 < T) {
+        lds_barrier();
+        phase_end(pc, 4);
+        stage_k_tile(t + 1, np);
+      }
+      phase_end(pc, 5);
+      pv(exact);
+      phase_end(pc, 6);
+      // the next tile's V half, once every wave is done with this V tile
+      if (t + 1 < T) {
+        lds_barrier();
+        phase_end(pc, 7);
+        stage_v_tile(t + 1, np);
+      }
+      phase_end(pc, 8);
+      present = np;
     }
-    phase_end(pc, 8);
-    present = np;
   }
   phase_store(((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * NW + w, pc);
 
