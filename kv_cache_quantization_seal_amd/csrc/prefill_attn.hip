@@ -333,6 +333,9 @@ template <int D, int GQ, int MAXB, int NW>
 __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefill_attn_kernel(PrefillAttnArgs a) {
   static_assert(NW == 4 || (NW == 8 && D == 128), "four waves, or eight at head dimension 128");
   constexpr bool SPLIT = NW == 8;  // K and V staging split between the wave halves
+  // MFMA A operands read a group ahead: eight-wave workgroups, and D 256,
+  // where one wave per SIMD has no other wave to cover its LDS latency.
+  constexpr bool READ_AHEAD = SPLIT || D == 256;
   __shared__ PaSmem<D, SPLIT> sm;
   constexpr int ROWS = 16 * NW;   // query rows
   constexpr int KS = D / 32;      // MFMA k-steps over the channels
@@ -640,12 +643,13 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
   // QK^T with the query operand in bhi / blo: logits of the lane's row for K
   // tile rows 16 tt + 4 G + i.
   auto qk_products = [&]() {
-    if constexpr (SPLIT) {
+    if constexpr (READ_AHEAD) {
       // Two token tiles at a time (independent MFMA chains), in groups of two
       // k-steps: the next group's A operands are read from LDS before this
       // group's eight products are issued, so a wave covers its own LDS
       // latency (in an eight-wave workgroup, half the waves stage meanwhile;
-      // a four-wave one has no registers to spare for it).
+      // at D 256 a wave has its SIMD to itself; a four-wave workgroup at
+      // D 128 has no registers to spare for it).
       constexpr int NG = 4 * KS / 2;   // groups: 4 token-tile pairs x KS / 2
       v8h A[2][4];
       auto load_a = [&](v8h* dst, int gi) {
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 4) ? 2 : 1) void prefil
       rotate_out<NCT>(o, G);
       rotated = !exact;
     }
-    if constexpr (SPLIT) {
+    if constexpr (READ_AHEAD) {
       // Two channel tiles at a time, in groups of two token steps, the next
       // group's A operands read ahead as in QK.
       constexpr int NG = NCT / 2 * 2;   // groups: NCT / 2 channel-tile pairs x 2
