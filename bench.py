@@ -252,7 +252,14 @@ def trace_run(args, reps=8):
             rec = wavetrace.read(which, 4 * (n_ex + n_rec))
             names = {0: "start", 1: "query", 2: "first_ck", 3: "first_qk", 4: "first_pv", 5: "groups_done",
                      6: "partial_written"}
-            groups = {"exact": range(0, 4 * n_ex), "record": range(4 * n_ex, 4 * (n_ex + n_rec))}
+            # the split kernel's grid order, as the plan chooses it: record
+            # workgroups first when each pair has four exact splits (few
+            # pairs) and the record workgroups are one per CU at most
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+            if plan["exact_splits"] == 4 and n_rec <= cus:
+                groups = {"record": range(0, 4 * n_rec), "exact": range(4 * n_rec, 4 * (n_ex + n_rec))}
+            else:
+                groups = {"exact": range(0, 4 * n_ex), "record": range(4 * n_ex, 4 * (n_ex + n_rec))}
         else:
             n_tiles = 2 * B * hkv * max(0, (max(lens) - 128) // 128)
             rec = wavetrace.read(which, n_tiles * d // 16)

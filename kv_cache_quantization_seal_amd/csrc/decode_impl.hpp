@@ -805,19 +805,21 @@ union DecodeSmemU {
   ExactSmem<D, GQ> ex;
 };
 
-// 1-D grid: the exact workgroups of every pair first (n_exact_splits per
-// pair), then the record workgroups, pair-major.  Only the record workgroups
-// are sized to be resident together; the short exact ones are dispatched
-// first and the record workgroups that do not fit start as they retire.
+// 1-D grid of the record workgroups (pair-major) and the exact workgroups of
+// every pair (n_exact_splits per pair), in the order the plan chose
+// (record_first: record workgroups first).
 template <int D, int KB, int VB, int GQ, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ DecodeSmemU<D, KB, VB, GQ> sm;
   trace_begin((int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6));
   const int nex = a.nsplit - a.n_rec_splits;
   const int npair = a.c.batch * a.c.hkv;
+  const int nrw = a.n_rec_splits * npair, nxw = nex * npair;
+  const bool rec_first = a.record_first != 0;
   const int bx = blockIdx.x;
-  if (bx < nex * npair) {
-    const int pair = bx / nex, es = bx - pair * nex;
+  if (rec_first ? bx >= nrw : bx < nxw) {
+    const int ex = rec_first ? bx - nrw : bx;
+    const int pair = ex / nex, es = ex - pair * nex;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
     const int n = a.c.seq_len[b];
     const bool fold = fold_ok(a, n);   // the step's own token counts (append folded in)
@@ -826,7 +828,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     else
       exact_split<D, GQ, 2>(sm.ex, a, b, kvh, es, a.n_rec_splits + es, n + fold, fold);
   } else {
-    const int r = bx - nex * npair;
+    const int r = rec_first ? bx : bx - nxw;
     const int pair = r / a.n_rec_splits, split = r - pair * a.n_rec_splits;
     const int b = pair / a.c.hkv, kvh = pair - b * a.c.hkv;
     const int n = a.c.seq_len[b];

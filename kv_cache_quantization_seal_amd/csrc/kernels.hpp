@@ -159,6 +159,7 @@ struct DecodeArgs {
   int n_rec_splits;
   int groups_per_split;
   int groups_per_wave;
+  int record_first;    // grid order: record workgroups first (else exact ones)
   // Append folded into the step (both NULL: the cache already holds the
   // step's token): fp16 [B][Hkv][D], the token at position seq_len[b].  The
   // exact split that covers that position reads it from here and writes it
@@ -185,6 +186,7 @@ struct DecodePlan {
   int n_rec_splits;
   int n_exact_splits;
   int nsplit;
+  int record_first;   // record workgroups first in the split kernel's grid
   size_t ws_bytes;
 };
 

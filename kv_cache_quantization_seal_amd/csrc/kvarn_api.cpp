@@ -378,6 +378,7 @@ static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* ca
   a.n_rec_splits = p.n_rec_splits;
   a.groups_per_split = p.groups_per_split;
   a.groups_per_wave = p.groups_per_wave;
+  a.record_first = p.record_first;
   a.k_new = (const __half*)k_new;
   a.v_new = (const __half*)v_new;
   return hip_status(kvarn::launch_decode(cfg->head_dim, cfg->k_bits, cfg->v_bits,
