@@ -5,7 +5,7 @@
 
 namespace kvarn {
 
-DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs, int cus) {
+DecodePlan plan_decode(int D, int kb, int hq, int hkv, int batch, int max_groups, int resident_wgs, int cus) {
   DecodePlan p;
   // Each record workgroup is four independent waves; at run time each wave
   // takes an even share of its pair's sealed groups, at most groups_per_wave
@@ -26,8 +26,12 @@ DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int re
   // with fewer other waves.  Same-box A/B of the split kernel: Llama-3.1-8B
   // 11.45 -> 10.84 us (256 record workgroups of two groups per wave instead
   // of 512 of one), Phi-4 69.3 -> 65.5 us; at Qwen3-4B (many pairs) the cap
-  // would cost 44.3 -> 45.8 us, so it is not applied there.
-  if (cus > 0 && !(2 * 4 * pairs > (int64_t)resident_wgs)) resident_wgs = std::min(resident_wgs, 2 * cus);
+  // would cost 44.3 -> 45.8 us, so it is not applied there.  3-bit K codes
+  // (bit-field extraction, a longer chain per group) keep three: the Llama
+  // shape's 3-bit K preset 13.4 -> 12.5 us with 512 record workgroups of one
+  // group per wave, where 2-bit K went 10.59 -> 11.35 us.
+  const int cap = kb == 3 ? 3 : 2;
+  if (cus > 0 && !(2 * 4 * pairs > (int64_t)resident_wgs)) resident_wgs = std::min(resident_wgs, cap * cus);
   const bool many = 2 * 4 * pairs > (int64_t)resident_wgs;
   p.n_exact_splits = many ? 2 : 4;
   const int64_t target = many ? std::max<int64_t>(pairs, resident_wgs - 2 * pairs) : resident_wgs;

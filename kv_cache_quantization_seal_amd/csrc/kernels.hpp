@@ -197,7 +197,7 @@ constexpr int kMaxResidentWgs = 4096;
 // cus: compute units of the launch's device, or 0 (a device-free plan, used
 // for the workspace bound; rounding to whole workgroups per CU only ever
 // removes splits).
-DecodePlan plan_decode(int D, int hq, int hkv, int batch, int max_groups, int resident_wgs, int cus);
+DecodePlan plan_decode(int D, int kb, int hq, int hkv, int batch, int max_groups, int resident_wgs, int cus);
 // Resident split workgroups on the current device for this configuration.
 int decode_resident_wgs(int D, int kb, int vb, int gq);
 // Compute units of the current device (0 if unknown).

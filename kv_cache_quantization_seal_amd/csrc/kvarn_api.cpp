@@ -136,7 +136,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int3
   if (check_cfg(cfg) != KVARN_OK || batch <= 0 || max_groups < 0) return 0;
   // Planned for the most resident workgroups any device allows: a launch
   // plans for fewer, hence fewer splits and no more workspace.
-  return kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch, max_groups,
+  return kvarn::plan_decode(cfg->head_dim, cfg->k_bits, cfg->num_q_heads, cfg->num_kv_heads, batch, max_groups,
                             kvarn::kMaxResidentWgs, 0)
       .ws_bytes;
 }
@@ -148,7 +148,7 @@ kvarn_status kvarn_decode_plan(const kvarn_config* cfg, int32_t batch, int32_t m
   if (batch <= 0 || max_groups < 0) return fail(KVARN_EINVAL, "batch must be > 0 and max_groups >= 0");
   const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
                                                   cfg->num_q_heads / cfg->num_kv_heads);
-  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, batch,
+  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->k_bits, cfg->num_q_heads, cfg->num_kv_heads, batch,
                                                  max_groups, resident, kvarn::decode_cu_count());
   const int64_t pairs = (int64_t)batch * cfg->num_kv_heads;
   out[0] = p.n_rec_splits;
@@ -358,7 +358,7 @@ static kvarn_status decode_common(const kvarn_config* cfg, const kvarn_cache* ca
     return fail(KVARN_EINVAL, "q and out must be 16-byte aligned");
   const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
                                                   cfg->num_q_heads / cfg->num_kv_heads);
-  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
+  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->k_bits, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
                                                  cache->max_groups, resident, kvarn::decode_cu_count());
   if (!workspace || ws_bytes < p.ws_bytes)
     return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, p.ws_bytes);
@@ -421,7 +421,7 @@ kvarn_status kvarn_decode_attn_noalloc(const kvarn_config* cfg, const kvarn_cach
   if (!(softmax_scale == softmax_scale)) return fail(KVARN_EINVAL, "softmax_scale is NaN");
   const int resident = kvarn::decode_resident_wgs(cfg->head_dim, cfg->k_bits, cfg->v_bits,
                                                   cfg->num_q_heads / cfg->num_kv_heads);
-  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
+  const kvarn::DecodePlan p = kvarn::plan_decode(cfg->head_dim, cfg->k_bits, cfg->num_q_heads, cfg->num_kv_heads, cache->batch,
                                                  cache->max_groups, resident, kvarn::decode_cu_count());
   if (p.ws_bytes > kNoAllocScratchBytes)
     return fail(KVARN_EWORKSPACE,
