@@ -190,3 +190,57 @@ def test_prefill_attn_eight_wave_grid(kb, vb, lens):
                 worst = max(worst, float(np.abs(got[b, i, h] - ref).max()))
     print(f"eight-wave grid k{kb} v{vb} lens={lens}: sampled max abs err {worst:.3e}")
     assert worst <= ATTN_ATOL
+
+
+def test_prefill_attn_eight_wave_paged_absent_groups():
+    """Eight-wave workgroups over a block-table cache with two entries outside
+    the pool: request 0's first sealed group (so the first record tile has no
+    storage and its c^K buffer is never staged) and a middle group of request
+    1.  Every query skips those 128 positions; every 41st row of every head
+    against the oracle's materialization without them."""
+    d, hq, hkv, kb, vb, chunk = 128, 32, 8, 2, 2, 2048
+    lens = [2100, 2080]   # both longer than the chunk: every row has a position
+    B = len(lens)
+    mg = max((n - 128) // 128 for n in lens) + 1
+    states = _states(d, hkv, kb, vb, lens, 930)
+    cfg = K.make_config(d, hq, hkv, kb, vb)
+    nblk = B * mg + 2
+    cache = K.KVarNCache(cfg, B, mg, num_blocks=nblk)
+    table = np.random.default_rng(17).permutation(nblk)[:B * mg].astype(np.int32).reshape(B, mg)
+    absent = [(0, 0), (1, 6)]
+    for r, g in absent:
+        table[r, g] = nblk + 5   # past the pool: no storage
+    cache.block_table.copy_(torch.from_numpy(table))
+    dev = cache.sink_k.device
+    for b, row in enumerate(states):
+        for h, st in enumerate(row):
+            cache.sink_k[b, h, :len(st.sink_k)] = torch.from_numpy(np.stack(st.sink_k)).to(dev)
+            cache.sink_v[b, h, :len(st.sink_v)] = torch.from_numpy(np.stack(st.sink_v)).to(dev)
+            if st.tail_k:
+                cache.tail_k[b, h, :st.tail_len] = torch.from_numpy(np.stack(st.tail_k)).to(dev)
+                cache.tail_v[b, h, :st.tail_len] = torch.from_numpy(np.stack(st.tail_v)).to(dev)
+            for g, (rk, rv) in enumerate(zip(st.rec_k, st.rec_v)):
+                if (b, g) not in absent:
+                    cache.record(b, h, g, "k").copy_(torch.frombuffer(bytearray(rk), dtype=torch.uint8).to(dev))
+                    cache.record(b, h, g, "v").copy_(torch.frombuffer(bytearray(rv), dtype=torch.uint8).to(dev))
+    cache.seq_len.copy_(torch.tensor(lens, dtype=torch.int32, device=dev))
+    q = np.random.default_rng(19).standard_normal((B, chunk, hq, d)).astype(np.float16)
+    out = cache.prefill_attn(torch.from_numpy(q).to(dev)).cpu().numpy()
+    assert np.isfinite(out).all()
+    gq = hq // hkv
+    worst = 0.0
+    for b, n in enumerate(lens):
+        mats = [st.materialize() for st in states[b]]
+        keep = np.ones(n, dtype=bool)
+        for r, g in absent:
+            if r == b:
+                keep[128 + 128 * g:256 + 128 * g] = False
+        for i in range(0, chunk, 41):
+            p = n - chunk + i
+            sel = np.flatnonzero(keep[:p + 1])
+            for h in range(hq):
+                kall, vall = mats[h // gq]
+                ref = O.attention(q[b, i, h], kall[sel], vall[sel])
+                worst = max(worst, float(np.abs(out[b, i, h] - ref).max()))
+    print(f"eight-wave grid, paged with absent groups: sampled max abs err {worst:.3e}")
+    assert worst <= ATTN_ATOL
