@@ -30,9 +30,9 @@ DecodePlan plan_decode(int D, int kb, int hq, int hkv, int batch, int max_groups
   // (bit-field extraction, a longer chain per group) keep three: the Llama
   // shape's 3-bit K preset 13.4 -> 12.5 us with 512 record workgroups of one
   // group per wave, where 2-bit K went 10.59 -> 11.35 us.
-  // "Many pairs" is judged against the capped count: at the Phi-4 shape (80
+  // "Many pairs" is decided against the capped count: at the Phi-4 shape (80
   // pairs, three workgroups per CU) that gives two counted exact splits per
-  // pair and 240 record workgroups, 66.0 us; judged against the uncapped
+  // pair and 240 record workgroups, 66.0 us; decided against the uncapped
   // count it gave four uncounted exact splits and 480 record workgroups,
   // more workgroups than fit at once, 79 us.
   const int cap = kb == 3 ? 3 : 2;
