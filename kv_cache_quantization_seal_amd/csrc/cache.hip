@@ -188,8 +188,20 @@ __global__ __launch_bounds__(4 * D) void dequant_kernel(const uint8_t* __restric
     }
     lds_barrier();
     uint4* out = reinterpret_cast<uint4*>(dst + (int64_t)blockIdx.x * kGroup * D);
+    if constexpr (D == 128) {
+      // Streaming (nontemporal) stores: the tile is written once and not read
+      // back here.  8192 records at D 128: 67-79 -> 62-66 us; at D 256 (64 KB
+      // tiles) they were slower (V records 186 -> 248 us), so not used there.
 #pragma unroll
-    for (int k = 0; k < 4; ++k) out[threadIdx.x + 4 * D * k] = os_[threadIdx.x + 4 * D * k];
+      for (int k = 0; k < 4; ++k) {
+        const uint4 o = os_[threadIdx.x + 4 * D * k];
+        __builtin_nontemporal_store(v4i{(int)o.x, (int)o.y, (int)o.z, (int)o.w},
+                                    reinterpret_cast<v4i*>(out + threadIdx.x + 4 * D * k));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[threadIdx.x + 4 * D * k] = os_[threadIdx.x + 4 * D * k];
+    }
   } else {
     uint4* out = reinterpret_cast<uint4*>(dst + ((int64_t)blockIdx.x * kGroup + t) * D + 32 * bl);
 #pragma unroll
