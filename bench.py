@@ -35,7 +35,7 @@ import numpy as np
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_F16_PEAK = 2.5e15     # flop/s, dense fp16 MFMA, MI355X
-# fp32 vector peak without packed instructions (disabled in this build):
+# fp32 vector peak without packed instructions (the library is compiled with them off):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop per FMA x 2.4 GHz.  The 157.3 TFLOP/s
 # vendor figure counts packed FMAs, which no kernel here issues.
 VALU_FP32_PEAK = 78.6e12
