@@ -854,11 +854,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int ns = a.nsplit, nrec = a.n_rec_splits;
   // Append folded into the step: the split kernel has attended over the new
   // token and stored it; the length moves on here, once per request (no
-  // kernel of this launch reads it).
-  if (a.k_new && hq == 0 && tid == 0) {
-    const int n = a.c.seq_len[b];
-    if (fold_ok(a, n)) a.c.seq_len[b] = n + 1;
-  }
+  // kernel of this launch reads it).  Read first, written last, so that the
+  // read's round trip overlaps the loads of the partials instead of coming
+  // before them.
+  const bool advance = a.k_new && hq == 0 && tid == 0;
+  const int n_old = advance ? a.c.seq_len[b] : 0;
   const int64_t base = ((int64_t)b * a.hq + hq) * ns;
   const float* ml = a.ws_ml + 2 * base;
   const float* ob = a.ws_o + base * D + P * l;
@@ -877,15 +877,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     }
   };
 
+  // (max, sum) of splits l and l + 64 in lane l (then further passes),
+  // loaded first and unconditionally (clamped to the last split, masked
+  // after): loads complete in issue order, so the weights can be formed
+  // while the partial outputs behind them are still arriving.
+  const float2 ml0 = *reinterpret_cast<const float2*>(ml + 2 * min(l, ns - 1));
+  const float2 ml1 = *reinterpret_cast<const float2*>(ml + 2 * min(l + kWave, ns - 1));
+  __builtin_amdgcn_sched_barrier(0);
   // First batch of this wave's partial outputs: splits w, w+4, ... (clamped
   // to the last split; the extra loads are discarded).
   float ov[OPW][P];
 #pragma unroll
   for (int u = 0; u < OPW; ++u) load_o(min(w + kWaves * u, ns - 1), ov[u]);
-  // (max, sum) of splits l and l + 64 in lane l (then further passes).
-  float m0 = l < ns ? ml[2 * l] : -INFINITY, l0 = l < ns ? ml[2 * l + 1] : 0.f;
-  float m1 = l + kWave < ns ? ml[2 * (l + kWave)] : -INFINITY;
-  float l1 = l + kWave < ns ? ml[2 * (l + kWave) + 1] : 0.f;
+  float m0 = l < ns ? ml0.x : -INFINITY, l0 = l < ns ? ml0.y : 0.f;
+  float m1 = l + kWave < ns ? ml1.x : -INFINITY;
+  float l1 = l + kWave < ns ? ml1.y : 0.f;
   float mloc = fmaxf(m0, m1);
   for (int s = l + 2 * kWave; s < ns; s += kWave) mloc = fmaxf(mloc, ml[2 * s]);
   const float M = wave_max_f(mloc);
@@ -991,6 +997,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   float* out = a.out + ((int64_t)b * a.hq + hq) * D + P * l;
 #pragma unroll
   for (int i = 0; i < P; ++i) out[i] = (x[i] * rs + e[i]) * inv;
+  if (advance && fold_ok(a, n_old)) a.c.seq_len[b] = n_old + 1;
 }
 
 template <int D, int KB, int VB, int GQ>
