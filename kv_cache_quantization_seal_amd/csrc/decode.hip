@@ -121,10 +121,20 @@ hipError_t launch_decode(int D, int kb, int vb, int gq, const DecodeArgs& a, int
     if (e != hipSuccess) return e;
   }
   if (phases & 2) {
-    if (D == 128)
-      hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.hq, a.c.batch), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(decode_combine_kernel<256>, dim3(a.hq, a.c.batch), dim3(256), 0, st, a);
+    // First batch sized to the splits (clamped loads past the last split
+    // repeat it; fewer of them with few splits, e.g. 6 at B 16).
+    const dim3 grid(a.hq, a.c.batch);
+    const int ns = a.nsplit;
+#define KVARN_COMBINE(d)                                                                                  \
+  do {                                                                                                    \
+    if (ns <= 8) hipLaunchKernelGGL((decode_combine_kernel<d, 2>), grid, dim3(256), 0, st, a);           \
+    else if (ns <= 20) hipLaunchKernelGGL((decode_combine_kernel<d, 5>), grid, dim3(256), 0, st, a);     \
+    else if (ns <= 40) hipLaunchKernelGGL((decode_combine_kernel<d, 10>), grid, dim3(256), 0, st, a);    \
+    else hipLaunchKernelGGL((decode_combine_kernel<d, 20>), grid, dim3(256), 0, st, a);                  \
+  } while (0)
+    if (D == 128) KVARN_COMBINE(128);
+    else KVARN_COMBINE(256);
+#undef KVARN_COMBINE
   }
   return hipGetLastError();
 }

@@ -843,10 +843,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // w the partial outputs of splits w, w+4, ... for channels P*l .. P*l+P-1.
 // Each wave then finds the maximum M and normalizer L itself, takes the
 // weight of split s from lane s % 64, and one barrier joins the four sums.
-template <int D>
+// OPW: partial outputs per wave in the first batch (4 OPW splits; the host
+// picks the smallest instance that covers the launch's splits, up to 80).
+template <int D, int OPW>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int P = D / 64;
-  constexpr int OPW = 20;  // partial outputs per wave in the first batch (80 splits)
+  static_assert(4 * OPW <= 2 * 64, "first-batch weights come from lanes of two (max, sum) passes");
   __shared__ float orec[kWaves][D];
   __shared__ float oex[kWaves][D];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
